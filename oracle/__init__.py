@@ -168,8 +168,9 @@ def pack(src, src_off, real_len, q: int, pack_start, capacity: int, fold: bool =
                           _ptr(packed), _ptr(tm), _ptr(cu), _ptr(cp))
     if st != 0:
         return {"status": int(st)}
+    used = int(ps[-1]) + P if P > 0 else 0
     return {"status": 0, "packed": packed, "token_mask": tm,
-            "cu_seqlens": cu[:csr], "cu_seqlens_padded": cp[:csr]}
+            "cu_seqlens": cu[:used], "cu_seqlens_padded": cp[:used]}
 
 
 def pack_csr_slices(cu_csr, pack_start):

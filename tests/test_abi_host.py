@@ -1,0 +1,146 @@
+"""The C-ABI library on the host (CPU only): it loads, exports every
+function ``include/psq.h`` declares, and rejects bad arguments before any
+HIP call.  No case here reaches a kernel launch."""
+import ctypes
+import subprocess
+
+import pytest
+
+from varlen_attention_metadata_amd import _lib
+
+FAKE = 0x10000          # never dereferenced: every case fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert {"psq_params_from_doc_ids", "psq_process_thd", "psq_pack_rows",
+            "psq_status_string", "psq_workspace_init"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert _lib.status_string(0, False) == "ok"
+    assert "workspace" in _lib.status_string(_lib.ERR_WORKSPACE, False)
+    assert "capacity" in _lib.status_string(_lib.DATA_PACK_OVERFLOW, True)
+    assert "no sequence" in _lib.status_string(_lib.DATA_EMPTY_ROW, True)
+    assert _lib.status_string(999, False) == "unknown error code"
+
+
+def test_workspace_sizes(lib):
+    assert lib.psq_params_from_doc_ids_workspace(0, 0) >= 256
+    a = lib.psq_params_from_doc_ids_workspace(4, 64)
+    b = lib.psq_params_from_doc_ids_workspace(32, 32768)
+    assert a >= 256 and b > a and b % 256 == 0
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, _lib.I64, 64)
+    assert _lib.psq_process_thd_workspace(lay, 16, 8192) >= 256 + 8 * 16
+    assert lib.psq_pack_rows_workspace(65536, 3555, 16384) >= 256
+
+
+def _doc(lib, **kw):
+    a = dict(doc=FAKE, dt=_lib.I32, B=4, S=64, cu=FAKE, n=FAKE, mx=FAKE, mask=None,
+             st=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.psq_params_from_doc_ids(a["doc"], a["dt"], a["B"], a["S"], a["cu"], a["n"],
+                                       a["mx"], a["mask"], a["st"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_doc_ids_validation(lib):
+    assert _doc(lib, B=-1) == _lib.ERR_ARG
+    assert _doc(lib, S=-3) == _lib.ERR_ARG
+    assert _doc(lib, dt=7) == _lib.ERR_ARG
+    assert _doc(lib, B=1 << 16, S=1 << 15) == _lib.ERR_OVERFLOW
+    assert _doc(lib, B=1, S=1 << 31) == _lib.ERR_OVERFLOW
+    assert _doc(lib, cu=None) == _lib.ERR_ARG
+    assert _doc(lib, doc=None) == _lib.ERR_ARG
+    assert _doc(lib, ws=None) == _lib.ERR_WORKSPACE
+    assert _doc(lib, ws=FAKE, wsb=8) == _lib.ERR_WORKSPACE
+
+
+def _thd(lib, layout, copies=None, n_copies=0, **kw):
+    a = dict(B=2, S=6, cu=FAKE, cp=None, n=FAKE, mx=FAKE, pb=FAKE, mask=None, st=FAKE,
+             ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    if copies is None:
+        copies, _ = _lib.make_copies([])
+    lay = ctypes.byref(layout) if layout is not None else None
+    return lib.psq_process_thd(lay, a["B"], a["S"], a["cu"], a["cp"], a["n"], a["mx"], a["pb"],
+                               a["mask"], copies, n_copies, a["st"], a["ws"], a["wsb"],
+                               a["stream"])
+
+
+def test_process_thd_validation(lib):
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, FAKE, _lib.I64, 2)
+    assert _thd(lib, None) == _lib.ERR_ARG
+    assert _thd(lib, lay, B=-1) == _lib.ERR_ARG
+    assert _thd(lib, lay, st=None) == _lib.ERR_ARG
+    assert _thd(lib, lay, cu=None) == _lib.ERR_ARG
+    assert _thd(lib, _lib.make_layout(5)) == _lib.ERR_ARG
+    assert _thd(lib, _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, 9, 2)) == _lib.ERR_ARG
+    assert _thd(lib, _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, _lib.I64, -1)) == _lib.ERR_ARG
+    assert _thd(lib, _lib.make_layout(_lib.LAYOUT_SEQ_LENS, None, None, _lib.I64, 2)) == _lib.ERR_ARG
+    assert _thd(lib, _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=FAKE, doc_dtype=3)) == _lib.ERR_ARG
+    assert _thd(lib, _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=None)) == _lib.ERR_ARG
+    big = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, _lib.I64, 1 << 20)
+    assert _thd(lib, big, B=1 << 11, S=4) == _lib.ERR_OVERFLOW
+    assert _thd(lib, lay, B=1 << 20, S=1 << 12) == _lib.ERR_OVERFLOW
+    assert _thd(lib, lay) == _lib.ERR_WORKSPACE           # wsb = 0
+    assert _thd(lib, lay, ws=None, wsb=1 << 20) == _lib.ERR_WORKSPACE
+    # copies: too many, null pointers, overlap, bad stride
+    arr, _ = _lib.make_copies([(FAKE, FAKE + 4096, 1, 64, 64)] * 9)
+    assert _thd(lib, lay, copies=arr, n_copies=9, wsb=1 << 20) == _lib.ERR_ARG
+    arr, n = _lib.make_copies([(None, FAKE, 1, 64, 64)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+    arr, n = _lib.make_copies([(FAKE, FAKE + 32, 1, 64, 64)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+    arr, n = _lib.make_copies([(FAKE, FAKE + 65536, 4, 64, 32)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+    arr, n = _lib.make_copies([(FAKE, FAKE + 65536, -1, 64, 64)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+
+
+def _pack(lib, **kw):
+    a = dict(src=FAKE, src_len=100, off=FAKE, rl=FAKE, N=4, q=4, order=None, ps=FAKE, P=2,
+             C=36, fold=1, pad=0, packed=FAKE, tm=FAKE, cu=FAKE, cp=FAKE, st=FAKE, ws=FAKE,
+             wsb=256, stream=None)
+    a.update(kw)
+    return lib.psq_pack_rows(a["src"], a["src_len"], a["off"], a["rl"], a["N"], a["q"],
+                             a["order"], a["ps"], a["P"], a["C"], a["fold"], a["pad"],
+                             a["packed"], a["tm"], a["cu"], a["cp"], a["st"], a["ws"], a["wsb"],
+                             a["stream"])
+
+
+def test_pack_rows_validation(lib):
+    assert _pack(lib, q=0) == _lib.ERR_ARG
+    assert _pack(lib, C=0) == _lib.ERR_ARG
+    assert _pack(lib, C=(1 << 30) + 1) == _lib.ERR_ARG
+    assert _pack(lib, N=-1) == _lib.ERR_ARG
+    assert _pack(lib, P=-1) == _lib.ERR_ARG
+    assert _pack(lib, N=(1 << 31) - 5, P=10) == _lib.ERR_OVERFLOW
+    assert _pack(lib, ps=None) == _lib.ERR_ARG
+    assert _pack(lib, st=None) == _lib.ERR_ARG
+    assert _pack(lib, packed=None) == _lib.ERR_ARG
+    assert _pack(lib, rl=None) == _lib.ERR_ARG
+    assert _pack(lib, src=None) == _lib.ERR_ARG
+    assert _pack(lib, ws=None) == _lib.ERR_WORKSPACE
+    assert _pack(lib, wsb=16) == _lib.ERR_WORKSPACE
+
+
+def test_python_api_refuses_cpu_tensors():
+    import torch
+    import varlen_attention_metadata_amd as psq
+    with pytest.raises(ValueError, match="GPU"):
+        psq.packed_seq_params_from_doc_ids(torch.zeros((2, 3), dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        psq.process_input_for_thd({"input_ids": torch.zeros((1, 4), dtype=torch.int64),
+                                   "position_ids": torch.zeros((1, 4), dtype=torch.int64),
+                                   "seq_lens": torch.tensor([[4]])})

@@ -1,0 +1,484 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every output is an integer or a byte copy, so every comparison is exact.
+Cases cover the five workloads at full size, seeded fuzz across tile and
+chunk boundaries, the degenerate shapes, the data-error bits, repeat-run
+determinism (the cross-workgroup look-back), and the workspace contract.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import varlen_attention_metadata_amd as psq
+from varlen_attention_metadata_amd import _lib
+
+pytestmark = pytest.mark.gpu
+V = -1000
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    _lib.load()                       # fails loudly if the library is missing
+    return torch.device("cuda:0")
+
+
+# ---------------------------------------------------------------------------
+# document maps
+# ---------------------------------------------------------------------------
+
+def run_doc(dev, doc_np, dtype=torch.int32, want_mask=True):
+    """Raw C-ABI call: returns (cu[:n+1], n, max, mask, status)."""
+    d = torch.from_numpy(np.ascontiguousarray(doc_np)).to(dev, dtype)
+    B, S = doc_np.shape
+    cu = torch.full((B * S + 1,), -7, dtype=torch.int32, device=dev)
+    scal = torch.full((4,), -7, dtype=torch.int32, device=dev)
+    mask = torch.full((max(B * S, 1),), 7, dtype=torch.uint8, device=dev)
+    ws = psq.workspace_for(dev, _lib.psq_params_from_doc_ids_workspace(B, S))
+    sp = scal.data_ptr()
+    _lib.psq_params_from_doc_ids(d.data_ptr(), _lib.I32 if dtype == torch.int32 else _lib.I64,
+                                 B, S, cu.data_ptr(), sp, sp + 4,
+                                 mask.data_ptr() if want_mask else None, sp + 8,
+                                 ws.data_ptr(), ws.numel(), torch.cuda.current_stream(dev).cuda_stream)
+    n, mx, st, _ = scal.cpu().tolist()
+    return cu[: n + 1].cpu().numpy(), n, mx, mask[: B * S].cpu().numpy(), st
+
+
+def check_doc(dev, doc_np, dtype=torch.int32):
+    say(f"doc map {doc_np.shape} {dtype}")
+    cu, n, mx, mask, st = run_doc(dev, doc_np, dtype)
+    ref = oracle.doc_segments(doc_np)
+    assert st == 0
+    assert n == ref["num_segments"]
+    assert np.array_equal(cu, ref["cu_seqlens"]), "cu_seqlens differ"
+    assert mx == ref["max_seqlen"]
+    assert np.array_equal(mask, ref["padding_mask"])
+
+
+@pytest.mark.parametrize("gen", [synth.doc_map_small, synth.doc_map_medium])
+def test_doc_workloads(dev, gen):
+    check_doc(dev, gen())
+
+
+def test_doc_stage_embedding_map(dev):
+    check_doc(dev, synth.stage_embedding()["doc_ids"])
+
+
+def test_doc_page_examples(dev):
+    for m in ([[1, 1, 2, 2, 2, 0]], [[1, 1, 1], [1, 1, 0]], [[1, 0, 0, 0]], [[1, 2, 1]]):
+        check_doc(dev, np.array(m, dtype=np.int32))
+
+
+@pytest.mark.parametrize("B,S", [(0, 5), (3, 0), (1, 1), (5, 1), (1, 2), (2, 3), (3, 4),
+                                 (1, 5), (2, 63), (3, 64), (2, 65), (1, 255), (4, 256),
+                                 (3, 1000), (2, 4095), (1, 4096), (2, 4097), (3, 8191),
+                                 (1, 12289), (2, 50000), (7, 3333)])
+@pytest.mark.parametrize("kind", ["alphabet3", "runs", "const", "pad_heavy"])
+def test_doc_fuzz(dev, B, S, kind):
+    rng = np.random.default_rng(hash((B, S, kind)) % 2**32)
+    if kind == "alphabet3":
+        d = rng.integers(0, 3, size=(B, S))
+    elif kind == "const":
+        d = np.ones((B, S), dtype=np.int64)          # only row starts are boundaries
+    elif kind == "pad_heavy":
+        d = np.where(rng.random((B, S)) < 0.8, 0, rng.integers(1, 4, size=(B, S)))
+    else:
+        d = np.zeros((B, S), dtype=np.int64)
+        for r in range(B):
+            t, idx = 0, 1
+            while t < S:
+                n = int(rng.geometric(1 / 300))
+                d[r, t:t + n] = idx if rng.random() > 0.1 else 0
+                t += n
+                idx += 1
+    check_doc(dev, d.astype(np.int32), torch.int32)
+    if B * S <= 20000:
+        # values that differ only in their upper 32 bits
+        check_doc(dev, d.astype(np.int64) * (1 << 32) + 7, torch.int64)
+
+
+def test_doc_unaligned_input(dev):
+    # a view that starts 4 bytes into its storage: the scalar-load path
+    d = synth.doc_map_medium()
+    base = torch.from_numpy(np.concatenate([[9], d.reshape(-1)]).astype(np.int32)).to(dev)
+    view = base[1:].view(d.shape)
+    assert view.data_ptr() % 16 != 0
+    B, S = d.shape
+    cu = torch.empty(B * S + 1, dtype=torch.int32, device=dev)
+    scal = torch.empty(4, dtype=torch.int32, device=dev)
+    mask = torch.empty(B * S + 1, dtype=torch.uint8, device=dev)[1:]   # unaligned mask too
+    ws = psq.workspace_for(dev, _lib.psq_params_from_doc_ids_workspace(B, S))
+    sp = scal.data_ptr()
+    say("doc map unaligned")
+    _lib.psq_params_from_doc_ids(view.data_ptr(), _lib.I32, B, S, cu.data_ptr(), sp, sp + 4,
+                                 mask.data_ptr(), sp + 8, ws.data_ptr(), ws.numel(),
+                                 torch.cuda.current_stream(dev).cuda_stream)
+    n, mx, st, _ = scal.cpu().tolist()
+    ref = oracle.doc_segments(d)
+    assert st == 0 and mx == ref["max_seqlen"]
+    assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
+    assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
+
+
+def test_doc_repeat_determinism(dev):
+    d = synth.stage_embedding()["doc_ids"]
+    first = run_doc(dev, d)
+    for i in range(20):
+        again = run_doc(dev, d)
+        assert np.array_equal(first[0], again[0]) and first[1:3] == again[1:3], i
+
+
+def test_doc_python_api(dev):
+    d = synth.doc_map_medium()
+    t = torch.from_numpy(d).to(dev)
+    p = psq.packed_seq_params_from_doc_ids(t)
+    ref = oracle.doc_segments(d)
+    assert p.doc_ids is t
+    assert p.cu_seqlens.dtype == torch.int32
+    assert np.array_equal(p.cu_seqlens.cpu().numpy(), ref["cu_seqlens"])
+    assert p.max_seqlen == ref["max_seqlen"]
+    kw = psq.to_flash_attention_kwargs(p)
+    assert kw["cu_seq_lens_q"] is kw["cu_seq_lens_k"] is p.cu_seqlens
+    assert kw["max_length_q"] == kw["max_length_k"] == p.max_seqlen
+
+
+def test_workspace_left_zeroed(dev):
+    d = synth.doc_map_medium()
+    run_doc(dev, d)
+    ws = psq.workspace_for(dev, 0)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    L = torch.tensor([[3, 2], [6, V]], device=dev)
+    psq.process_input_for_thd({"input_ids": torch.zeros((2, 6), dtype=torch.int64, device=dev),
+                               "position_ids": torch.zeros((2, 6), dtype=torch.int64, device=dev),
+                               "seq_lens": L})
+    torch.cuda.synchronize()
+    assert int(psq.workspace_for(dev, 0).count_nonzero()) == 0
+
+
+# ---------------------------------------------------------------------------
+# length tables (THD)
+# ---------------------------------------------------------------------------
+
+def run_thd_raw(dev, L, Lp, S, dtype=torch.int64, copies=()):
+    """Raw C-ABI call on tables; returns a dict like the oracle's."""
+    B, P = L.shape
+    tL = torch.from_numpy(np.ascontiguousarray(L)).to(dev, dtype)
+    tLp = torch.from_numpy(np.ascontiguousarray(Lp)).to(dev, dtype) if Lp is not None else None
+    cap = B * P + 1
+    cu = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+    cp = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+    mask = torch.full((max(B * S, 1),), 7, dtype=torch.uint8, device=dev)
+    scal = torch.full((4,), -7, dtype=torch.int32, device=dev)
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, tL.data_ptr(),
+                           tLp.data_ptr() if tLp is not None else None,
+                           _lib.I64 if dtype == torch.int64 else _lib.I32, P, V)
+    ws = psq.workspace_for(dev, _lib.psq_process_thd_workspace(lay, B, S))
+    arr, n_c = _lib.make_copies(list(copies))
+    sp = scal.data_ptr()
+    _lib.psq_process_thd(lay, B, S, cu.data_ptr(), cp.data_ptr(), sp, sp + 4, sp + 8,
+                         mask.data_ptr(), arr, n_c, sp + 12, ws.data_ptr(), ws.numel(),
+                         torch.cuda.current_stream(dev).cuda_stream)
+    n, mx, pb, st = scal.cpu().tolist()
+    if st != 0:
+        return {"status": st}
+    return {"status": 0, "cu_seqlens": cu[: n + 1].cpu().numpy(),
+            "cu_seqlens_padded": cp[: n + 1].cpu().numpy(), "num_seqs": n, "max_seqlen": mx,
+            "pad_between_seqs": pb, "padding_mask": mask[: B * S].cpu().numpy()}
+
+
+def check_thd(dev, L, Lp, S, dtype=torch.int64):
+    say(f"thd tables {L.shape} S={S} padded={Lp is not None} {dtype}")
+    got = run_thd_raw(dev, L, Lp, S, dtype)
+    ref = oracle.thd_tables(L, Lp, S)
+    assert got["status"] == ref["status"]
+    if ref["status"] != 0:
+        return
+    for key in ("cu_seqlens", "cu_seqlens_padded", "padding_mask"):
+        assert np.array_equal(got[key], ref[key]), key
+    for key in ("num_seqs", "max_seqlen", "pad_between_seqs"):
+        assert got[key] == ref[key], key
+
+
+def test_thd_page_example(dev):
+    check_thd(dev, np.array([[3, 2], [6, V]]), np.array([[4, 2], [6, V]]), 6)
+
+
+@pytest.mark.parametrize("L,Lp,S", [
+    ([[3, 2], [6, V]], [[4, 2], [6, V]], 8),
+    ([[3, 2]], [[3, 2]], 8),
+    ([[3], [4]], [[3], [4]], 4),
+    ([[0, 3]], [[0, 4]], 4),
+    ([[3, 2], [6, V]], None, 6),
+    ([[2, V, 3]], [[2, V, 3]], 9),            # a hole in the middle of a row
+])
+def test_thd_hand_cases(dev, L, Lp, S):
+    check_thd(dev, np.array(L), None if Lp is None else np.array(Lp), S)
+
+
+@pytest.mark.parametrize("L,Lp,S", [
+    ([[3, V]], [[3, 2]], 8),
+    ([[3, 2]], [[3, V]], 8),
+    ([[5]], [[4]], 8),
+    ([[-1]], [[2]], 8),
+    ([[V, V], [2, V]], [[V, V], [2, V]], 8),
+    ([[4, 4]], [[5, 4]], 8),
+    ([[4]], [[2**62]], 8),
+    ([[5], [V]], [[4], [V]], 8),
+])
+def test_thd_error_bits(dev, L, Lp, S):
+    check_thd(dev, np.array(L), np.array(Lp), S)
+
+
+def rand_tables(rng, B, P, S, q, tight=False, holes=False, zero_frac=0.1, maxlen=None):
+    L = np.full((B, P), V, dtype=np.int64)
+    Lp = np.full((B, P), V, dtype=np.int64)
+    maxlen = maxlen or max(1, S // 3)
+    for r in range(B):
+        used, j = 0, 0
+        slots = rng.permutation(P) if holes else np.arange(P)
+        order = sorted(slots[: rng.integers(1, P + 1)])
+        for j in order:
+            real = 0 if rng.random() < zero_frac else int(rng.integers(1, maxlen + 1))
+            padded = real if tight else -(-real // q) * q + int(rng.integers(0, 2)) * q
+            if used + padded > S:
+                break
+            L[r, j], Lp[r, j] = real, padded
+            used += padded
+        if not (L[r] != V).any():
+            L[r, order[0]], Lp[r, order[0]] = 0, 0
+    return L, Lp
+
+
+@pytest.mark.parametrize("B,P,S", [(1, 1, 1), (1, 4, 7), (3, 5, 16), (2, 8, 4096),
+                                   (3, 16, 4097), (2, 64, 8192), (4, 7, 12345),
+                                   (1, 2000, 30000), (2, 3000, 9000)])
+@pytest.mark.parametrize("mode", ["plain", "tight", "holes", "nopad", "int32"])
+def test_thd_fuzz(dev, B, P, S, mode):
+    rng = np.random.default_rng(hash((B, P, S, mode)) % 2**32)
+    q = int(rng.choice([1, 4, 8]))
+    L, Lp = rand_tables(rng, B, P, S, q, tight=(mode == "tight"), holes=(mode == "holes"),
+                        maxlen=(8 if P > 1000 else None))
+    if mode == "nopad":
+        check_thd(dev, L, None, S)
+    else:
+        check_thd(dev, L, Lp, S, torch.int32 if mode == "int32" else torch.int64)
+
+
+def test_thd_full_rows_absorb(dev):
+    # every row fully tight except the very last sequence: absorption fires
+    L = np.array([[100, 28], [64, 50]])
+    Lp = np.array([[100, 28], [64, 64]])
+    check_thd(dev, L, Lp, 128)
+
+
+def test_thd_workload_with_copies(dev):
+    w = synth.thd_tables()
+    S = w["S"]
+    B = w["seq_lens"].shape[0]
+    say("thd workload 3 via process_input_for_thd")
+    batch = {k: torch.from_numpy(w[k]).to(dev) for k in
+             ("input_ids", "labels", "position_ids", "seq_lens", "seq_lens_padded")}
+    batch["qkv_format"] = "thd"
+    out = psq.process_input_for_thd(batch)
+    ref = oracle.thd_tables(w["seq_lens"], w["seq_lens_padded"], S)
+    assert ref["status"] == 0
+    assert np.array_equal(out["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+    assert np.array_equal(out["cu_seqlens_padded"].cpu().numpy(), ref["cu_seqlens_padded"])
+    assert int(out["max_seqlen"]) == ref["max_seqlen"]
+    assert out["max_seqlen"].dtype == torch.int32 and out["max_seqlen"].dim() == 0
+    assert out["pad_between_seqs"] == bool(ref["pad_between_seqs"])
+    assert np.array_equal(out["padding_mask"].cpu().numpy().astype(np.uint8), ref["padding_mask"])
+    assert out["qkv_format"] == "thd"
+    for key in ("input_ids", "labels", "position_ids"):
+        want = oracle.copy_rows(w[key], 1, w[key].nbytes, w[key].nbytes)
+        got = out[key].cpu().numpy()
+        assert got.shape == (B * S,)
+        assert got.tobytes() == want.tobytes(), key
+
+
+def test_thd_embeddings_mrope_and_strided(dev):
+    rng = np.random.default_rng(11)
+    B, S, H, n_rope = 3, 40, 24, 3
+    emb = torch.randn((B, S, H), dtype=torch.bfloat16, device=dev)
+    pos = torch.from_numpy(rng.integers(0, 50, size=(n_rope, B, S))).to(dev)
+    wide = torch.from_numpy(rng.integers(0, 9, size=(B, S + 5))).to(dev)
+    labels = wide[:, :S]                                  # row-strided view
+    L = torch.tensor([[10, 20], [40, V], [5, V]], device=dev)
+    say("thd embeddings + mRoPE + strided labels")
+    out = psq.process_input_for_thd({"input_ids": emb, "labels": labels, "position_ids": pos,
+                                     "seq_lens": L})
+    assert out["input_ids"].shape == (B * S, H)
+    assert torch.equal(out["input_ids"].view(torch.int16), emb.reshape(B * S, H).view(torch.int16))
+    assert out["position_ids"].shape == (n_rope, 1, B * S)
+    assert torch.equal(out["position_ids"], pos.reshape(n_rope, 1, B * S))
+    got = out["labels"].cpu().numpy()
+    want = oracle.copy_rows(wide.cpu().numpy(), B, S * 8, (S + 5) * 8)
+    assert got.tobytes() == want.tobytes()
+    assert "cu_seqlens_padded" not in out
+    ref = oracle.thd_tables(L.cpu().numpy(), None, S)
+    assert np.array_equal(out["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+
+
+def test_stage_embedding_full(dev):
+    """Workload 5 at full size: doc-map layout, bf16 hidden [32,32768,4096]."""
+    w = synth.stage_embedding()
+    B, S, H = 32, 32768, 4096
+    say("workload 5 full size")
+    hidden = synth.stage_hidden(5, B, S, H, dev)
+    doc = torch.from_numpy(w["doc_ids"]).to(dev)
+    pos = torch.from_numpy(w["position_ids"]).to(dev)
+    out = psq.process_input_for_thd({"input_ids": hidden, "position_ids": pos, "doc_ids": doc})
+    ref = oracle.doc_segments(w["doc_ids"])
+    assert np.array_equal(out["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+    assert int(out["max_seqlen"]) == ref["max_seqlen"]
+    assert out["pad_between_seqs"] is False
+    assert np.array_equal(out["padding_mask"].cpu().numpy().astype(np.uint8), ref["padding_mask"])
+    flat = out["input_ids"]
+    assert flat.shape == (B * S, H)
+    # identity at full size, checked on the device ...
+    assert torch.equal(flat.view(torch.int16), hidden.reshape(B * S, H).view(torch.int16))
+    assert torch.equal(out["position_ids"], pos.reshape(-1))
+    # ... and sampled token rows through the oracle's copy
+    rng = np.random.default_rng(5)
+    for t in rng.integers(0, B * S, size=16).tolist() + [0, B * S - 1]:
+        src = hidden.reshape(B * S, H)[t].view(torch.int16).cpu().numpy()
+        want = oracle.copy_rows(src, 1, H * 2, H * 2)
+        assert flat[t].view(torch.int16).cpu().numpy().tobytes() == want.tobytes()
+    del hidden, flat, out
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# the squeeze into packs
+# ---------------------------------------------------------------------------
+
+def run_pack_raw(dev, src, off, rl, q, ps, C, fold, pad_token=0, order=None):
+    N = len(rl)
+    P = len(ps) - 1
+    t_src = torch.from_numpy(np.ascontiguousarray(src, dtype=np.int64)).to(dev) if len(src) else \
+        torch.zeros(1, dtype=torch.int64, device=dev)
+    t_off = torch.from_numpy(np.ascontiguousarray(off, dtype=np.int64)).to(dev)
+    t_rl = torch.from_numpy(np.ascontiguousarray(rl, dtype=np.int32)).to(dev)
+    t_ps = torch.from_numpy(np.ascontiguousarray(ps, dtype=np.int64)).to(dev)
+    t_od = torch.from_numpy(np.ascontiguousarray(order, dtype=np.int32)).to(dev) if order is not None else None
+    packed = torch.full((max(P, 1), C), -5, dtype=torch.int64, device=dev)
+    tm = torch.full((max(P, 1), C), 9, dtype=torch.uint8, device=dev)
+    csr = max(N + P, 1)
+    cu = torch.full((csr,), -7, dtype=torch.int32, device=dev)
+    cp = torch.full((csr,), -7, dtype=torch.int32, device=dev)
+    st = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, _lib.psq_pack_rows_workspace(N, P, C))
+    _lib.psq_pack_rows(t_src.data_ptr(), len(src), t_off.data_ptr(), t_rl.data_ptr(), N, q,
+                       t_od.data_ptr() if t_od is not None else None, t_ps.data_ptr(), P, C,
+                       int(fold), pad_token, packed.data_ptr(), tm.data_ptr(), cu.data_ptr(),
+                       cp.data_ptr(), st.data_ptr(), ws.data_ptr(), ws.numel(),
+                       torch.cuda.current_stream(dev).cuda_stream)
+    status = int(st.item())
+    if status != 0:
+        return {"status": status}
+    used = (int(ps[-1]) + P) if P else 0
+    return {"status": 0, "packed": packed[:P].cpu().numpy(), "token_mask": tm[:P].cpu().numpy(),
+            "cu_seqlens": cu[:used].cpu().numpy(), "cu_seqlens_padded": cp[:used].cpu().numpy()}
+
+
+def check_pack(dev, src, off, rl, q, ps, C, fold, pad_token=0, order=None, what=""):
+    say(f"pack {what} N={len(rl)} P={len(ps) - 1} q={q} C={C} fold={fold}")
+    got = run_pack_raw(dev, src, off, rl, q, ps, C, fold, pad_token, order)
+    ref = oracle.pack(src, off, rl, q, ps, C, fold=fold, pad_token=pad_token, order=order)
+    assert got["status"] == ref["status"]
+    if ref["status"] != 0:
+        return
+    for key in ("packed", "token_mask", "cu_seqlens", "cu_seqlens_padded"):
+        assert np.array_equal(got[key], ref[key]), key
+
+
+@pytest.mark.parametrize("C,fold", [(20, False), (36, True)])
+def test_pack_page_examples(dev, C, fold):
+    src = np.arange(100, 115)
+    check_pack(dev, src, [0, 5], [5, 10], 4, [0, 2], C, fold, what="page")
+
+
+def test_pack_workload_full(dev):
+    w = synth.pack_sources()
+    check_pack(dev, w["src"], w["src_off"], w["real_len"], w["q"], w["pack_start"],
+               w["capacity"], True, what="workload 4")
+
+
+@pytest.mark.parametrize("q,C,fold", [(1, 64, True), (3, 100, False), (8, 4096, True),
+                                      (64, 16384, True), (2, 9001, True), (5, 8191, False),
+                                      (64, 20000, True)])
+@pytest.mark.parametrize("ordered", [False, True])
+def test_pack_fuzz(dev, q, C, fold, ordered):
+    rng = np.random.default_rng(hash((q, C, fold, ordered)) % 2**32)
+    N = int(rng.integers(1, 700))
+    hi = max(1, C // 3)
+    rl = np.where(rng.random(N) < 0.05, 0, rng.integers(1, hi + 1, size=N)).astype(np.int32)
+    off = np.zeros(N, dtype=np.int64)
+    off[1:] = np.cumsum(rl[:-1])
+    src = rng.integers(0, 151936, size=int(rl.sum()) + 3)
+    order = rng.permutation(N).astype(np.int32) if ordered else None
+    members = order if ordered else np.arange(N)
+    padded = -(-rl[members].astype(np.int64) // q) * q
+    ps = synth.next_fit(padded, C)
+    check_pack(dev, src, off, rl, q, ps, C, fold, pad_token=int(rng.integers(-5, 5)),
+               order=order, what="fuzz")
+
+
+def test_pack_many_members_per_pack(dev):
+    # more than one LDS batch of members in a pack (q = 1, tiny sources)
+    rng = np.random.default_rng(3)
+    N = 3000
+    rl = rng.integers(0, 4, size=N).astype(np.int32)
+    off = np.zeros(N, dtype=np.int64)
+    off[1:] = np.cumsum(rl[:-1])
+    src = rng.integers(0, 1000, size=int(rl.sum()))
+    C = int(rl.sum()) + 17
+    check_pack(dev, src, off, rl, 1, [0, 1000, N], C, True, what="many members")
+
+
+@pytest.mark.parametrize("case", ["overflow", "empty", "pack_range", "order_range",
+                                  "src_range", "neg_len"])
+def test_pack_error_bits(dev, case):
+    src = np.arange(1, 7)
+    off = np.array([0, 3, 4])
+    rl = np.array([3, 1, 2])
+    q, ps, C, order = 2, [0, 2, 3], 8, None
+    if case == "overflow":
+        C = 5
+    elif case == "empty":
+        ps = [0, 0, 3]
+    elif case == "pack_range":
+        ps = [0, 4]
+    elif case == "order_range":
+        ps, order = [0, 3], [0, 1, 3]
+    elif case == "src_range":
+        off = np.array([0, 3, 5])
+    elif case == "neg_len":
+        rl = np.array([3, -2, 2])
+    check_pack(dev, src, off, rl, q, ps, C, True, order=order, what=case)
+
+
+def test_pack_no_packs(dev):
+    check_pack(dev, np.arange(3), [0], [3], 1, [0], 8, True, what="P=0")
+
+
+def test_pack_python_api(dev):
+    src = torch.arange(100, 115, dtype=torch.int64, device=dev)
+    out = psq.pack_rows(src, torch.tensor([0, 5], device=dev),
+                        torch.tensor([5, 10], dtype=torch.int32, device=dev), [0, 2],
+                        capacity=36, pad_to=4)
+    assert out["cu_seqlens"][0].cpu().tolist() == [0, 5, 15]
+    assert out["cu_seqlens_padded"][0].cpu().tolist() == [0, 8, 36]
+    assert int(out["token_mask"].sum()) == 15
+    with pytest.raises(ValueError, match="capacity"):
+        psq.pack_rows(src, torch.tensor([0, 5], device=dev),
+                      torch.tensor([5, 10], dtype=torch.int32, device=dev), [0, 2],
+                      capacity=16, pad_to=4)

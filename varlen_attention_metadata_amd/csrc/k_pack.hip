@@ -1,0 +1,247 @@
+// k_pack.hip -- the squeeze of padded sources into fixed-capacity packs.
+//
+// "Who packs the sequences: the loader, or the trainer?", What the data
+// looks like at each hop.  Trainer packs: each source is padded to a
+// multiple of q and the sources of a bin are laid end to end
+// (cu_seqlens [0,5,15], cu_seqlens_padded [0,8,20]).  Loader packs: the row
+// is always `capacity` wide, the tail is pad, token_mask is 1 where a token
+// counts, and the last padded boundary is set to the capacity
+// (cu_seqlens_padded [0,8,36]).
+//
+// Work layout: one 256-thread workgroup per (pack, chunk of 4096 slots).
+// The workgroup scans its pack's member lengths into LDS (256 members per
+// batch; a saturating scan so an overfull pack is detected exactly), then
+// every slot of its chunk finds its member with a binary search over the
+// member starts and takes either the member's token or the pad token.
+// Token-mask bytes are staged in LDS and leave as 16-byte stores.  The
+// chunk-0 workgroup of each pack also writes the pack's boundary arrays and
+// reports data errors; the last of those to finish publishes *status.
+// Every access is bounds-checked against the caller's sizes, so bad data
+// can only produce wrong values and status bits, never a stray access.
+#include "psq_device.hpp"
+#include "psq_internal.hpp"
+
+namespace psq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMembers = kThreads;       // members per LDS batch
+constexpr uint32_t kSlots = 4096;        // slots per workgroup
+constexpr int kPairs = 4;                // slot pairs per thread per step
+
+__device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat) {
+    const uint32_t s = a + b;
+    return s > sat ? sat : s;
+}
+
+// Inclusive wave scan with saturation at `sat` (<= 2^31, so no wrap).
+__device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
+    x = sat_add(x, (uint32_t)dpp0<0x111>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x112>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x114>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x118>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x142, 0xa>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x143, 0xc>((int)x), sat);
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads) void k_pack_rows(
+    const int64_t *__restrict__ src, int64_t src_len, const int64_t *__restrict__ src_off,
+    const int32_t *__restrict__ real_len, int64_t N, int32_t q,
+    const int32_t *__restrict__ order, const int64_t *__restrict__ pack_start, int64_t P,
+    int32_t C, int fold, int64_t pad_token, int64_t *__restrict__ packed,
+    uint8_t *__restrict__ tmask, int32_t *__restrict__ cu, int32_t *__restrict__ cp,
+    int32_t *__restrict__ status, WsHeader *__restrict__ ws, uint32_t n_chunks, int vec_out,
+    int vec_mask) {
+    __shared__ uint32_t m_start[kMembers];
+    __shared__ uint32_t m_real[kMembers];
+    __shared__ int64_t m_so[kMembers];
+    __shared__ __attribute__((aligned(16))) uint8_t s_mask[kSlots];
+    __shared__ uint32_t s_wsum[2][kWaves];
+    __shared__ uint32_t s_err, s_slot;
+
+    if (P == 0) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+        return;
+    }
+    const int64_t p = blockIdx.x / n_chunks;
+    const uint32_t c = blockIdx.x % n_chunks;
+    const bool leader = (c == 0);
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    const uint32_t sat = (uint32_t)C + 1u;
+    const uint32_t lo = c * kSlots;
+    const uint32_t hi = min((uint32_t)C, lo + kSlots);
+
+    const int64_t a = pack_start[p];
+    const int64_t b = pack_start[p + 1];
+    const bool range_ok = a >= 0 && b <= N && a <= b;
+    const int64_t k = range_ok ? b - a : 0;
+    if (threadIdx.x == 0) s_err = range_ok ? (k == 0 ? PSQ_DATA_EMPTY_PACK : 0u) : PSQ_DATA_BAD_INDEX;
+    for (uint32_t u = threadIdx.x * 16u; u < kSlots; u += kThreads * 16u)
+        *(u32x4 *)(s_mask + u) = u32x4{0u, 0u, 0u, 0u};
+
+    int64_t *__restrict__ row = packed + p * (int64_t)C;
+    const int64_t csr = a + p;            // this pack's first boundary entry
+    if (leader && range_ok && threadIdx.x == 0) {
+        cu[csr] = 0;
+        cp[csr] = 0;
+    }
+
+    uint32_t carry_pos = 0, carry_real = 0;
+    for (int64_t m0 = 0; m0 < k; m0 += kMembers) {
+        // ---- member lengths of this batch -> starts (saturating scan) ----
+        const int64_t j = m0 + threadIdx.x;
+        uint32_t real = 0, padded = 0;
+        int64_t so = 0;
+        bool readable = false;
+        uint32_t err = 0;
+        if (j < k) {
+            const int64_t i = order ? (int64_t)order[a + j] : a + j;
+            if (i < 0 || i >= N) {
+                err |= PSQ_DATA_BAD_INDEX;
+            } else {
+                int64_t r = real_len[i];
+                so = src_off[i];
+                if (r < 0) {
+                    err |= PSQ_DATA_BAD_LENGTH;
+                    r = 0;
+                }
+                if (so < 0 || so > src_len - r) {
+                    err |= PSQ_DATA_BAD_INDEX;
+                } else {
+                    readable = true;
+                }
+                const int64_t pd = (r + q - 1) / q * q;
+                padded = pd > (int64_t)sat ? sat : (uint32_t)pd;
+                real = r > (int64_t)sat ? sat : (uint32_t)r;
+            }
+        }
+        if (err) atomicOr(&s_err, err);
+        const uint32_t ip = wave_incl_sat(padded, sat);
+        const uint32_t ir = wave_incl_sat(real, sat);
+        if (lane == kWave - 1) {
+            s_wsum[0][w] = ip;
+            s_wsum[1][w] = ir;
+        }
+        __syncthreads();
+        uint32_t bp = 0, br = 0, tp = 0, tr = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            if (v == w) {
+                bp = tp;
+                br = tr;
+            }
+            tp = sat_add(tp, s_wsum[0][v], sat);
+            tr = sat_add(tr, s_wsum[1][v], sat);
+        }
+        const uint32_t incl_pos = sat_add(carry_pos, sat_add(bp, ip, sat), sat);
+        const uint32_t incl_real = sat_add(carry_real, sat_add(br, ir, sat), sat);
+        const uint32_t start = incl_pos >= padded ? incl_pos - padded : 0u;
+        m_start[threadIdx.x] = j < k ? start : 0xffffffffu;
+        m_real[threadIdx.x] = readable ? real : 0u;
+        m_so[threadIdx.x] = so;
+        if (leader && j < k) {
+            cu[csr + j + 1] = (int32_t)incl_real;
+            cp[csr + j + 1] = (fold && j == k - 1) ? C : (int32_t)incl_pos;
+        }
+        const uint32_t first = carry_pos;
+        carry_pos = sat_add(carry_pos, tp, sat);
+        carry_real = sat_add(carry_real, tr, sat);
+        __syncthreads();
+
+        // ---- slots owned by this batch's members --------------------------
+        const int64_t nb = min((int64_t)kMembers, k - m0);
+        const bool last_batch = m0 + kMembers >= k;
+        const uint32_t r_lo = max(lo, first);
+        const uint32_t r_hi = last_batch ? hi : min(hi, carry_pos);
+        if (r_lo < r_hi) {
+            const uint32_t base = r_lo & ~1u;
+            for (uint32_t u0 = base + 2u * threadIdx.x; u0 < r_hi; u0 += 2u * kThreads * kPairs) {
+                int64_t val[kPairs][2];
+                bool in[kPairs][2];
+#pragma unroll
+                for (int t = 0; t < kPairs; ++t) {
+                    const uint32_t u = u0 + 2u * kThreads * (uint32_t)t;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const uint32_t s = u + (uint32_t)e;
+                        in[t][e] = s >= r_lo && s < r_hi;
+                        val[t][e] = pad_token;
+                        if (in[t][e]) {
+                            uint32_t x = 0, y = (uint32_t)nb;
+                            while (y - x > 1) {
+                                const uint32_t m = (x + y) >> 1;
+                                if (m_start[m] <= s) x = m; else y = m;
+                            }
+                            const uint32_t off = s - m_start[x];
+                            const bool tok = off < m_real[x];
+                            if (tok) val[t][e] = src[m_so[x] + off];
+                            s_mask[s - lo] = tok ? 1 : 0;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < kPairs; ++t) {
+                    const uint32_t u = u0 + 2u * kThreads * (uint32_t)t;
+                    if (in[t][0] && in[t][1] && vec_out && ((p * (int64_t)C + u) & 1) == 0) {
+                        __builtin_nontemporal_store(i64x2{val[t][0], val[t][1]},
+                                                    (i64x2 *)(row + u));
+                    } else {
+                        if (in[t][0]) __builtin_nontemporal_store(val[t][0], row + u);
+                        if (in[t][1]) __builtin_nontemporal_store(val[t][1], row + u + 1);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- token mask of the chunk --------------------------------------
+    if (k > 0 && hi > lo) {
+        uint8_t *__restrict__ mrow = tmask + p * (int64_t)C;
+        const uint32_t len = hi - lo;
+        if (vec_mask && ((p * (int64_t)C + lo) % 16) == 0 && (len % 16) == 0) {
+            for (uint32_t u = threadIdx.x * 16u; u < len; u += kThreads * 16u)
+                __builtin_nontemporal_store(*(const u32x4 *)(s_mask + u), (u32x4 *)(mrow + lo + u));
+        } else {
+            for (uint32_t u = threadIdx.x; u < len; u += kThreads) mrow[lo + u] = s_mask[u];
+        }
+    }
+
+    if (leader) {
+        if (threadIdx.x == 0) {
+            uint32_t err = s_err;
+            if (carry_pos > (uint32_t)C) err |= PSQ_DATA_PACK_OVERFLOW;
+            if (err) or_relaxed(&ws->status, err);
+        }
+        if (finish_is_last(ws, (uint32_t)P, &s_slot) && threadIdx.x == 0) {
+            *status = (int32_t)ld_relaxed(&ws->status);
+            st_relaxed(&ws->status, 0u);
+            st_relaxed(&ws->done, 0u);
+        }
+    }
+}
+
+}  // namespace
+
+size_t pack_rows_workspace() { return 256; }
+
+hipError_t launch_pack_rows(const int64_t *src, int64_t src_len, const int64_t *src_off,
+                            const int32_t *real_len, int64_t N, int32_t q,
+                            const int32_t *order, const int64_t *pack_start, int64_t P,
+                            int32_t C, int fold, int64_t pad_token, int64_t *packed,
+                            uint8_t *tmask, int32_t *cu, int32_t *cp, int32_t *status,
+                            void *workspace, hipStream_t stream) {
+    const uint32_t n_chunks = (uint32_t)(((int64_t)C + kSlots - 1) / kSlots);
+    const uint64_t groups = P > 0 ? (uint64_t)P * n_chunks : 1ull;
+    const int vec_out = ((uintptr_t)packed % 16) == 0;
+    const int vec_mask = ((uintptr_t)tmask % 16) == 0;
+    hipLaunchKernelGGL(k_pack_rows, dim3((uint32_t)groups), dim3(kThreads), 0, stream, src,
+                       src_len, src_off, real_len, N, q, order, pack_start, P, C, fold,
+                       pad_token, packed, tmask, cu, cp, status, (WsHeader *)workspace,
+                       n_chunks, vec_out, vec_mask);
+    return hipGetLastError();
+}
+
+}  // namespace psq

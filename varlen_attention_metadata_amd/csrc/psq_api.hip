@@ -1,0 +1,170 @@
+// psq_api.hip -- the C ABI declared in include/psq.h: host-side argument
+// validation, workspace sizing and kernel dispatch.  Every check here runs
+// before the first HIP call, so a rejected call enqueues nothing.
+#include <string.h>
+
+#include "psq.h"
+#include "psq_internal.hpp"
+
+namespace {
+
+constexpr int64_t kI32Limit = (int64_t)1 << 31;
+
+bool valid_dtype(int d) { return d == PSQ_I32 || d == PSQ_I64; }
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int check_copies(const psq_copy *copies, int n_copies) {
+    if (n_copies < 0 || n_copies > PSQ_MAX_COPIES) return PSQ_ERR_ARG;
+    if (n_copies > 0 && copies == nullptr) return PSQ_ERR_ARG;
+    for (int i = 0; i < n_copies; ++i) {
+        const psq_copy &c = copies[i];
+        if (c.rows < 0 || c.row_bytes < 0) return PSQ_ERR_ARG;
+        if (c.rows == 0 || c.row_bytes == 0) continue;
+        if (c.src == nullptr || c.dst == nullptr) return PSQ_ERR_ARG;
+        if (c.rows > 1 && c.src_row_stride_bytes < c.row_bytes) return PSQ_ERR_ARG;
+        const int64_t dst_bytes = c.rows * c.row_bytes;
+        const int64_t src_span = (c.rows - 1) * c.src_row_stride_bytes + c.row_bytes;
+        if (overlaps(c.src, src_span, c.dst, dst_bytes)) return PSQ_ERR_ARG;
+    }
+    return PSQ_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PSQ_OK : PSQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *psq_status_string(int code, int is_status) {
+    if (!is_status) {
+        switch (code) {
+            case PSQ_OK: return "ok";
+            case PSQ_ERR_ARG: return "invalid argument (null pointer, negative size, bad enum)";
+            case PSQ_ERR_OVERFLOW: return "size does not fit int32 boundary arrays";
+            case PSQ_ERR_WORKSPACE: return "workspace missing or too small";
+            case PSQ_ERR_HIP: return "HIP runtime error while enqueuing";
+            default: return "unknown error code";
+        }
+    }
+    // data status bits: name the lowest set bit (callers see all bits too)
+    if (code == 0) return "ok";
+    if (code & PSQ_DATA_BAD_LENGTH) return "negative length, or real length above padded length";
+    if (code & PSQ_DATA_TABLE_MISMATCH) return "seq_lens and seq_lens_padded mark different unused slots";
+    if (code & PSQ_DATA_ROW_OVERFLOW) return "a row's padded lengths exceed the row length";
+    if (code & PSQ_DATA_EMPTY_ROW) return "a row holds no sequence";
+    if (code & PSQ_DATA_PACK_OVERFLOW) return "a pack's padded sources exceed its capacity";
+    if (code & PSQ_DATA_EMPTY_PACK) return "a pack has no member";
+    if (code & PSQ_DATA_BAD_INDEX) return "member, pack or source index out of range";
+    if (code & PSQ_DATA_WORKSPACE) return "workspace was not zero-filled before use";
+    return "unknown status bits";
+}
+
+int psq_workspace_init(void *workspace, size_t bytes, void *stream) {
+    if (bytes > 0 && workspace == nullptr) return PSQ_ERR_ARG;
+    return from_hip(psq::launch_zero_fill(workspace, bytes, (hipStream_t)stream));
+}
+
+size_t psq_params_from_doc_ids_workspace(int64_t B, int64_t S) {
+    if (B < 0 || S < 0) return 0;
+    return psq::doc_segments_workspace(B, S);
+}
+
+int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64_t S,
+                            int32_t *cu_seqlens, int32_t *num_segments, int32_t *max_seqlen,
+                            uint8_t *padding_mask, int32_t *status, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    if (B < 0 || S < 0 || !valid_dtype(doc_dtype)) return PSQ_ERR_ARG;
+    if (S > 0 && B > (kI32Limit - 1) / S) return PSQ_ERR_OVERFLOW;
+    if (cu_seqlens == nullptr || num_segments == nullptr || max_seqlen == nullptr)
+        return PSQ_ERR_ARG;
+    if (B * S > 0 && doc_ids == nullptr) return PSQ_ERR_ARG;
+    if (workspace == nullptr || workspace_bytes < psq::doc_segments_workspace(B, S))
+        return PSQ_ERR_WORKSPACE;
+    return from_hip(psq::launch_doc_segments(doc_ids, doc_dtype, B, S, cu_seqlens, nullptr,
+                                             num_segments, max_seqlen, padding_mask, status,
+                                             nullptr, workspace, (hipStream_t)stream));
+}
+
+size_t psq_process_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S) {
+    if (layout == nullptr || B < 0 || S < 0) return 0;
+    if (layout->kind == PSQ_LAYOUT_DOC_IDS) return psq::doc_segments_workspace(B, S);
+    return psq::thd_tables_workspace(B, S);
+}
+
+int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t *cu_seqlens,
+                    int32_t *cu_seqlens_padded, int32_t *num_seqs, int32_t *max_seqlen,
+                    int32_t *pad_between_seqs, uint8_t *padding_mask, const psq_copy *copies,
+                    int n_copies, int32_t *status, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    if (layout == nullptr || B < 0 || S < 0) return PSQ_ERR_ARG;
+    if (S > 0 && B > (kI32Limit - 1) / S) return PSQ_ERR_OVERFLOW;
+    if (cu_seqlens == nullptr || num_seqs == nullptr || max_seqlen == nullptr ||
+        pad_between_seqs == nullptr || status == nullptr)
+        return PSQ_ERR_ARG;
+    const int cc = check_copies(copies, n_copies);
+    if (cc != PSQ_OK) return cc;
+    const hipStream_t st = (hipStream_t)stream;
+
+    if (layout->kind == PSQ_LAYOUT_DOC_IDS) {
+        if (!valid_dtype(layout->doc_dtype)) return PSQ_ERR_ARG;
+        if (B * S > 0 && layout->doc_ids == nullptr) return PSQ_ERR_ARG;
+        if (workspace == nullptr || workspace_bytes < psq::doc_segments_workspace(B, S))
+            return PSQ_ERR_WORKSPACE;
+        hipError_t e = psq::launch_doc_segments(layout->doc_ids, layout->doc_dtype, B, S,
+                                                cu_seqlens, cu_seqlens_padded, num_seqs,
+                                                max_seqlen, padding_mask, status,
+                                                pad_between_seqs, workspace, st);
+        if (e != hipSuccess) return PSQ_ERR_HIP;
+        return from_hip(psq::launch_copies(copies, n_copies, st));
+    }
+    if (layout->kind != PSQ_LAYOUT_SEQ_LENS) return PSQ_ERR_ARG;
+    if (!valid_dtype(layout->lens_dtype) || layout->P < 0) return PSQ_ERR_ARG;
+    if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
+    if (layout->P > 0 && B > (kI32Limit - 2) / layout->P) return PSQ_ERR_OVERFLOW;
+    if (workspace == nullptr || workspace_bytes < psq::thd_tables_workspace(B, S))
+        return PSQ_ERR_WORKSPACE;
+    hipError_t e = psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
+                                          layout->lens_dtype, B, layout->P, S,
+                                          layout->pad_value, cu_seqlens, cu_seqlens_padded,
+                                          num_seqs, max_seqlen, pad_between_seqs,
+                                          padding_mask, status, workspace, st);
+    if (e != hipSuccess) return PSQ_ERR_HIP;
+    return from_hip(psq::launch_copies(copies, n_copies, st));
+}
+
+size_t psq_pack_rows_workspace(int64_t N, int64_t P, int32_t capacity) {
+    (void)N;
+    (void)P;
+    (void)capacity;
+    return psq::pack_rows_workspace();
+}
+
+int psq_pack_rows(const int64_t *src_tokens, int64_t src_len, const int64_t *src_offsets,
+                  const int32_t *real_len, int64_t N, int32_t pad_to, const int32_t *pack_order,
+                  const int64_t *pack_start, int64_t P, int32_t capacity, int fold,
+                  int64_t pad_token, int64_t *packed, uint8_t *token_mask, int32_t *cu_seqlens,
+                  int32_t *cu_seqlens_padded, int32_t *status, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    if (N < 0 || P < 0 || src_len < 0 || pad_to < 1 || capacity < 1) return PSQ_ERR_ARG;
+    if (capacity > (1 << 30)) return PSQ_ERR_ARG;
+    if (N + P >= kI32Limit) return PSQ_ERR_OVERFLOW;
+    if (pack_start == nullptr || status == nullptr) return PSQ_ERR_ARG;
+    if (P > 0 && (packed == nullptr || token_mask == nullptr || cu_seqlens == nullptr ||
+                  cu_seqlens_padded == nullptr))
+        return PSQ_ERR_ARG;
+    if (N > 0 && (src_offsets == nullptr || real_len == nullptr)) return PSQ_ERR_ARG;
+    if (src_len > 0 && src_tokens == nullptr) return PSQ_ERR_ARG;
+    if (workspace == nullptr || workspace_bytes < psq::pack_rows_workspace())
+        return PSQ_ERR_WORKSPACE;
+    return from_hip(psq::launch_pack_rows(src_tokens, src_len, src_offsets, real_len, N,
+                                          pad_to, pack_order, pack_start, P, capacity, fold,
+                                          pad_token, packed, token_mask, cu_seqlens,
+                                          cu_seqlens_padded, status, workspace,
+                                          (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// psq_device.hpp -- device-side building blocks shared by the psq kernels:
+// wave64 DPP scans, the workspace header, and the decoupled look-back over
+// per-tile descriptors.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psq {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Vector types (native clang vectors, so nontemporal builtins accept them).
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Workspace.  The first 256 bytes hold the header; per-tile descriptors
+// follow.  Every kernel that uses it leaves it zero-filled on completion (the
+// last workgroup to finish clears what the call used), so a workspace needs
+// one zero fill per allocation.
+// ---------------------------------------------------------------------------
+struct WsHeader {
+    uint32_t ticket;     // dynamic tile ids (dispatch order is not guaranteed)
+    uint32_t done;       // workgroups finished
+    uint32_t status;     // OR of data status bits
+    int32_t max;         // running maximum (segment / sequence length)
+    uint32_t flags;      // kernel-specific OR flags
+    int32_t n;           // kernel-specific scalars published by one tile
+    int32_t cu_last;
+    int32_t total;
+};
+constexpr size_t kWsDescOffset = 256;
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_relaxed(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_add_relaxed(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void or_relaxed(uint32_t *p, uint32_t v) {
+    __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void max_relaxed(int32_t *p, int32_t v) {
+    __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Claim a tile id: workgroups that got a smaller ticket were dispatched
+// earlier, so waiting on them always makes progress.
+__device__ __forceinline__ uint32_t claim_tile(WsHeader *ws, uint32_t *lds_slot) {
+    if (threadIdx.x == 0)
+        *lds_slot = fetch_add_relaxed(&ws->ticket, 1u);
+    __syncthreads();
+    return *lds_slot;
+}
+
+// Count this workgroup as finished.  Returns true in exactly one workgroup:
+// the last to finish, which then sees every earlier workgroup's writes to
+// the header (release on every increment, acquire on the last one).
+__device__ __forceinline__ bool finish_is_last(WsHeader *ws, uint32_t n_groups,
+                                               uint32_t *lds_slot) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t prev = __hip_atomic_fetch_add(&ws->done, 1u, __ATOMIC_RELEASE,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t last = (prev == n_groups - 1u);
+        if (last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // pairs with the releases
+        *lds_slot = last;
+    }
+    __syncthreads();
+    return *lds_slot != 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 scans with DPP.  Rows of 16 lanes are scanned with row_shr 1/2/4/8
+// (source lanes outside the row read the `old` operand, 0 here); rows are
+// then joined with row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3).
+// Values must be >= 0 for the max scan (0 is its identity).
+// ---------------------------------------------------------------------------
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ int dpp0(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, false);
+}
+
+__device__ __forceinline__ int wave_incl_sum(int x) {
+    x += dpp0<0x111>(x);
+    x += dpp0<0x112>(x);
+    x += dpp0<0x114>(x);
+    x += dpp0<0x118>(x);
+    x += dpp0<0x142, 0xa>(x);
+    x += dpp0<0x143, 0xc>(x);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_max(int x) {
+    x = max(x, dpp0<0x111>(x));
+    x = max(x, dpp0<0x112>(x));
+    x = max(x, dpp0<0x114>(x));
+    x = max(x, dpp0<0x118>(x));
+    x = max(x, dpp0<0x142, 0xa>(x));
+    x = max(x, dpp0<0x143, 0xc>(x));
+    return x;
+}
+
+// Lane l receives lane l-1's value; lane 0 receives `first`.
+__device__ __forceinline__ int wave_shr1(int x, int first) {
+    return __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int read_lane(int v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Decoupled look-back.  A descriptor is one 64-bit word, so relaxed agent-
+// scope atomics suffice (one word carries state and payload together):
+//   bits 63..62  state: 0 = not yet published, 1 = aggregate, 2 = inclusive
+//   bits 61..31  a: 31-bit sum
+//   bits 30..0   b: 31-bit second value (summed, or latest non-zero wins)
+// The combine of (a, b) pairs adds the a's; the b's either add too or the
+// later non-zero b wins.  Both are associative with identity (0, 0).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kDescAgg = 1ull << 62;
+constexpr uint64_t kDescIncl = 2ull << 62;
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ uint64_t desc_pack(uint64_t state, uint32_t a, uint32_t b) {
+    return state | ((uint64_t)(a & 0x7fffffffu) << 31) | (uint64_t)(b & 0x7fffffffu);
+}
+__device__ __forceinline__ uint32_t desc_a(uint64_t d) { return (uint32_t)(d >> 31) & 0x7fffffffu; }
+__device__ __forceinline__ uint32_t desc_b(uint64_t d) { return (uint32_t)d & 0x7fffffffu; }
+
+// Run by one full wave.  Returns the exclusive prefix (a, b) of tile `tile`
+// over tiles 0..tile-1 and sets *timed_out when a predecessor never
+// published within the spin bound (only possible with a dirty workspace).
+// kSumB selects the combine of b: summed (true) or latest non-zero (false).
+template <bool kSumB>
+__device__ inline void lookback(const uint64_t *desc, uint32_t tile, uint32_t *out_a,
+                                uint32_t *out_b, bool *timed_out) {
+    const int lane = lane_id();
+    uint32_t acc_a = 0, acc_b = 0;
+    int64_t base = (int64_t)tile - 1;
+    uint32_t spins = 0;
+    bool expired = false;
+    while (base >= 0) {
+        const int64_t idx = base - lane;
+        uint64_t d = kDescIncl;                 // before tile 0: inclusive identity
+        if (idx >= 0) {
+            d = ld_relaxed(desc + idx);
+            while ((d >> 62) == 0) {
+                if (++spins > kSpinLimit) {
+                    expired = true;
+                    d = kDescIncl;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                d = ld_relaxed(desc + idx);
+            }
+        }
+        // nearest lane holding an inclusive prefix
+        const uint64_t incl = __ballot((d >> 62) == 2);
+        const int stop = incl ? __builtin_ctzll(incl) : kWave - 1;
+        // combine lanes 0..stop (nearest first): sums add; b from the
+        // nearest lane with a non-zero b
+        const bool use = lane <= stop;
+        const uint32_t a = use ? desc_a(d) : 0u;
+        const uint32_t b = use ? desc_b(d) : 0u;
+        const uint32_t sum = (uint32_t)wave_incl_sum((int)a);
+        acc_a += (uint32_t)read_lane((int)sum, kWave - 1);
+        if constexpr (kSumB) {
+            const uint32_t bsum = (uint32_t)wave_incl_sum((int)b);
+            acc_b += (uint32_t)read_lane((int)bsum, kWave - 1);
+        } else {
+            const uint64_t has_b = __ballot(b != 0u);
+            uint32_t win_b = 0;
+            if (has_b)
+                win_b = (uint32_t)read_lane((int)b, __builtin_ctzll(has_b));
+            if (acc_b == 0u)
+                acc_b = win_b;
+        }
+        if (incl)
+            break;
+        base -= kWave;
+    }
+    *out_a = acc_a;
+    *out_b = acc_b;
+    *timed_out = __ballot(expired) != 0;
+}
+
+}  // namespace psq
