@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Throughput of the packed-sequence (THD) metadata path on one MI355X.
+
+One step is one ``psq_process_thd`` call on the pipeline-stage embedding
+workload: a document map int32 [32, 32768] (docs of length U{1..24},
+trailing pad U{0..16} per row) with bf16 hidden states [32, 32768, 4096]
+and int64 position ids, collapsed to THD [1048576, 4096] with cu_seqlens,
+max_seqlen and the padding mask -- one fused kernel launch.  Inputs are
+resident in HBM before timing starts.  The other four workloads are timed
+too and reported under ``per_config`` (the document maps [4, 64] and
+[8, 4096], the length tables with 3 collapsed int64 tensors, and the
+squeeze of 65536 sources into 16384-slot packs).
+
+Prints one JSON line.  ``roofline`` relates the algorithmic bytes of one
+launch (each input read once, each output written once) to the launch's
+average duration from HIP events on the launch stream; ``cpu_baseline`` is
+the CPU oracle on a bounded sample of the same workload, on one host core.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "packed tokens/sec (G tok/s) + achieved HBM GB/s vs MI355X peak, per config"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stage_embedding.json")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources: stored HBM counter figures are only used while
+    the kernels they were taken on are unchanged."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "varlen_attention_metadata_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--per-config-iters", type=int, default=50)
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events around each launch on the launch stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        t = self.torch
+        self.a = t.cuda.Event(enable_timing=True)
+        self.b = t.cuda.Event(enable_timing=True)
+        self.a.record(t.cuda.current_stream())
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.torch.cuda.current_stream())
+        self.pairs.append((self.a, self.b))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        v = [a.elapsed_time(b) for a, b in self.pairs]
+        return sum(v) / len(v), min(v)
+
+
+# ---------------------------------------------------------------------------
+# workloads: each returns (call, tokens_per_call, algorithmic_bytes, info)
+# ---------------------------------------------------------------------------
+
+def setup_stage_embedding(torch, psq, lib, synth, dev):
+    B, S, H = 32, 32768, 4096
+    w = synth.stage_embedding(5, B, S)
+    T = B * S
+    doc = torch.from_numpy(w["doc_ids"]).to(dev)
+    pos = torch.from_numpy(w["position_ids"]).to(dev)
+    hidden = synth.stage_hidden(5, B, S, H, dev)
+    out_h = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    out_p = torch.empty(T, dtype=torch.int64, device=dev)
+    cu = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    cp = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    mask = torch.empty(T, dtype=torch.bool, device=dev)
+    scal = torch.zeros(4, dtype=torch.int32, device=dev)
+    layout = lib.make_layout(lib.LAYOUT_DOC_IDS, doc_ids=doc.data_ptr(), doc_dtype=lib.I32)
+    copies, n_c = lib.make_copies([
+        (hidden.data_ptr(), out_h.data_ptr(), 1, hidden.numel() * 2, hidden.numel() * 2),
+        (pos.data_ptr(), out_p.data_ptr(), 1, pos.numel() * 8, pos.numel() * 8)])
+    ws = psq.workspace_for(dev, lib.psq_process_thd_workspace(layout, B, S))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    sp = scal.data_ptr()
+
+    def call():
+        lib.psq_process_thd(layout, B, S, cu.data_ptr(), cp.data_ptr(), sp, sp + 4, sp + 8,
+                            mask.data_ptr(), copies, n_c, sp + 12, ws.data_ptr(), ws.numel(),
+                            stream)
+
+    call()
+    n, mx, _, st = scal.cpu().tolist()
+    assert st == 0, st
+    algo = 4 * T + 4 * T * H + 16 * T + T + 8 * (n + 1) + 16
+    info = {"workload": "stage_embedding", "B": B, "S": S, "H": H, "num_segments": n,
+            "max_seqlen": mx}
+    keep = {"doc": doc, "pos": pos, "hidden": hidden, "out": (out_h, out_p, cu, cp, mask, scal, ws),
+            "host": w}
+    return call, T, algo, info, keep
+
+
+def setup_doc_map(torch, psq, lib, synth, dev, which):
+    d = synth.doc_map_small() if which == 1 else synth.doc_map_medium()
+    B, S = d.shape
+    doc = torch.from_numpy(d).to(dev)
+    cu = torch.empty(B * S + 1, dtype=torch.int32, device=dev)
+    scal = torch.zeros(4, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, lib.psq_params_from_doc_ids_workspace(B, S))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    sp = scal.data_ptr()
+
+    def call():
+        lib.psq_params_from_doc_ids(doc.data_ptr(), lib.I32, B, S, cu.data_ptr(), sp, sp + 4,
+                                    None, sp + 8, ws.data_ptr(), ws.numel(), stream)
+
+    call()
+    n = int(scal[0].item())
+    algo = 4 * B * S + 4 * (n + 1) + 12
+    name = "doc_map_small" if which == 1 else "doc_map_medium"
+    return call, B * S, algo, {"workload": name, "B": B, "S": S, "num_segments": n}, (doc, cu, scal, ws)
+
+
+def setup_thd(torch, psq, lib, synth, dev):
+    w = synth.thd_tables()
+    S = w["S"]
+    B, P = w["seq_lens"].shape
+    T = B * S
+    t = {k: torch.from_numpy(w[k]).to(dev) for k in
+         ("input_ids", "labels", "position_ids", "seq_lens", "seq_lens_padded")}
+    outs = {k: torch.empty(T, dtype=torch.int64, device=dev) for k in ("input_ids", "labels", "position_ids")}
+    cu = torch.empty(B * P + 1, dtype=torch.int32, device=dev)
+    cp = torch.empty(B * P + 1, dtype=torch.int32, device=dev)
+    mask = torch.empty(T, dtype=torch.bool, device=dev)
+    scal = torch.zeros(4, dtype=torch.int32, device=dev)
+    layout = lib.make_layout(lib.LAYOUT_SEQ_LENS, t["seq_lens"].data_ptr(),
+                             t["seq_lens_padded"].data_ptr(), lib.I64, P, -1000)
+    copies, n_c = lib.make_copies([(t[k].data_ptr(), outs[k].data_ptr(), 1, T * 8, T * 8)
+                                   for k in ("input_ids", "labels", "position_ids")])
+    ws = psq.workspace_for(dev, lib.psq_process_thd_workspace(layout, B, S))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    sp = scal.data_ptr()
+
+    def call():
+        lib.psq_process_thd(layout, B, S, cu.data_ptr(), cp.data_ptr(), sp, sp + 4, sp + 8,
+                            mask.data_ptr(), copies, n_c, sp + 12, ws.data_ptr(), ws.numel(),
+                            stream)
+
+    call()
+    n, _, _, st = scal.cpu().tolist()
+    assert st == 0, st
+    algo = 16 * B * P + 48 * T + T + 8 * (n + 1) + 16
+    return call, T, algo, {"workload": "thd_tables", "B": B, "S": S, "P": P, "num_seqs": n}, \
+        (t, outs, cu, cp, mask, scal, ws)
+
+
+def setup_pack(torch, psq, lib, synth, dev):
+    w = synth.pack_sources()
+    C, q = w["capacity"], w["q"]
+    N = w["real_len"].size
+    P = w["pack_start"].size - 1
+    src = torch.from_numpy(w["src"]).to(dev)
+    off = torch.from_numpy(w["src_off"]).to(dev)
+    rl = torch.from_numpy(w["real_len"]).to(dev)
+    ps = torch.from_numpy(w["pack_start"]).to(dev)
+    packed = torch.empty((P, C), dtype=torch.int64, device=dev)
+    tm = torch.empty((P, C), dtype=torch.uint8, device=dev)
+    cu = torch.empty(N + P, dtype=torch.int32, device=dev)
+    cp = torch.empty(N + P, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, lib.psq_pack_rows_workspace(N, P, C))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        lib.psq_pack_rows(src.data_ptr(), src.numel(), off.data_ptr(), rl.data_ptr(), N, q,
+                          None, ps.data_ptr(), P, C, 1, 0, packed.data_ptr(), tm.data_ptr(),
+                          cu.data_ptr(), cp.data_ptr(), st.data_ptr(), ws.data_ptr(),
+                          ws.numel(), stream)
+
+    call()
+    assert int(st.item()) == 0
+    real = int(w["real_len"].sum())
+    algo = 8 * real + 8 * N + 4 * N + 8 * (P + 1) + 9 * P * C + 8 * (N + P) + 4
+    info = {"workload": "pack_sources", "N": N, "P": P, "capacity": C, "pad_to": q,
+            "real_tokens": real}
+    return call, P * C, algo, info, (src, off, rl, ps, packed, tm, cu, cp, st, ws)
+
+
+def measure(torch, call, iters, flush=None):
+    timer = Timer(torch)
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        with timer:
+            call()
+    return timer.mean_ms()
+
+
+def roofline(algo_bytes, mean_ms, traffic=None):
+    gbs = algo_bytes / (mean_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def cpu_baseline(torch, keep):
+    """The oracle on 8 of the 32 rows of the stage-embedding workload."""
+    import numpy as np
+
+    import oracle
+    doc_np = keep["host"]["doc_ids"]
+    hidden = keep["hidden"]
+    rows = 8
+    H = hidden.shape[2]
+    sample_doc = np.ascontiguousarray(doc_np[:rows])
+    sample_h = hidden[:rows].contiguous().view(torch.int16).cpu().numpy()
+    sample_p = keep["host"]["position_ids"][:rows]
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.doc_segments(sample_doc)
+        oracle.copy_rows(sample_h, 1, sample_h.nbytes, sample_h.nbytes)
+        oracle.copy_rows(sample_p, 1, sample_p.nbytes, sample_p.nbytes)
+        times.append(time.perf_counter() - t0)
+    t = sorted(times)[1]
+    tokens = rows * doc_np.shape[1]
+    return {"value": round(tokens / t / 1e9, 6), "unit": "Gtok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of 32 rows ({tokens} tokens, {rows * doc_np.shape[1] * H * 2 >> 20} MiB "
+                      f"of bf16 hidden): segmentation + mask + both collapses, median of 3, "
+                      f"single-threaded C at -O2",
+            "seconds": round(t, 3), "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import varlen_attention_metadata_amd as psq
+    from varlen_attention_metadata_amd import _lib as lib
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    call, tokens, algo, info, keep = setup_stage_embedding(torch, psq, lib, synth, dev)
+    print(f"[bench] stage_embedding ready: {algo / 1e9:.2f} GB per step", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        with timer:
+            call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    k_mean, k_min = timer.mean_ms()
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, kernel {k_mean:.3f} ms",
+          file=sys.stderr, flush=True)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_per_step * 1e-3) / 1e9, 4),
+        "unit": "Gtok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic (seeded generators; bf16 hidden N(0,1) drawn on the device)",
+        "config": dict(info, **{"algorithmic_bytes_per_step": algo,
+                                "hbm_gbs_per_step": round(algo / (ms_per_step * 1e-3) / 1e9, 1)}),
+        "roofline": dict(roofline(algo, k_mean, traffic),
+                         kernel="k_doc_segments_copy<int> (segmentation + mask + collapse, one launch)",
+                         kernel_ms_mean=round(k_mean, 4), kernel_ms_min=round(k_min, 4)),
+    }
+
+    if not args.no_per_config:
+        per = {}
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def flush():
+            flush_buf.fill_(1)
+
+        for name, setup, do_flush in (
+                ("doc_map_small", lambda: setup_doc_map(torch, psq, lib, synth, dev, 1), False),
+                ("doc_map_medium", lambda: setup_doc_map(torch, psq, lib, synth, dev, 2), False),
+                ("thd_tables", lambda: setup_thd(torch, psq, lib, synth, dev), False),
+                ("pack_sources", lambda: setup_pack(torch, psq, lib, synth, dev), True)):
+            c_call, c_tok, c_algo, c_info, c_keep = setup()
+            for _ in range(5):
+                c_call()
+            m, mn = measure(torch, c_call, args.per_config_iters, flush if do_flush else None)
+            per[name] = dict(c_info, **{
+                "us_mean": round(m * 1e3, 2), "us_min": round(mn * 1e3, 2),
+                "gtok_s": round(c_tok / (m * 1e-3) / 1e9, 4), "tokens_per_call": c_tok,
+                "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m)})
+            print(f"[bench] {name}: {m * 1e3:.2f} us", file=sys.stderr, flush=True)
+            del c_keep
+        per["stage_embedding"] = {"us_mean": round(k_mean * 1e3, 2), "gtok_s": result["value"],
+                                  "roofline": roofline(algo, k_mean, traffic)}
+        result["per_config"] = per
+        del flush_buf
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(torch, keep)
+        print(f"[bench] cpu baseline: {result['cpu_baseline']['seconds']} s", file=sys.stderr, flush=True)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

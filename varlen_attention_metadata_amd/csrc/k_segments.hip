@@ -18,6 +18,7 @@
 // a decoupled look-back whose descriptors carry (boundary count, last
 // boundary + 1), so the compaction and the longest-segment reduction finish
 // in the same pass.
+#include "psq_copy.hpp"
 #include "psq_device.hpp"
 #include "psq_internal.hpp"
 
@@ -84,12 +85,25 @@ __device__ __forceinline__ T bcast_lane(T x, int lane) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_doc_segments(
+struct DocSegArgs {
+    const T *doc;
+    uint32_t S, total, n_tiles;
+    int vec_in, vec_mask;
+    int32_t *cu, *cu2, *num_segments, *max_seqlen;
+    uint8_t *mask;
+    int32_t *status, *pad_between;
+    WsHeader *ws;
+};
+
+// One tile per workgroup; `n_groups` is the number of workgroups running
+// this body (the launch may append copy workgroups after them).
+template <typename T>
+__device__ __forceinline__ void doc_segments_body(
     const T *__restrict__ doc, uint32_t S, uint32_t total, uint32_t n_tiles, int vec_in,
     int vec_mask, int32_t *__restrict__ cu, int32_t *__restrict__ cu2,
     int32_t *__restrict__ num_segments, int32_t *__restrict__ max_seqlen,
     uint8_t *__restrict__ mask, int32_t *__restrict__ status,
-    int32_t *__restrict__ pad_between, WsHeader *__restrict__ ws) {
+    int32_t *__restrict__ pad_between, WsHeader *__restrict__ ws, uint32_t n_groups) {
     __shared__ uint32_t s_slot;
     __shared__ uint32_t s_wcnt[kWaves], s_wlast[kWaves];
     __shared__ uint32_t s_ex_a, s_ex_b;
@@ -262,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void k_doc_segments(
         if (s_err) or_relaxed(&ws->status, s_err);
     }
 
-    if (finish_is_last(ws, gridDim.x, &s_slot)) {
+    if (finish_is_last(ws, n_groups, &s_slot)) {
         if (threadIdx.x == 0) {
             *max_seqlen = (int32_t)ld_relaxed((const uint32_t *)&ws->max);
             const uint32_t st = ld_relaxed(&ws->status);
@@ -278,6 +292,45 @@ __global__ __launch_bounds__(kThreads) void k_doc_segments(
     }
 }
 
+#define PSQ_DOC_ARGS(a)                                                                       \
+    a.doc, a.S, a.total, a.n_tiles, a.vec_in, a.vec_mask, a.cu, a.cu2, a.num_segments,       \
+        a.max_seqlen, a.mask, a.status, a.pad_between, a.ws
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_doc_segments(DocSegArgs<T> a) {
+    doc_segments_body<T>(PSQ_DOC_ARGS(a), gridDim.x);
+}
+
+// The same tiles followed, in one grid, by the 16-byte dense copies of the
+// THD collapse: one launch per call instead of two.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_doc_segments_copy(DocSegArgs<T> a, uint32_t n_meta,
+                                                                CopyBatch batch) {
+    if (blockIdx.x < n_meta)
+        doc_segments_body<T>(PSQ_DOC_ARGS(a), n_meta);
+    else
+        copy_group<u32x4, true>(batch, (int64_t)blockIdx.x - n_meta);
+}
+#undef PSQ_DOC_ARGS
+
+template <typename T>
+hipError_t launch_typed(DocSegArgs<T> a, const psq_copy *copies, int n_copies,
+                        hipStream_t stream) {
+    const uint32_t n_meta = a.n_tiles > 0 ? a.n_tiles : 1u;
+    CopyPlan plan;
+    plan_copies(copies, n_copies, &plan);
+    if (plan.groups[0] > 0) {
+        const uint64_t grid = (uint64_t)n_meta + (uint64_t)plan.groups[0];
+        hipLaunchKernelGGL(k_doc_segments_copy<T>, dim3((uint32_t)grid), dim3(kThreads), 0,
+                           stream, a, n_meta, plan.batch[0]);
+    } else {
+        hipLaunchKernelGGL(k_doc_segments<T>, dim3(n_meta), dim3(kThreads), 0, stream, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_copy_plan(plan, 1, stream);
+}
+
 }  // namespace
 
 size_t doc_segments_workspace(int64_t B, int64_t S) {
@@ -289,23 +342,22 @@ size_t doc_segments_workspace(int64_t B, int64_t S) {
 hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_t S,
                                int32_t *cu, int32_t *cu2, int32_t *num_segments,
                                int32_t *max_seqlen, uint8_t *mask, int32_t *status,
-                               int32_t *pad_between, void *workspace, hipStream_t stream) {
+                               int32_t *pad_between, void *workspace, const psq_copy *copies,
+                               int n_copies, hipStream_t stream) {
     const uint32_t total = (uint32_t)(B * S);
     const uint32_t n_tiles = (total + kTile - 1) / kTile;
-    const dim3 grid(n_tiles > 0 ? n_tiles : 1);
     const int vec_in = ((uintptr_t)doc % 16) == 0;
     const int vec_mask = ((uintptr_t)mask % 4) == 0;
     WsHeader *ws = (WsHeader *)workspace;
     if (doc_dtype == PSQ_I32) {
-        hipLaunchKernelGGL(k_doc_segments<int32_t>, grid, dim3(kThreads), 0, stream,
-                           (const int32_t *)doc, (uint32_t)S, total, n_tiles, vec_in, vec_mask,
-                           cu, cu2, num_segments, max_seqlen, mask, status, pad_between, ws);
-    } else {
-        hipLaunchKernelGGL(k_doc_segments<int64_t>, grid, dim3(kThreads), 0, stream,
-                           (const int64_t *)doc, (uint32_t)S, total, n_tiles, vec_in, vec_mask,
-                           cu, cu2, num_segments, max_seqlen, mask, status, pad_between, ws);
+        DocSegArgs<int32_t> a{(const int32_t *)doc, (uint32_t)S, total, n_tiles, vec_in,
+                              vec_mask, cu, cu2, num_segments, max_seqlen, mask, status,
+                              pad_between, ws};
+        return launch_typed(a, copies, n_copies, stream);
     }
-    return hipGetLastError();
+    DocSegArgs<int64_t> a{(const int64_t *)doc, (uint32_t)S, total, n_tiles, vec_in, vec_mask,
+                          cu, cu2, num_segments, max_seqlen, mask, status, pad_between, ws};
+    return launch_typed(a, copies, n_copies, stream);
 }
 
 }  // namespace psq

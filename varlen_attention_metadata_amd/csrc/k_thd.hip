@@ -26,6 +26,7 @@
 // carrying (sequence count, real-token sum) and writes the row's entries of
 // cu_seqlens / cu_seqlens_padded.  The last workgroup to finish applies the
 // absorption and writes the scalars.
+#include "psq_copy.hpp"
 #include "psq_device.hpp"
 #include "psq_internal.hpp"
 
@@ -148,12 +149,27 @@ __device__ __forceinline__ uint32_t row_batch(RowLds &s, const TL *__restrict__ 
 }
 
 template <typename TL>
-__global__ __launch_bounds__(kThreads) void k_thd_tables(
+struct ThdArgs {
+    const TL *L, *Lp;
+    uint32_t B, P, S;
+    int64_t pad_value;
+    uint32_t n_chunks;
+    int vec_mask;
+    int32_t *cu, *cp, *num_seqs, *max_seqlen, *pad_between;
+    uint8_t *mask;
+    int32_t *status;
+    WsHeader *ws;
+};
+
+// One (row, chunk) per workgroup; `n_groups` is the number of workgroups
+// running this body (the launch may append copy workgroups after them).
+template <typename TL>
+__device__ __forceinline__ void thd_tables_body(
     const TL *__restrict__ L, const TL *__restrict__ Lp, uint32_t B, uint32_t P, uint32_t S,
     int64_t pad_value, uint32_t n_chunks, int vec_mask, int32_t *__restrict__ cu,
     int32_t *__restrict__ cp, int32_t *__restrict__ num_seqs, int32_t *__restrict__ max_seqlen,
     int32_t *__restrict__ pad_between, uint8_t *__restrict__ mask, int32_t *__restrict__ status,
-    WsHeader *__restrict__ ws) {
+    WsHeader *__restrict__ ws, uint32_t n_groups) {
     __shared__ RowLds s;
     __shared__ __attribute__((aligned(16))) uint8_t s_mask[kSlots];
     __shared__ uint32_t s_slot;
@@ -301,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void k_thd_tables(
         or_relaxed(&ws->status, PSQ_DATA_WORKSPACE);
     }
 
-    if (finish_is_last(ws, gridDim.x, &s_slot)) {
+    if (finish_is_last(ws, n_groups, &s_slot)) {
         if (threadIdx.x == 0) {
             const uint32_t st = ld_relaxed(&ws->status);
             const uint32_t n = ld_relaxed((const uint32_t *)&ws->n);
@@ -337,6 +353,44 @@ __global__ __launch_bounds__(kThreads) void k_thd_tables(
     }
 }
 
+#define PSQ_THD_ARGS(a)                                                                       \
+    a.L, a.Lp, a.B, a.P, a.S, a.pad_value, a.n_chunks, a.vec_mask, a.cu, a.cp, a.num_seqs,    \
+        a.max_seqlen, a.pad_between, a.mask, a.status, a.ws
+
+template <typename TL>
+__global__ __launch_bounds__(kThreads) void k_thd_tables(ThdArgs<TL> a) {
+    thd_tables_body<TL>(PSQ_THD_ARGS(a), gridDim.x);
+}
+
+// The same workgroups followed, in one grid, by the 16-byte dense copies of
+// the THD collapse: one launch per call instead of two.
+template <typename TL>
+__global__ __launch_bounds__(kThreads) void k_thd_tables_copy(ThdArgs<TL> a, uint32_t n_meta,
+                                                              CopyBatch batch) {
+    if (blockIdx.x < n_meta)
+        thd_tables_body<TL>(PSQ_THD_ARGS(a), n_meta);
+    else
+        copy_group<u32x4, true>(batch, (int64_t)blockIdx.x - n_meta);
+}
+#undef PSQ_THD_ARGS
+
+template <typename TL>
+hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, int n_copies,
+                        hipStream_t stream) {
+    CopyPlan plan;
+    plan_copies(copies, n_copies, &plan);
+    if (plan.groups[0] > 0) {
+        const uint64_t grid = (uint64_t)n_meta + (uint64_t)plan.groups[0];
+        hipLaunchKernelGGL(k_thd_tables_copy<TL>, dim3((uint32_t)grid), dim3(kThreads), 0,
+                           stream, a, n_meta, plan.batch[0]);
+    } else {
+        hipLaunchKernelGGL(k_thd_tables<TL>, dim3(n_meta), dim3(kThreads), 0, stream, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_copy_plan(plan, 1, stream);
+}
+
 }  // namespace
 
 size_t thd_tables_workspace(int64_t B, int64_t /*S*/) {
@@ -347,24 +401,23 @@ hipError_t launch_thd_tables(const void *L, const void *Lp, int lens_dtype, int6
                              int64_t P, int64_t S, int64_t pad_value, int32_t *cu,
                              int32_t *cp, int32_t *num_seqs, int32_t *max_seqlen,
                              int32_t *pad_between, uint8_t *mask, int32_t *status,
-                             void *workspace, hipStream_t stream) {
+                             void *workspace, const psq_copy *copies, int n_copies,
+                             hipStream_t stream) {
     const uint32_t n_chunks = S > 0 ? (uint32_t)((S + kSlots - 1) / kSlots) : 1u;
     const uint64_t groups = (uint64_t)B * n_chunks;
-    const dim3 grid((uint32_t)(groups > 0 ? groups : 1));
+    const uint32_t n_meta = (uint32_t)(groups > 0 ? groups : 1);
     const int vec_mask = ((uintptr_t)mask % 16) == 0;
     WsHeader *ws = (WsHeader *)workspace;
     if (lens_dtype == PSQ_I64) {
-        hipLaunchKernelGGL(k_thd_tables<int64_t>, grid, dim3(kThreads), 0, stream,
-                           (const int64_t *)L, (const int64_t *)Lp, (uint32_t)B, (uint32_t)P,
+        ThdArgs<int64_t> a{(const int64_t *)L, (const int64_t *)Lp, (uint32_t)B, (uint32_t)P,
                            (uint32_t)S, pad_value, n_chunks, vec_mask, cu, cp, num_seqs,
-                           max_seqlen, pad_between, mask, status, ws);
-    } else {
-        hipLaunchKernelGGL(k_thd_tables<int32_t>, grid, dim3(kThreads), 0, stream,
-                           (const int32_t *)L, (const int32_t *)Lp, (uint32_t)B, (uint32_t)P,
-                           (uint32_t)S, pad_value, n_chunks, vec_mask, cu, cp, num_seqs,
-                           max_seqlen, pad_between, mask, status, ws);
+                           max_seqlen, pad_between, mask, status, ws};
+        return launch_typed(a, n_meta, copies, n_copies, stream);
     }
-    return hipGetLastError();
+    ThdArgs<int32_t> a{(const int32_t *)L, (const int32_t *)Lp, (uint32_t)B, (uint32_t)P,
+                       (uint32_t)S, pad_value, n_chunks, vec_mask, cu, cp, num_seqs,
+                       max_seqlen, pad_between, mask, status, ws};
+    return launch_typed(a, n_meta, copies, n_copies, stream);
 }
 
 }  // namespace psq

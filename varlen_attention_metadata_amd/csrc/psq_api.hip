@@ -86,7 +86,8 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_doc_segments(doc_ids, doc_dtype, B, S, cu_seqlens, nullptr,
                                              num_segments, max_seqlen, padding_mask, status,
-                                             nullptr, workspace, (hipStream_t)stream));
+                                             nullptr, workspace, nullptr, 0,
+                                             (hipStream_t)stream));
 }
 
 size_t psq_process_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S) {
@@ -114,12 +115,11 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t 
         if (B * S > 0 && layout->doc_ids == nullptr) return PSQ_ERR_ARG;
         if (workspace == nullptr || workspace_bytes < psq::doc_segments_workspace(B, S))
             return PSQ_ERR_WORKSPACE;
-        hipError_t e = psq::launch_doc_segments(layout->doc_ids, layout->doc_dtype, B, S,
-                                                cu_seqlens, cu_seqlens_padded, num_seqs,
-                                                max_seqlen, padding_mask, status,
-                                                pad_between_seqs, workspace, st);
-        if (e != hipSuccess) return PSQ_ERR_HIP;
-        return from_hip(psq::launch_copies(copies, n_copies, st));
+        return from_hip(psq::launch_doc_segments(layout->doc_ids, layout->doc_dtype, B, S,
+                                                 cu_seqlens, cu_seqlens_padded, num_seqs,
+                                                 max_seqlen, padding_mask, status,
+                                                 pad_between_seqs, workspace, copies,
+                                                 n_copies, st));
     }
     if (layout->kind != PSQ_LAYOUT_SEQ_LENS) return PSQ_ERR_ARG;
     if (!valid_dtype(layout->lens_dtype) || layout->P < 0) return PSQ_ERR_ARG;
@@ -127,13 +127,12 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t 
     if (layout->P > 0 && B > (kI32Limit - 2) / layout->P) return PSQ_ERR_OVERFLOW;
     if (workspace == nullptr || workspace_bytes < psq::thd_tables_workspace(B, S))
         return PSQ_ERR_WORKSPACE;
-    hipError_t e = psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
-                                          layout->lens_dtype, B, layout->P, S,
-                                          layout->pad_value, cu_seqlens, cu_seqlens_padded,
-                                          num_seqs, max_seqlen, pad_between_seqs,
-                                          padding_mask, status, workspace, st);
-    if (e != hipSuccess) return PSQ_ERR_HIP;
-    return from_hip(psq::launch_copies(copies, n_copies, st));
+    return from_hip(psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
+                                           layout->lens_dtype, B, layout->P, S,
+                                           layout->pad_value, cu_seqlens, cu_seqlens_padded,
+                                           num_seqs, max_seqlen, pad_between_seqs,
+                                           padding_mask, status, workspace, copies, n_copies,
+                                           st));
 }
 
 size_t psq_pack_rows_workspace(int64_t N, int64_t P, int32_t capacity) {

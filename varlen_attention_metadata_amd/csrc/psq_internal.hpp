@@ -10,20 +10,22 @@
 
 namespace psq {
 
-// k_segments.hip -- document map -> segment boundaries.
+// k_segments.hip -- document map -> segment boundaries (+ fused collapse copies).
 size_t doc_segments_workspace(int64_t B, int64_t S);
 hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_t S,
                                int32_t *cu, int32_t *cu2, int32_t *num_segments,
                                int32_t *max_seqlen, uint8_t *mask, int32_t *status,
-                               int32_t *pad_between, void *workspace, hipStream_t stream);
+                               int32_t *pad_between, void *workspace, const psq_copy *copies,
+                               int n_copies, hipStream_t stream);
 
-// k_thd.hip -- length tables -> THD metadata and layout mask.
+// k_thd.hip -- length tables -> THD metadata and layout mask (+ fused copies).
 size_t thd_tables_workspace(int64_t B, int64_t S);
 hipError_t launch_thd_tables(const void *L, const void *Lp, int lens_dtype, int64_t B,
                              int64_t P, int64_t S, int64_t pad_value, int32_t *cu,
                              int32_t *cp, int32_t *num_seqs, int32_t *max_seqlen,
                              int32_t *pad_between, uint8_t *mask, int32_t *status,
-                             void *workspace, hipStream_t stream);
+                             void *workspace, const psq_copy *copies, int n_copies,
+                             hipStream_t stream);
 
 // k_copy.hip -- batched byte copies (the BSHD -> THD collapse).
 hipError_t launch_copies(const psq_copy *copies, int n_copies, hipStream_t stream);
