@@ -33,6 +33,7 @@ struct WsHeader {
     int32_t n;           // kernel-specific scalars published by one tile
     int32_t cu_last;
     int32_t total;
+    uint64_t fin;        // finished count (high half) | status bits (low half)
 };
 constexpr size_t kWsDescOffset = 256;
 
@@ -83,6 +84,27 @@ __device__ __forceinline__ bool finish_is_last(WsHeader *ws, uint32_t n_groups,
     }
     __syncthreads();
     return *lds_slot != 0u;
+}
+
+// Count this workgroup as finished and fold `bits` into the shared status in
+// one 64-bit word (count in the high half, status bits in the low half).
+// Both updates hit the same location, so relaxed atomics keep them ordered:
+// the workgroup whose count reaches n_groups holds every other workgroup's
+// bits, with no cache write-back (a release would flush L2 once per
+// workgroup, which costs more than the work itself).  Returns the final
+// status in *final_bits and true in that last workgroup, which also clears
+// the word.  Called by one thread.
+__device__ __forceinline__ bool finish_status(WsHeader *ws, uint32_t bits, uint32_t n_groups,
+                                              uint32_t *final_bits) {
+    if (bits)
+        __hip_atomic_fetch_or(&ws->fin, (uint64_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t old = __hip_atomic_fetch_add(&ws->fin, 1ull << 32, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(old >> 32) != n_groups - 1u)
+        return false;
+    *final_bits = (uint32_t)old;
+    st_relaxed(&ws->fin, 0ull);
+    return true;
 }
 
 // ---------------------------------------------------------------------------
