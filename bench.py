@@ -34,15 +34,60 @@ METRIC = "packed tokens/sec (G tok/s) + achieved HBM GB/s vs MI355X peak, per co
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stage_embedding.json")
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources: stored HBM counter figures are only used while
-    the kernels they were taken on are unchanged."""
+# the sources the stage-embedding kernel (k_doc_segments_copy) is built from
+STAGE_KERNEL_SOURCES = ("k_segments.hip", "psq_copy.hpp", "psq_device.hpp")
+
+
+def source_hash(names=STAGE_KERNEL_SOURCES) -> str:
+    """Hash of the kernel's sources: stored HBM counter figures are only used
+    while the kernel they were taken on is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "varlen_attention_metadata_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> None:
+    """Turn two rocprofv3 --pmc runs of ``--profile-launches`` (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch) into per-kernel HBM bytes, scaled by
+    what the same counters read for the 1 GiB calibration copy."""
+    import csv
+    import statistics
+
+    calib_grid = str((1 + (1 << 30) // 4096) * 256)      # 1 GiB copy + one metadata tile
+
+    def load(path):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            if "psq::" not in name:
+                continue
+            short = name.split("(")[0].replace("void ", "")
+            key = "calibration_copy_1GiB" if r["Grid_Size"] == calib_grid else short
+            per.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in per.items()}
+
+    fetch, write = load(fetch_csv), load(write_csv)
+    f_scale = (1 << 30) / 1024 / fetch["calibration_copy_1GiB"]
+    w_scale = (1 << 30) / 1024 / write["calibration_copy_1GiB"]
+    rows = {}
+    for k in fetch:
+        if k in write:
+            rb, wb = fetch[k] * f_scale * 1024, write[k] * w_scale * 1024
+            rows[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
+                       "read_bytes": round(rb), "write_bytes": round(wb),
+                       "bytes_per_launch": round(rb + wb)}
+    stage = next(v for k, v in rows.items() if k.startswith("psq::k_doc_segments_copy"))
+    out = {"source_hash": source_hash(), "kernel": "psq::k_doc_segments_copy<int>",
+           "workload": "stage_embedding", "bytes_per_launch": stage["bytes_per_launch"],
+           "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "kernels": rows}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def parse():
@@ -53,6 +98,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--per-config-iters", type=int, default=50)
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
+                    help="write a markdown summary of a rocprofv3 kernel_stats.csv")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_stage_embedding.json from two rocprofv3 "
+                         "--pmc runs (FETCH_SIZE, WRITE_SIZE) of --profile-launches")
+    ap.add_argument("--profile-launches", type=int, default=0,
+                    help="for counter runs under rocprofv3: launch every workload and a "
+                         "plain 1 GiB calibration copy this many times, print no JSON")
     return ap.parse_args()
 
 
@@ -217,6 +270,46 @@ def measure(torch, call, iters, flush=None):
     return timer.mean_ms()
 
 
+def setup_calibration_copy(torch, psq, lib, dev, nbytes=1 << 30):
+    """A plain device copy of known size (the collapse path with a one-token
+    map): its HBM counters calibrate the counters of the other kernels."""
+    src = torch.empty(nbytes // 8, dtype=torch.int64, device=dev).random_()
+    dst = torch.empty_like(src)
+    doc = torch.ones((1, 1), dtype=torch.int32, device=dev)
+    cu = torch.empty(2, dtype=torch.int32, device=dev)
+    scal = torch.zeros(4, dtype=torch.int32, device=dev)
+    layout = lib.make_layout(lib.LAYOUT_DOC_IDS, doc_ids=doc.data_ptr(), doc_dtype=lib.I32)
+    copies, n_c = lib.make_copies([(src.data_ptr(), dst.data_ptr(), 1, nbytes, nbytes)])
+    ws = psq.workspace_for(dev, lib.psq_process_thd_workspace(layout, 1, 1))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    sp = scal.data_ptr()
+
+    def call():
+        lib.psq_process_thd(layout, 1, 1, cu.data_ptr(), None, sp, sp + 4, sp + 8, None, copies,
+                            n_c, sp + 12, ws.data_ptr(), ws.numel(), stream)
+
+    return call, (src, dst, doc, cu, scal, ws)
+
+
+def profile_launches(torch, psq, lib, synth, dev, n):
+    """Launch each workload n times (plus the calibration copy) for a
+    counter run; prints what ran, in launch order."""
+    runs = [("calibration_copy_1GiB", lambda: setup_calibration_copy(torch, psq, lib, dev))]
+    for name, setup in (("stage_embedding", lambda: setup_stage_embedding(torch, psq, lib, synth, dev)),
+                        ("pack_sources", lambda: setup_pack(torch, psq, lib, synth, dev)),
+                        ("thd_tables", lambda: setup_thd(torch, psq, lib, synth, dev)),
+                        ("doc_map_medium", lambda: setup_doc_map(torch, psq, lib, synth, dev, 2))):
+        runs.append((name, (lambda st: (lambda: st()[::4]))(setup)))
+    for name, setup in runs:
+        call, keep = setup()
+        torch.cuda.synchronize()
+        for _ in range(n):
+            call()
+        torch.cuda.synchronize()
+        print(f"[profile] {name}: {n} launches", file=sys.stderr, flush=True)
+        del keep
+
+
 def roofline(algo_bytes, mean_ms, traffic=None):
     gbs = algo_bytes / (mean_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -251,8 +344,43 @@ def cpu_baseline(torch, keep):
             "seconds": round(t, 3), "host_cpus": os.cpu_count()}
 
 
+WORKLOAD_OF = {
+    "k_doc_segments_copy": "stage_embedding: doc map [32,32768] + bf16 [32,32768,4096] collapse "
+                           "(and the 1 GiB calibration copy when present)",
+    "k_pack_rows": "pack_sources: 65536 sources -> 16384-slot packs",
+    "k_thd_tables_copy": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses",
+    "k_doc_segments": "doc_map_small [4,64] and doc_map_medium [8,4096]",
+    "k_zero_fill": "workspace zero fill (once per workspace)",
+}
+
+
+def summarize_trace(stats_csv: str, out_md: str, command: str) -> None:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    import csv
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "psq::" in r["Name"]]
+    lines = ["# Kernel trace: " + os.path.basename(out_md)[:-3], "",
+             "Command (GPU box, repository root):", "", "```", command, "```", "",
+             "| kernel | workload | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+        short = name.split("(")[0]
+        base = short.split("<")[0].replace("psq::", "")
+        lines.append(f"| `{short}` | {WORKLOAD_OF.get(base, '')} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -270,6 +398,9 @@ def main():
     lib.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_launches > 0:
+        profile_launches(torch, psq, lib, synth, dev, args.profile_launches)
+        return
 
     call, tokens, algo, info, keep = setup_stage_embedding(torch, psq, lib, synth, dev)
     print(f"[bench] stage_embedding ready: {algo / 1e9:.2f} GB per step", file=sys.stderr, flush=True)

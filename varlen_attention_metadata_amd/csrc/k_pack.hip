@@ -31,7 +31,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMembers = kThreads;       // members per LDS batch
 constexpr uint32_t kSlots = 4096;        // slots per workgroup
-constexpr int kPairs = 2;                // slot pairs per thread per step
+constexpr int kPairs = 8;                // slot pairs per thread: one round per chunk
+constexpr int kOwnWords = kSlots / kThreads / 2;   // owner-map words per thread
+static_assert(kSlots % (kThreads * 8) == 0, "chunk must cover whole 16-byte LDS stores");
 
 __device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat) {
     const uint32_t s = a + b;
@@ -174,14 +176,14 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
                 s_own[my_start - lo] = (uint16_t)(threadIdx.x + 1);
             __syncthreads();
             {
-                uint32_t v[8];
-                const u32x4 x0 = *(const u32x4 *)(s_own + threadIdx.x * 16u);
-                const u32x4 x1 = *(const u32x4 *)(s_own + threadIdx.x * 16u + 8u);
-                v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-                v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+                // thread t owns kOwnWords consecutive words (2 entries each)
+                uint32_t v[kOwnWords];
+                const uint32_t *own_w = (const uint32_t *)s_own + threadIdx.x * kOwnWords;
+#pragma unroll
+                for (int e = 0; e < kOwnWords; ++e) v[e] = own_w[e];
                 uint32_t run = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {        // two 16-bit entries per word
+                for (int e = 0; e < kOwnWords; ++e) {
                     const uint32_t a0 = max(run, v[e] & 0xffffu);
                     const uint32_t a1 = max(a0, v[e] >> 16);
                     run = a1;
@@ -195,11 +197,10 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
                 for (int q2 = 0; q2 < kWaves; ++q2)
                     if (q2 < w) pre = max(pre, s_wsum[0][q2]);
                 pre = max(pre, (uint32_t)wave_shr1((int)incl, 0));
+                uint32_t *own_o = (uint32_t *)s_own + threadIdx.x * kOwnWords;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    v[e] = max(v[e] & 0xffffu, pre) | (max(v[e] >> 16, pre) << 16);
-                *(u32x4 *)(s_own + threadIdx.x * 16u) = u32x4{v[0], v[1], v[2], v[3]};
-                *(u32x4 *)(s_own + threadIdx.x * 16u + 8u) = u32x4{v[4], v[5], v[6], v[7]};
+                for (int e = 0; e < kOwnWords; ++e)
+                    own_o[e] = max(v[e] & 0xffffu, pre) | (max(v[e] >> 16, pre) << 16);
             }
             __syncthreads();
 
@@ -211,21 +212,27 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
                 for (int t = 0; t < kPairs; ++t) {
                     const uint32_t u = u0 + 2u * kThreads * (uint32_t)t;
                     const uint32_t own = (u < hi) ? *(const uint32_t *)(s_own + (u - lo)) : 0u;
-                    uint32_t mk = 0;
+                    bool tok[2];
+                    int64_t idx[2];
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const uint32_t s = u + (uint32_t)e;
-                        in[t][e] = s >= r_lo && s < r_hi;
-                        val[t][e] = pad_token;
                         const uint32_t o1 = (own >> (16 * e)) & 0xffffu;
+                        in[t][e] = s >= r_lo && s < r_hi;
+                        tok[e] = false;
+                        idx[e] = 0;
+                        val[t][e] = pad_token;
                         if (in[t][e] && o1 != 0u) {     // o1 >= 1 for every slot in range
                             const uint32_t x = o1 - 1u;
                             const uint32_t off = s - m_start[x];
-                            const bool tok = off < m_real[x];
-                            if (tok) val[t][e] = src[m_so[x] + off];
-                            mk |= (tok ? 1u : 0u) << (8 * e);
+                            tok[e] = off < m_real[x];
+                            idx[e] = m_so[x] + off;
                         }
                     }
+                    // two 8-byte loads (a paired 16-byte load measured slower)
+                    if (tok[0]) val[t][0] = src[idx[0]];
+                    if (tok[1]) val[t][1] = src[idx[1]];
+                    const uint32_t mk = (tok[0] ? 1u : 0u) | (tok[1] ? 0x100u : 0u);
                     if (in[t][0] && in[t][1])
                         *(uint16_t *)(s_mask + (u - lo)) = (uint16_t)mk;
                     else if (in[t][0])
