@@ -470,6 +470,22 @@ def test_pack_no_packs(dev):
     check_pack(dev, np.arange(3), [0], [3], 1, [0], 8, True, what="P=0")
 
 
+def test_pack_workspace_header_left_zeroed(dev):
+    # the squeeze's counters (finish word, fallback list) are cleared by the
+    # call itself; descriptors are rewritten by every call
+    rng = np.random.default_rng(5)
+    rl = rng.integers(0, 4, size=600).astype(np.int32)          # q = 1: many runs,
+    off = np.zeros(600, dtype=np.int64)                          # fallback chunks
+    off[1:] = np.cumsum(rl[:-1])
+    src = rng.integers(0, 1000, size=int(rl.sum()))
+    C = int(rl.sum()) + 5
+    for _ in range(2):
+        check_pack(dev, src, off, rl, 1, [0, 300, 600], C, True, what="fallback twice")
+    torch.cuda.synchronize()
+    ws = psq.workspace_for(dev, 0)
+    assert int(ws[:256].count_nonzero()) == 0
+
+
 def test_pack_python_api(dev):
     src = torch.arange(100, 115, dtype=torch.int64, device=dev)
     out = psq.pack_rows(src, torch.tensor([0, 5], device=dev),
