@@ -15,8 +15,10 @@ Pages followed:
   * NeMo AutoModel 0.5 API reference, ``nemo_automodel.components.distributed.thd_utils``
     (``process_input_for_thd``, ``_thd_padding_mask``) -> :func:`thd_tables`,
     :func:`copy_rows`.
+    ``split_batch_into_thd_chunks`` -> :func:`split_thd`;
+    ``thd_padding_mask_from_token_ids`` -> :func:`pad_mask_from_ids`.
   * "Who packs the sequences: the loader, or the trainer?" (Trainer packs /
-    Loader packs) -> :func:`pack`.
+    Loader packs) -> :func:`pack`, :func:`pack_rect`, :func:`trainer_width`.
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ EMPTY_ROW = 8
 PACK_OVERFLOW = 16
 EMPTY_PACK = 32
 BAD_INDEX = 64
+PAD_IS_CONTENT = 256
 
 _lib = None
 
@@ -67,6 +70,11 @@ def _load():
     lib.orc_pack.restype = ctypes.c_uint32
     lib.orc_pack.argtypes = [vp, i64, vp, vp, i64, i32, vp, vp, i64, i32,
                              ctypes.c_int, i64, vp, vp, vp, vp]
+    lib.orc_pack_rect.restype = ctypes.c_uint32
+    lib.orc_pack_rect.argtypes = [vp, i64, vp, i64, i32, vp, vp, i64, i32,
+                                  ctypes.c_int, i64, vp, vp, vp, vp]
+    lib.orc_pad_mask_from_ids.restype = ctypes.c_uint32
+    lib.orc_pad_mask_from_ids.argtypes = [vp, i64, i64, vp, vp]
     _lib = lib
     return lib
 
@@ -181,3 +189,109 @@ def pack_csr_slices(cu_csr, pack_start):
         a, b = int(ps[p]), int(ps[p + 1])
         out.append(np.asarray(cu_csr)[a + p: b + p + 1])
     return out
+
+
+def split_thd(seq_lens, seq_lens_padded, S: int, num_chunks: int,
+              pad_value: int = -1000) -> dict:
+    """``split_batch_into_thd_chunks`` on ``[B, P]`` length tables.
+
+    The batch is cut along rows into ``num_chunks`` equal groups, each group
+    goes through :func:`thd_tables` on its own, and the results are stacked:
+    ``cu_seqlens`` / ``cu_seqlens_padded`` become ``[num_chunks, L]`` with
+    every row filled up to ``L`` (the longest) with ``pad_value``;
+    ``max_seqlen``, ``num_seqs`` and ``pad_between_seqs`` become
+    ``[num_chunks]``; ``padding_mask`` becomes ``[num_chunks, B/num_chunks*S]``.
+    Returns ``status`` (OR over chunks) and, on success, those arrays.
+    """
+    L = np.asarray(seq_lens)
+    Lp = None if seq_lens_padded is None else np.asarray(seq_lens_padded)
+    B = L.shape[0]
+    if num_chunks < 1 or B % num_chunks != 0:
+        raise ValueError("num_chunks must evenly divide the batch size")
+    rows = B // num_chunks
+    parts = []
+    status = 0
+    for c in range(num_chunks):
+        part = thd_tables(L[c * rows:(c + 1) * rows],
+                          None if Lp is None else Lp[c * rows:(c + 1) * rows],
+                          S, pad_value)
+        status |= part["status"]
+        parts.append(part)
+    if status != 0:
+        return {"status": status}
+    width = max(p["cu_seqlens"].size for p in parts)
+
+    def stacked(key):
+        out = np.full((num_chunks, width), pad_value, dtype=np.int32)
+        for c, p in enumerate(parts):
+            out[c, :p[key].size] = p[key]
+        return out
+
+    return {"status": 0,
+            "cu_seqlens": stacked("cu_seqlens"),
+            "cu_seqlens_padded": stacked("cu_seqlens_padded"),
+            "num_seqs": np.array([p["num_seqs"] for p in parts], dtype=np.int32),
+            "max_seqlen": np.array([p["max_seqlen"] for p in parts], dtype=np.int32),
+            "pad_between_seqs": np.array([p["pad_between_seqs"] for p in parts],
+                                         dtype=np.int32),
+            "padding_mask": np.stack([p["padding_mask"] for p in parts])}
+
+
+def pad_mask_from_ids(input_ids, pad_id: int) -> dict:
+    """``thd_padding_mask_from_token_ids`` on a flat ``[T]`` id stream.
+
+    Returns ``status`` (``PAD_IS_CONTENT`` when the pad id occurs before the
+    pad tail), ``padding_mask`` (uint8 0/1) and ``num_content`` (index of the
+    first pad slot, ``T`` when there is none).
+    """
+    ids = np.ascontiguousarray(np.asarray(input_ids), dtype=np.int64).reshape(-1)
+    mask = np.empty(ids.size, dtype=np.uint8)
+    nc = np.zeros(1, dtype=np.int64)
+    st = _load().orc_pad_mask_from_ids(_ptr(ids), ids.size, pad_id, _ptr(mask), _ptr(nc))
+    return {"status": int(st), "padding_mask": mask, "num_content": int(nc[0])}
+
+
+def bins_to_csr(bins):
+    """Bin membership lists -> (pack_order int32 [sum], pack_start int64 [P+1])."""
+    order = np.array([i for b in bins for i in b], dtype=np.int32)
+    start = np.zeros(len(bins) + 1, dtype=np.int64)
+    start[1:] = np.cumsum([len(b) for b in bins])
+    return order, start
+
+
+def trainer_width(real_len, bins, q: int) -> int:
+    """Trainer packs: the row is as wide as the widest bin's padded sources."""
+    rl = np.asarray(real_len, dtype=np.int64)
+    widths = [sum(-(-int(rl[i]) // q) * q for i in b) for b in bins]
+    return max(widths) if widths else 0
+
+
+def pack_rect(rows, real_len, q: int, bins, width: int | None = None,
+              fold: bool = False, pad_token: int = 0) -> dict:
+    """Trainer packs: squeeze the padded rectangle ``rows [N, W]`` into bins.
+
+    ``bins`` lists the member row indices of each bin (chosen on the host).
+    ``width`` defaults to :func:`trainer_width`.  Returns the same keys as
+    :func:`pack` plus ``width``.
+    """
+    r = np.ascontiguousarray(np.asarray(rows), dtype=np.int64)
+    assert r.ndim == 2
+    N, W = r.shape
+    rl = np.ascontiguousarray(np.asarray(real_len), dtype=np.int32)
+    assert rl.size == N
+    order, start = bins_to_csr(bins)
+    C = trainer_width(rl, bins, q) if width is None else int(width)
+    P = len(bins)
+    csr = order.size + P
+    packed = np.empty((P, C), dtype=np.int64)
+    tm = np.empty((P, C), dtype=np.uint8)
+    cu = np.zeros(max(csr, 1), dtype=np.int32)
+    cp = np.zeros(max(csr, 1), dtype=np.int32)
+    st = _load().orc_pack_rect(_ptr(r), W, _ptr(rl), N, q, _ptr(order), _ptr(start), P,
+                               C, int(bool(fold)), pad_token, _ptr(packed), _ptr(tm),
+                               _ptr(cu), _ptr(cp))
+    if st != 0:
+        return {"status": int(st)}
+    return {"status": 0, "packed": packed, "token_mask": tm, "width": C,
+            "cu_seqlens": cu[:csr], "cu_seqlens_padded": cp[:csr],
+            "pack_order": order, "pack_start": start}

@@ -18,6 +18,8 @@
  *   [P2] NeMo AutoModel 0.5 API reference, "nemo_automodel.components.
  *        distributed.thd_utils" (_thd_padding_mask; process_input_for_thd,
  *        its Example and Returns).
+ *        Also thd_padding_mask_from_token_ids and split_batch_into_thd_chunks
+ *        (the latter is assembled from orc_thd_tables in oracle/__init__.py).
  *   [P3] "Who packs the sequences: the loader, or the trainer?" (sections
  *        "What the data looks like at each hop": Trainer packs / Loader packs).
  *
@@ -35,6 +37,7 @@
 #define ORC_PACK_OVERFLOW  16u   /* padded sources exceed the pack capacity    */
 #define ORC_EMPTY_PACK     32u   /* a pack has no member                       */
 #define ORC_BAD_INDEX      64u   /* member / pack / source range out of bounds */
+#define ORC_PAD_IS_CONTENT 256u   /* the pad id also occurs before the pad tail */
 
 /* ------------------------------------------------------------------------ */
 /* [P1] packed_seq_params_from_doc_ids.                                      */
@@ -330,4 +333,74 @@ uint32_t orc_pack(const int64_t *src, int64_t src_len, const int64_t *src_off,
             pcp[k] = C;
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P3] Trainer packs: the squeeze straight from the padded rectangle the    */
+/* worker receives (input_ids [N, W] with input_lengths), bins chosen on the  */
+/* host.  Row i holds source i in its first real_len[i] slots, so the source */
+/* offsets are i*W, and a length beyond the row is an error.  Everything     */
+/* else is orc_pack (the trainer path runs it without the fold).             */
+/* ------------------------------------------------------------------------ */
+uint32_t orc_pack_rect(const int64_t *rows, int64_t W, const int32_t *real_len,
+                       int64_t N, int32_t q, const int32_t *order,
+                       const int64_t *pack_start, int64_t P, int32_t C, int fold,
+                       int64_t pad_token, int64_t *packed, uint8_t *token_mask,
+                       int32_t *cu, int32_t *cp)
+{
+    uint32_t status = 0;
+    int64_t i;
+    int64_t *off;
+
+    for (i = 0; i < N; i++) {
+        if (real_len[i] > W)
+            status |= ORC_BAD_LENGTH;
+    }
+    if (status != 0)
+        return status;
+    off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+    for (i = 0; i < N; i++)
+        off[i] = i * W;
+    status = orc_pack(rows, N * W, off, real_len, N, q, order, pack_start, P, C,
+                      fold, pad_token, packed, token_mask, cu, cp);
+    free(off);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P2] thd_padding_mask_from_token_ids: the metadata-free mask.             */
+/*                                                                          */
+/* A slot is padding when its id equals the pad id.  That comparison is only */
+/* right when the pad id fills a right-padded tail and occurs nowhere else,  */
+/* so the stream is checked for exactly that: from the first pad slot on,    */
+/* every slot must be pad.  Otherwise the pad id is also content (the        */
+/* page's pad == end-of-text case) and the call fails.                       */
+/*                                                                          */
+/* ids: T token ids.  mask: T bytes.  *num_content: index of the first pad   */
+/* slot (T when there is none), i.e. the length of the content prefix.       */
+/* ------------------------------------------------------------------------ */
+uint32_t orc_pad_mask_from_ids(const int64_t *ids, int64_t T, int64_t pad,
+                               uint8_t *mask, int64_t *num_content)
+{
+    uint32_t status = 0;
+    int64_t t, first_pad = T;
+
+    /* Step 1: the value comparison. */
+    for (t = 0; t < T; t++)
+        mask[t] = (uint8_t)(ids[t] == pad);
+
+    /* Step 2: find where the tail would begin ... */
+    for (t = 0; t < T; t++) {
+        if (mask[t]) {
+            first_pad = t;
+            break;
+        }
+    }
+    /* ... and reject a non-pad id after it. */
+    for (t = first_pad; t < T; t++) {
+        if (!mask[t])
+            status |= ORC_PAD_IS_CONTENT;
+    }
+    *num_content = first_pad;
+    return status;
 }

@@ -6,6 +6,10 @@ by the printed examples ([0,5,15] / [0,8,20] at width 20, [0,8,36] at
 capacity 36, 16 tail pad, 15 real of 36), a numpy reduction (pad multiple 1,
 no fold, one pack holding everything is a concatenation), brute force against
 an independent list-building formulation, and invariants on the workload.
+The trainer-path squeeze straight from the padded rectangle is pinned by the
+same printed trainer example (width 20 is the widest bin's padded sum), the
+concatenation reduction, and brute force over small rectangles and bin
+splits against the list formulation.
 """
 import itertools
 
@@ -164,3 +168,70 @@ def test_workload_invariants():
             a = int(cp_l[p][j])
             got = out["packed"][p][a:a + int(rl[i])]
             assert np.array_equal(got, w["src"][w["src_off"][i]:w["src_off"][i] + rl[i]])
+
+
+def test_trainer_rectangle_printed_example():
+    # input_ids [2, 10] holding A (5 tokens) and B (10), bins [[0, 1]], q = 4:
+    # packed [1, 20] = A, its pad, B, its pad; [0,5,15] and [0,8,20].
+    g = load_golden("trainer_pack_example.json")
+    inp = g["input"]
+    rows = np.zeros((2, 10), dtype=np.int64)
+    rows[0, :5] = np.arange(101, 106)
+    rows[1, :10] = np.arange(201, 211)
+    out = oracle.pack_rect(rows, inp["real_len"], inp["pad_to"], inp["bins"])
+    assert out["status"] == 0
+    pr = g["printed"]
+    assert out["width"] == inp["capacity"]
+    assert list(out["packed"].shape) == pr["packed_shape"]
+    assert out["cu_seqlens"].tolist() == pr["cu_seqlens"]
+    assert out["cu_seqlens_padded"].tolist() == pr["cu_seqlens_padded"]
+    assert out["packed"][0].tolist() == list(range(101, 106)) + [0] * 3 + \
+        list(range(201, 211)) + [0] * 2
+    # the rectangle had 5 of its 20 slots as padding; the squeeze keeps 15 real
+    assert int(out["token_mask"].sum()) == 15
+
+
+def test_trainer_rectangle_concatenation():
+    rng = np.random.default_rng(11)
+    N, W = 9, 7
+    rows = rng.integers(0, 1000, size=(N, W))
+    lens = rng.integers(0, W + 1, size=N).astype(np.int32)
+    out = oracle.pack_rect(rows, lens, 1, [list(range(N))])
+    assert out["status"] == 0
+    want = np.concatenate([rows[i, :lens[i]] for i in range(N)])
+    assert out["width"] == want.size
+    assert out["packed"][0].tolist() == want.tolist()
+    assert out["cu_seqlens"].tolist() == out["cu_seqlens_padded"].tolist() == \
+        np.concatenate([[0], np.cumsum(lens)]).tolist()
+
+
+def test_trainer_rectangle_brute_force():
+    checked = 0
+    W = 4
+    for lens in itertools.product(range(0, W + 1), repeat=3):
+        rows = np.array([[10 * (i + 1) + j for j in range(W)] for i in range(3)])
+        sources = [rows[i, :lens[i]].tolist() for i in range(3)]
+        for q in (1, 3, 4):
+            for bins in ([[0, 1, 2]], [[2, 0], [1]], [[1], [2], [0]], [[0, 2, 1]]):
+                for fold in (False, True):
+                    out = oracle.pack_rect(rows, list(lens), q, bins, fold=fold, pad_token=-5)
+                    if out["width"] == 0:
+                        continue
+                    assert out["status"] == 0
+                    C = out["width"]
+                    starts = out["pack_start"]
+                    cu_l = oracle.pack_csr_slices(out["cu_seqlens"], starts)
+                    cp_l = oracle.pack_csr_slices(out["cu_seqlens_padded"], starts)
+                    for p, members in enumerate(bins):
+                        row, tm, cu, cp = list_formulation(sources, members, q, C, fold, -5)
+                        assert out["packed"][p].tolist() == row
+                        assert out["token_mask"][p].tolist() == tm
+                        assert cu_l[p].tolist() == cu and cp_l[p].tolist() == cp
+                    checked += 1
+    assert checked > 800
+
+
+def test_trainer_rectangle_length_beyond_row_is_rejected():
+    rows = np.zeros((2, 4), dtype=np.int64)
+    assert oracle.pack_rect(rows, [4, 5], 1, [[0, 1]], width=9)["status"] == oracle.BAD_LENGTH
+    assert oracle.pack_rect(rows, [4, -1], 1, [[0, 1]], width=9)["status"] == oracle.BAD_LENGTH

@@ -94,6 +94,70 @@ def test_chunks_example_printed_values():
         assert out["padding_mask"].sum() == 0
 
 
+def test_split_chunks_example_printed_values():
+    # split_batch_into_thd_chunks Example: input_ids [2, 12], cu_seqlens [2, 3],
+    # each chunk [0, 6, 12].
+    g = load_golden("thd_chunks_example.json")
+    inp = g["input"]
+    out = oracle.split_thd(inp["seq_lens"], inp["seq_lens_padded"], inp["S"],
+                           inp["num_chunks"])
+    assert out["status"] == 0
+    pr = g["printed"]
+    assert list(out["cu_seqlens"].shape) == pr["cu_seqlens_shape"]
+    assert out["cu_seqlens"].tolist() == pr["cu_seqlens_per_chunk"]
+    assert list(out["padding_mask"].shape) == pr["input_ids_shape"]
+    assert out["cu_seqlens_padded"].tolist() == g["derived"]["cu_seqlens_padded_per_chunk"]
+    assert out["max_seqlen"].tolist() == [g["derived"]["max_seqlen"]] * 2
+    assert out["pad_between_seqs"].tolist() == [g["derived"]["pad_between_seqs"]] * 2
+
+
+def test_split_ragged_chunks_are_filled_with_the_sentinel():
+    # Hand case: chunk 0 holds 3 sequences, chunk 1 one, so chunk 1's arrays
+    # are filled with the sentinel up to chunk 0's length 4.  Chunk 0 is
+    # tight up to its last sequence (absorbs: [0,2,5,8]); chunk 1's single
+    # sequence absorbs too ([0,1] -> [0,4]).
+    out = oracle.split_thd([[2, 3, 1], [1, V, V]], [[2, 3, 1], [1, V, V]], S=8,
+                           num_chunks=2)
+    assert out["status"] == 0
+    assert out["cu_seqlens_padded"].tolist() == [[0, 2, 5, 8], [0, 8, V, V]]
+    assert out["cu_seqlens"].tolist() == [[0, 2, 5, 8], [0, 8, V, V]]
+    assert out["num_seqs"].tolist() == [3, 1]
+    assert out["max_seqlen"].tolist() == [3, 8]
+    assert out["pad_between_seqs"].tolist() == [0, 0]
+    assert np.flatnonzero(out["padding_mask"][0]).tolist() == [6, 7]
+    assert np.flatnonzero(out["padding_mask"][1]).tolist() == list(range(1, 8))
+
+
+def test_split_is_per_row_local():
+    # Rows are independent once each row's tail pad is folded into it, so
+    # the chunks' physical boundaries are the whole batch's, rebased, and
+    # the stacked mask is the whole batch's mask.  Absorption is per chunk:
+    # the real boundaries agree with the whole batch's except at a chunk end.
+    w = synth.thd_tables(B=16)
+    L, Lp, S = w["seq_lens"], w["seq_lens_padded"], w["S"]
+    whole = oracle.thd_tables(L, Lp, S)
+    for chunks in (1, 2, 4, 16):
+        out = oracle.split_thd(L, Lp, S, chunks)
+        assert out["status"] == 0
+        rows = L.shape[0] // chunks
+        assert np.array_equal(out["padding_mask"].reshape(-1), whole["padding_mask"])
+        first = 0
+        for c in range(chunks):
+            k = int(out["num_seqs"][c])
+            cp_whole = whole["cu_seqlens_padded"][first:first + k + 1].astype(np.int64)
+            assert np.array_equal(out["cu_seqlens_padded"][c, :k + 1], cp_whole - c * rows * S)
+            cu_whole = whole["cu_seqlens"][first:first + k].astype(np.int64)
+            assert np.array_equal(out["cu_seqlens"][c, :k], cu_whole - cu_whole[0])
+            assert np.all(out["cu_seqlens"][c, k + 1:] == V)
+            first += k
+        assert first == whole["num_seqs"]
+
+
+def test_split_rejects_uneven_chunks():
+    with pytest.raises(ValueError):
+        oracle.split_thd([[1], [1], [1]], None, S=2, num_chunks=2)
+
+
 def test_row_fold_with_tail_pad_in_every_row():
     out = oracle.thd_tables([[3, 2], [6, V]], [[4, 2], [6, V]], S=8)
     assert out["cu_seqlens"].tolist() == [0, 3, 5, 11]
