@@ -1,8 +1,8 @@
 /*
  * psq.h -- packed-sequence (THD) varlen-attention metadata on MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels.  Three operations, one per page of
- * the method:
+ * A C ABI over hand-written HIP kernels.  The operations follow the pages'
+ * functions one for one:
  *
  *   psq_params_from_doc_ids  document map -> cu_seqlens, max_seqlen
  *       NeMo AutoModel API, nemo_automodel.components.datasets.packed_seq:
@@ -11,10 +11,17 @@
  *       metadata, layout padding mask, and the BSHD -> THD collapse copies
  *       NeMo AutoModel 0.5 API, nemo_automodel.components.distributed.
  *       thd_utils: process_input_for_thd and _thd_padding_mask.
+ *   psq_split_thd            the same for equal row groups, results stacked
+ *       (split_batch_into_thd_chunks, same page).
+ *   psq_padding_mask_from_token_ids   the metadata-free padding mask,
+ *       rejecting a pad id that is also content
+ *       (thd_padding_mask_from_token_ids, same page).
  *   psq_pack_rows            the squeeze of padded sources into fixed-capacity
  *       packs, last padded boundary folded to capacity
  *       "Who packs the sequences: the loader, or the trainer?", What the data
  *       looks like at each hop (Trainer packs, Loader packs).
+ *   psq_pack_padded_rows     the trainer's squeeze straight from the padded
+ *       [N, W] rectangle (same page, Trainer packs).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -69,6 +76,7 @@ extern "C" {
 #define PSQ_DATA_BAD_INDEX      64   /* member, pack or source out of range   */
 #define PSQ_DATA_WORKSPACE     128   /* workspace was not zero-filled (a
                                         bounded wait or a bound check failed) */
+#define PSQ_DATA_PAD_IS_CONTENT 256  /* the pad id occurs before the pad tail */
 
 /* layouts accepted by psq_process_thd */
 #define PSQ_LAYOUT_SEQ_LENS 0
@@ -114,15 +122,17 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
                             void *stream);
 
 /* One byte copy of the BSHD -> THD collapse: `rows` rows of `row_bytes`
- * bytes, read at a stride of src_row_stride_bytes, written densely.  A
- * contiguous tensor is one row (or rows with stride == row_bytes).  src and
- * dst must not overlap. */
+ * bytes, read at a stride of src_row_stride_bytes and written at a stride of
+ * dst_row_stride_bytes (0 = row_bytes, i.e. densely).  A contiguous tensor
+ * is one row (or rows with both strides == row_bytes).  Strides are at least
+ * row_bytes; src and dst must not overlap. */
 typedef struct psq_copy {
     const void *src;
     void *dst;
     int64_t rows;
     int64_t row_bytes;
     int64_t src_row_stride_bytes;
+    int64_t dst_row_stride_bytes;
 } psq_copy;
 
 /* Where the THD layout comes from (host struct). */
@@ -181,6 +191,67 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S,
                     void *stream);
 
 /* ------------------------------------------------------------------------
+ * psq_split_thd
+ *
+ * NeMo AutoModel 0.5 API, thd_utils: split_batch_into_thd_chunks.  The B rows
+ * are cut into num_chunks equal groups of Bc = B / num_chunks consecutive
+ * rows; each group is one psq_process_thd call on a batch of Bc rows (its own
+ * boundaries starting at 0, its own absorption, scalars and mask), and the
+ * results are stacked.  Table layout only (PSQ_LAYOUT_SEQ_LENS).
+ *
+ *   cu_seqlens        int32, capacity num_chunks * (Bc*P+1).  On completion
+ *                     the first num_chunks * L entries hold a row-major
+ *                     [num_chunks, L] array, L = *cu_width = the longest
+ *                     group's n+1; a shorter group's row is filled up to L
+ *                     with layout->pad_value.
+ *   cu_seqlens_padded the same for the physical boundaries, or NULL.
+ *   cu_width          int32 scalar L (0 when *status != 0).
+ *   num_seqs, max_seqlen, pad_between_seqs   int32 [num_chunks].
+ *   padding_mask      uint8 [B*S] (= [num_chunks, Bc*S]), or NULL.
+ *   copies            as in psq_process_thd; a [B,S,...] tensor stacked per
+ *                     group is the same bytes as its flattening, and the
+ *                     destination row stride of a copy allows the mRoPE
+ *                     [n, B, S] -> [num_chunks, n, 1, Bc*S] reordering.
+ *   status            int32 scalar, required (OR over the groups).
+ *   workspace         psq_split_thd_workspace(layout, B, S, num_chunks) bytes.
+ * Host errors: as psq_process_thd, plus PSQ_ERR_ARG when num_chunks < 1,
+ * num_chunks does not divide B, or the layout is not a table layout.
+ * ---------------------------------------------------------------------- */
+size_t psq_split_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S,
+                               int64_t num_chunks);
+int psq_split_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int64_t num_chunks,
+                  int32_t *cu_seqlens, int32_t *cu_seqlens_padded, int32_t *cu_width,
+                  int32_t *num_seqs, int32_t *max_seqlen, int32_t *pad_between_seqs,
+                  uint8_t *padding_mask, const psq_copy *copies, int n_copies,
+                  int32_t *status, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * psq_padding_mask_from_token_ids
+ *
+ * NeMo AutoModel 0.5 API, thd_utils: thd_padding_mask_from_token_ids, for
+ * callers without pack metadata.  padding_mask[t] = (input_ids[t] == pad_id).
+ * That comparison is a correct mask only when the pad slots form a right-
+ * padded tail, so the call checks exactly that and sets
+ * PSQ_DATA_PAD_IS_CONTENT in *status when some pad slot comes before a
+ * non-pad slot (the pad id is also content).
+ *
+ *   input_ids     [T], element type ids_dtype (PSQ_I32 or PSQ_I64).  With
+ *                 int32 ids, a pad_id outside the int32 range matches none.
+ *   padding_mask  uint8 [T], required.
+ *   num_content   int32 scalar: index of the first pad slot (T when there is
+ *                 none), i.e. the content length; or NULL.
+ *   status        int32 scalar, required.
+ *   workspace     psq_padding_mask_from_token_ids_workspace(T) bytes.
+ * Host errors: PSQ_ERR_ARG (null pointer, T < 0, bad dtype),
+ * PSQ_ERR_OVERFLOW (T >= 2^31), PSQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t psq_padding_mask_from_token_ids_workspace(int64_t T);
+int psq_padding_mask_from_token_ids(const void *input_ids, int ids_dtype, int64_t T,
+                                    int64_t pad_id, uint8_t *padding_mask,
+                                    int32_t *num_content, int32_t *status, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * psq_pack_rows
  *
  * "Who packs the sequences: the loader, or the trainer?", Trainer packs and
@@ -205,7 +276,8 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S,
  *   workspace      psq_pack_rows_workspace(N, P, capacity) bytes.
  * Data errors: PACK_OVERFLOW, EMPTY_PACK, BAD_INDEX (pack_start outside
  * [0, N] or decreasing, a member index outside [0, N), a source outside
- * src_tokens), BAD_LENGTH (real_len < 0).
+ * src_tokens), BAD_LENGTH (real_len < 0).  With pack_order, the members
+ * are pack_start[P] entries of it and the CSR holds pack_start[P] + P.
  * Host errors: PSQ_ERR_ARG (null pointer, negative size, pad_to < 1,
  * capacity < 1 or > 2^30), PSQ_ERR_OVERFLOW (N+P >= 2^31),
  * PSQ_ERR_WORKSPACE.
@@ -218,6 +290,33 @@ int psq_pack_rows(const int64_t *src_tokens, int64_t src_len, const int64_t *src
                   int64_t *packed, uint8_t *token_mask,
                   int32_t *cu_seqlens, int32_t *cu_seqlens_padded, int32_t *status,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * psq_pack_padded_rows
+ *
+ * "Who packs the sequences: the loader, or the trainer?", Trainer packs: the
+ * batch reaches the worker as a padded rectangle input_ids [N, W] with
+ * input_lengths, the bins are chosen on the host, and the squeeze lays each
+ * bin's rows end to end.  Exactly psq_pack_rows with source i = row i
+ * (offset i*W); the row width of the output (`capacity`) is the caller's,
+ * the trainer taking the widest bin's padded sum, with fold = 0.
+ *
+ *   rows           int64 [N, W] row-major.       real_len int32 [N].
+ *   pack_order     int32 [N] or NULL.            pack_start int64 [P+1].
+ *   packed, token_mask, cu_seqlens, cu_seqlens_padded, status   as in
+ *                  psq_pack_rows.
+ *   workspace      psq_pack_rows_workspace(N, P, capacity) bytes.
+ * Data errors: as psq_pack_rows; BAD_LENGTH also for a member whose length
+ * exceeds W (such a member counts as empty toward its pack's fill).
+ * Host errors: as psq_pack_rows, plus PSQ_ERR_ARG for W < 0 and
+ * PSQ_ERR_OVERFLOW when N*W >= 2^62.
+ * ---------------------------------------------------------------------- */
+int psq_pack_padded_rows(const int64_t *rows, int64_t W, const int32_t *real_len, int64_t N,
+                         int32_t pad_to, const int32_t *pack_order, const int64_t *pack_start,
+                         int64_t P, int32_t capacity, int fold, int64_t pad_token,
+                         int64_t *packed, uint8_t *token_mask, int32_t *cu_seqlens,
+                         int32_t *cu_seqlens_padded, int32_t *status, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -250,12 +250,14 @@ void orc_copy_rows(const uint8_t *src, uint8_t *dst, int64_t rows,
 /* are stored one after another: pack p's k+1 entries start at               */
 /* pack_start[p] + p.                                                        */
 /* ------------------------------------------------------------------------ */
-uint32_t orc_pack(const int64_t *src, int64_t src_len, const int64_t *src_off,
-                  const int32_t *real_len, int64_t N, int32_t q,
-                  const int32_t *order, const int64_t *pack_start, int64_t P,
-                  int32_t C, int fold, int64_t pad_token,
-                  int64_t *packed, uint8_t *token_mask,
-                  int32_t *cu, int32_t *cp)
+/* row_width >= 0: the sources are the rows of a rectangle that wide, and a */
+/* length beyond it is a BAD_LENGTH (the trainer path, orc_pack_rect).       */
+static uint32_t pack_impl(const int64_t *src, int64_t src_len, const int64_t *src_off,
+                          const int32_t *real_len, int64_t N, int32_t q,
+                          const int32_t *order, const int64_t *pack_start, int64_t P,
+                          int32_t C, int fold, int64_t pad_token,
+                          int64_t *packed, uint8_t *token_mask,
+                          int32_t *cu, int32_t *cp, int64_t row_width)
 {
     uint32_t status = 0;
     int64_t p, j, s;
@@ -279,7 +281,7 @@ uint32_t orc_pack(const int64_t *src, int64_t src_len, const int64_t *src_off,
                 continue;
             }
             real = real_len[i];
-            if (real < 0) {
+            if (real < 0 || (row_width >= 0 && real > row_width)) {
                 status |= ORC_BAD_LENGTH;
                 continue;
             }
@@ -335,12 +337,24 @@ uint32_t orc_pack(const int64_t *src, int64_t src_len, const int64_t *src_off,
     return 0;
 }
 
+uint32_t orc_pack(const int64_t *src, int64_t src_len, const int64_t *src_off,
+                  const int32_t *real_len, int64_t N, int32_t q,
+                  const int32_t *order, const int64_t *pack_start, int64_t P,
+                  int32_t C, int fold, int64_t pad_token,
+                  int64_t *packed, uint8_t *token_mask,
+                  int32_t *cu, int32_t *cp)
+{
+    return pack_impl(src, src_len, src_off, real_len, N, q, order, pack_start, P, C,
+                     fold, pad_token, packed, token_mask, cu, cp, -1);
+}
+
 /* ------------------------------------------------------------------------ */
 /* [P3] Trainer packs: the squeeze straight from the padded rectangle the    */
 /* worker receives (input_ids [N, W] with input_lengths), bins chosen on the  */
 /* host.  Row i holds source i in its first real_len[i] slots, so the source */
-/* offsets are i*W, and a length beyond the row is an error.  Everything     */
-/* else is orc_pack (the trainer path runs it without the fold).             */
+/* offsets are i*W, and a member whose length is negative or beyond the row  */
+/* is a BAD_LENGTH.  Everything else is orc_pack (the trainer path runs it   */
+/* without the fold).                                                        */
 /* ------------------------------------------------------------------------ */
 uint32_t orc_pack_rect(const int64_t *rows, int64_t W, const int32_t *real_len,
                        int64_t N, int32_t q, const int32_t *order,
@@ -348,21 +362,15 @@ uint32_t orc_pack_rect(const int64_t *rows, int64_t W, const int32_t *real_len,
                        int64_t pad_token, int64_t *packed, uint8_t *token_mask,
                        int32_t *cu, int32_t *cp)
 {
-    uint32_t status = 0;
+    uint32_t status;
     int64_t i;
     int64_t *off;
 
-    for (i = 0; i < N; i++) {
-        if (real_len[i] > W)
-            status |= ORC_BAD_LENGTH;
-    }
-    if (status != 0)
-        return status;
     off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
     for (i = 0; i < N; i++)
         off[i] = i * W;
-    status = orc_pack(rows, N * W, off, real_len, N, q, order, pack_start, P, C,
-                      fold, pad_token, packed, token_mask, cu, cp);
+    status = pack_impl(rows, N * W, off, real_len, N, q, order, pack_start, P, C,
+                       fold, pad_token, packed, token_mask, cu, cp, W);
     free(off);
     return status;
 }

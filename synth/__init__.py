@@ -28,6 +28,16 @@ The five workloads are:
      int64 position_ids counting from 0 inside every run (padding runs too);
      the bf16 [32, 32768, 4096] N(0, 1) hidden tensor is drawn on the device
      by :func:`stage_hidden` with a seeded torch generator.
+
+Inputs of the steps around the workloads:
+
+  * ``pad_tail_stream``   a flat int64 token stream of workload 3's size
+    (131072 ids, uniform over 0..151935) whose last U{0..8192} slots hold a
+    pad id outside the token range: the metadata-free padding mask.
+  * ``trainer_rectangle`` a trainer micro-batch: 256 conversations of
+    workload 4's length law in a padded [N, max_len] rectangle (0 past each
+    length), bins chosen by first-fit decreasing on a 16384-token budget
+    (:func:`token_budget_bins`), pad multiple 64.
 """
 from __future__ import annotations
 
@@ -155,6 +165,52 @@ def pack_sources(seed: int = 4, N: int = 65536, capacity: int = 16384, q: int = 
     pack_start = next_fit(_round_up(real, q), capacity)
     return {"src": tokens, "src_off": src_off, "real_len": real.astype(np.int32),
             "pack_start": pack_start, "q": q, "capacity": capacity}
+
+
+def token_budget_bins(padded_len, budget: int) -> list:
+    """First-fit decreasing on the host: longest padded source first, each
+    into the first bin with room for it.  Returns each bin's source indices
+    in the order they were placed."""
+    padded = np.asarray(padded_len, dtype=np.int64)
+    order = sorted(range(padded.size), key=lambda i: (-int(padded[i]), i))
+    bins, room = [], []
+    for i in order:
+        n = int(padded[i])
+        if n > budget:
+            raise ValueError(f"source {i} ({n} slots) exceeds the budget {budget}")
+        for b in range(len(bins)):
+            if room[b] >= n:
+                bins[b].append(i)
+                room[b] -= n
+                break
+        else:
+            bins.append([i])
+            room.append(budget - n)
+    return bins
+
+
+def trainer_rectangle(seed: int = 6, N: int = 256, q: int = 64, budget: int = 16384,
+                      median: float = 400.0, sigma: float = 1.2, max_len: int = 8192) -> dict:
+    """A trainer micro-batch: padded rectangle, lengths, token-budget bins."""
+    rng_len, rng_tok = _streams(seed)
+    real = _lognormal_int(rng_len, median, sigma, 1, max_len, size=N)
+    W = int(real.max()) if N > 0 else 0
+    rows = np.zeros((N, W), dtype=np.int64)
+    for i in range(N):
+        rows[i, :real[i]] = rng_tok.integers(0, TOKEN_HIGH + 1, size=int(real[i]))
+    bins = token_budget_bins(_round_up(real, q), budget)
+    return {"rows": rows, "real_len": real.astype(np.int32), "bins": bins, "q": q,
+            "budget": budget}
+
+
+def pad_tail_stream(seed: int = 7, T: int = 131072, tail_hi: int = 8192) -> dict:
+    """A flat token stream with a right-padded tail of a non-content pad id."""
+    rng_len, rng_tok = _streams(seed)
+    tail = int(rng_len.integers(0, tail_hi + 1))
+    ids = rng_tok.integers(0, TOKEN_HIGH + 1, size=T, dtype=np.int64)
+    pad_id = TOKEN_HIGH + 1
+    ids[T - tail:] = pad_id
+    return {"input_ids": ids, "pad_id": pad_id, "tail": tail}
 
 
 def run_positions(doc_ids: np.ndarray) -> np.ndarray:

@@ -19,6 +19,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert {"psq_params_from_doc_ids", "psq_process_thd", "psq_pack_rows",
+            "psq_split_thd", "psq_padding_mask_from_token_ids", "psq_pack_padded_rows",
             "psq_status_string", "psq_workspace_init"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -34,6 +35,7 @@ def test_status_strings(lib):
     assert "capacity" in _lib.status_string(_lib.DATA_PACK_OVERFLOW, True)
     assert "no sequence" in _lib.status_string(_lib.DATA_EMPTY_ROW, True)
     assert _lib.status_string(999, False) == "unknown error code"
+    assert "content" in _lib.status_string(_lib.DATA_PAD_IS_CONTENT, True)
 
 
 def test_workspace_sizes(lib):
@@ -44,6 +46,14 @@ def test_workspace_sizes(lib):
     lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, _lib.I64, 64)
     assert _lib.psq_process_thd_workspace(lay, 16, 8192) >= 256 + 8 * 16
     assert lib.psq_pack_rows_workspace(65536, 3555, 16384) >= 256
+    assert lib.psq_padding_mask_from_token_ids_workspace(131072) >= 256
+    # the split stages both boundary arrays of every group: 2 * 4 * G * (Bc*P+1)
+    one = _lib.psq_split_thd_workspace(lay, 16, 8192, 1)
+    four = _lib.psq_split_thd_workspace(lay, 16, 8192, 4)
+    assert one == _lib.psq_process_thd_workspace(lay, 16, 8192)
+    assert four >= one + 2 * 4 * 4 * (4 * 64 + 1)
+    assert _lib.psq_split_thd_workspace(lay, 16, 8192, 3) == 0     # 3 does not divide 16
+    assert _lib.psq_split_thd_workspace(lay, 16, 8192, 0) == 0
 
 
 def _doc(lib, **kw):
@@ -106,6 +116,81 @@ def test_process_thd_validation(lib):
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
     arr, n = _lib.make_copies([(FAKE, FAKE + 65536, -1, 64, 64)])
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+    # a destination stride below the row length, or negative
+    arr, n = _lib.make_copies([(FAKE, FAKE + 65536, 4, 64, 64, 32)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+    arr, n = _lib.make_copies([(FAKE, FAKE + 65536, 1, 64, 64, -8)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+    # destination rows at a stride reaching back into the source
+    arr, n = _lib.make_copies([(FAKE + 4096, FAKE, 4, 64, 64, 2048)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+
+
+def _split(lib, layout, **kw):
+    a = dict(B=4, S=6, G=2, cu=FAKE, cp=None, w=FAKE, n=FAKE, mx=FAKE, pb=FAKE, mask=None,
+             st=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    copies, _ = _lib.make_copies([])
+    lay = ctypes.byref(layout) if layout is not None else None
+    return lib.psq_split_thd(lay, a["B"], a["S"], a["G"], a["cu"], a["cp"], a["w"], a["n"],
+                             a["mx"], a["pb"], a["mask"], copies, 0, a["st"], a["ws"], a["wsb"],
+                             a["stream"])
+
+
+def test_split_thd_validation(lib):
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, FAKE, _lib.I64, 1)
+    assert _split(lib, None) == _lib.ERR_ARG
+    assert _split(lib, lay, G=0) == _lib.ERR_ARG
+    assert _split(lib, lay, G=3) == _lib.ERR_ARG                   # does not divide B
+    assert _split(lib, _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=FAKE)) == _lib.ERR_ARG
+    assert _split(lib, lay, w=None) == _lib.ERR_ARG
+    assert _split(lib, lay, n=None) == _lib.ERR_ARG
+    assert _split(lib, lay, st=None) == _lib.ERR_ARG
+    assert _split(lib, lay, B=1 << 20, S=1 << 12, G=1 << 10) == _lib.ERR_OVERFLOW
+    assert _split(lib, lay, ws=None) == _lib.ERR_WORKSPACE
+    assert _split(lib, lay, wsb=256) == _lib.ERR_WORKSPACE
+
+
+def _padids(lib, **kw):
+    a = dict(ids=FAKE, dt=_lib.I64, T=64, pad=0, mask=FAKE, nc=None, st=FAKE, ws=FAKE,
+             wsb=256, stream=None)
+    a.update(kw)
+    return lib.psq_padding_mask_from_token_ids(a["ids"], a["dt"], a["T"], a["pad"], a["mask"],
+                                               a["nc"], a["st"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_padding_mask_from_token_ids_validation(lib):
+    assert _padids(lib, T=-1) == _lib.ERR_ARG
+    assert _padids(lib, dt=2) == _lib.ERR_ARG
+    assert _padids(lib, T=1 << 31) == _lib.ERR_OVERFLOW
+    assert _padids(lib, ids=None) == _lib.ERR_ARG
+    assert _padids(lib, mask=None) == _lib.ERR_ARG
+    assert _padids(lib, st=None) == _lib.ERR_ARG
+    assert _padids(lib, ws=None) == _lib.ERR_WORKSPACE
+    assert _padids(lib, wsb=8) == _lib.ERR_WORKSPACE
+
+
+def _rect(lib, **kw):
+    a = dict(rows=FAKE, W=10, rl=FAKE, N=2, q=4, order=None, ps=FAKE, P=1, C=20, fold=0,
+             pad=0, packed=FAKE, tm=FAKE, cu=FAKE, cp=FAKE, st=FAKE, ws=FAKE, wsb=256,
+             stream=None)
+    a.update(kw)
+    return lib.psq_pack_padded_rows(a["rows"], a["W"], a["rl"], a["N"], a["q"], a["order"],
+                                    a["ps"], a["P"], a["C"], a["fold"], a["pad"], a["packed"],
+                                    a["tm"], a["cu"], a["cp"], a["st"], a["ws"], a["wsb"],
+                                    a["stream"])
+
+
+def test_pack_padded_rows_validation(lib):
+    assert _rect(lib, W=-1) == _lib.ERR_ARG
+    assert _rect(lib, q=0) == _lib.ERR_ARG
+    assert _rect(lib, C=0) == _lib.ERR_ARG
+    assert _rect(lib, N=1 << 30, W=1 << 33) == _lib.ERR_OVERFLOW
+    assert _rect(lib, rows=None) == _lib.ERR_ARG
+    assert _rect(lib, rl=None) == _lib.ERR_ARG
+    assert _rect(lib, ps=None) == _lib.ERR_ARG
+    assert _rect(lib, cu=None) == _lib.ERR_ARG
+    assert _rect(lib, ws=None) == _lib.ERR_WORKSPACE
 
 
 def _pack(lib, **kw):
@@ -144,3 +229,11 @@ def test_python_api_refuses_cpu_tensors():
         psq.process_input_for_thd({"input_ids": torch.zeros((1, 4), dtype=torch.int64),
                                    "position_ids": torch.zeros((1, 4), dtype=torch.int64),
                                    "seq_lens": torch.tensor([[4]])})
+    with pytest.raises(ValueError, match="GPU"):
+        psq.split_batch_into_thd_chunks({"input_ids": torch.zeros((2, 4), dtype=torch.int64),
+                                         "position_ids": torch.zeros((2, 4), dtype=torch.int64),
+                                         "seq_lens": torch.tensor([[4], [4]])}, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        psq.thd_padding_mask_from_token_ids(torch.zeros(4, dtype=torch.int64), 0)
+    with pytest.raises(ValueError, match="GPU"):
+        psq.pack_padded_rows(torch.zeros((2, 4), dtype=torch.int64), [1, 2], [[0, 1]], 4)

@@ -235,3 +235,7 @@ def test_trainer_rectangle_length_beyond_row_is_rejected():
     rows = np.zeros((2, 4), dtype=np.int64)
     assert oracle.pack_rect(rows, [4, 5], 1, [[0, 1]], width=9)["status"] == oracle.BAD_LENGTH
     assert oracle.pack_rect(rows, [4, -1], 1, [[0, 1]], width=9)["status"] == oracle.BAD_LENGTH
+    # every condition is reported: a too-long member (not counted toward the
+    # pack's fill) together with an empty bin
+    st = oracle.pack_rect(rows, [7, 3], 1, [[0, 1], []], width=3)["status"]
+    assert st == oracle.BAD_LENGTH | oracle.EMPTY_PACK

@@ -57,3 +57,25 @@ def test_next_fit_closure():
 def test_run_positions():
     d = np.array([[1, 1, 2, 0, 0], [1, 1, 1, 1, 0]])
     assert synth.run_positions(d).tolist() == [[0, 1, 0, 0, 1], [0, 1, 2, 3, 0]]
+
+
+def test_token_budget_bins():
+    padded = np.array([64, 128, 16384, 64, 8192, 8192, 192])
+    bins = synth.token_budget_bins(padded, 16384)
+    flat = sorted(i for b in bins for i in b)
+    assert flat == list(range(padded.size))
+    assert all(int(padded[b].sum()) <= 16384 for b in bins)
+    assert bins[0] == [2]                     # the longest source opens the first bin
+    w = synth.trainer_rectangle()
+    rows, rl = w["rows"], w["real_len"]
+    assert rows.shape == (256, int(rl.max()))
+    assert sorted(i for b in w["bins"] for i in b) == list(range(256))
+    for i in range(0, 256, 17):               # zero past each length
+        assert not rows[i, rl[i]:].any()
+
+
+def test_pad_tail_stream():
+    w = synth.pad_tail_stream()
+    ids, pad, tail = w["input_ids"], w["pad_id"], w["tail"]
+    assert ids.size == 131072 and pad > synth.TOKEN_HIGH
+    assert np.all(ids[ids.size - tail:] == pad) and not np.any(ids[:ids.size - tail] == pad)

@@ -10,11 +10,13 @@ must not synchronize use the C ABI (or :mod:`._lib`) directly.
 * :func:`packed_seq_params_from_doc_ids`, :class:`PackedSeqParams`,
   :func:`to_flash_attention_kwargs` -- NeMo AutoModel API,
   ``nemo_automodel.components.datasets.packed_seq``.
-* :func:`process_input_for_thd` -- NeMo AutoModel 0.5 API,
+* :func:`process_input_for_thd`, :func:`split_batch_into_thd_chunks`,
+  :func:`thd_padding_mask_from_token_ids` -- NeMo AutoModel 0.5 API,
   ``nemo_automodel.components.distributed.thd_utils`` (with
   ``_thd_padding_mask``).
-* :func:`pack_rows` -- "Who packs the sequences: the loader, or the
-  trainer?", Trainer packs / Loader packs.
+* :func:`pack_rows` (Loader packs) and :func:`pack_padded_rows` (Trainer
+  packs, from the padded rectangle) -- "Who packs the sequences: the loader,
+  or the trainer?".
 """
 from __future__ import annotations
 
@@ -25,7 +27,9 @@ import torch
 from . import _lib
 
 __all__ = ["PackedSeqParams", "packed_seq_params_from_doc_ids", "to_flash_attention_kwargs",
-           "process_input_for_thd", "pack_rows", "workspace_for"]
+           "process_input_for_thd", "split_batch_into_thd_chunks",
+           "thd_padding_mask_from_token_ids", "pack_rows", "pack_padded_rows",
+           "workspace_for"]
 
 _DTYPES = {torch.int32: _lib.I32, torch.int64: _lib.I64}
 _WORKSPACES: dict = {}
@@ -113,6 +117,25 @@ def to_flash_attention_kwargs(params: PackedSeqParams) -> dict:
             "max_length_q": params.max_seqlen, "max_length_k": params.max_seqlen}
 
 
+def _table_layout(batch: dict, B: int, seq_lens_padding_value: int):
+    """(layout, P, has_padded) of a ``seq_lens`` / ``seq_lens_padded`` batch."""
+    L = batch["seq_lens"]
+    Lp = batch.get("seq_lens_padded")
+    _require_gpu(L, "seq_lens")
+    lt = _int_dtype(L, "seq_lens")
+    if L.dim() != 2 or L.shape[0] != B or not L.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous [B, num_packs] tensor")
+    P = int(L.shape[1])
+    if Lp is not None:
+        _require_gpu(Lp, "seq_lens_padded")
+        if Lp.shape != L.shape or Lp.dtype != L.dtype or not Lp.is_contiguous():
+            raise ValueError("seq_lens_padded must match seq_lens in shape and dtype")
+    layout = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, L.data_ptr(),
+                              Lp.data_ptr() if Lp is not None else None, lt, P,
+                              seq_lens_padding_value)
+    return layout, P, Lp is not None
+
+
 def _copy_desc(src: torch.Tensor, dst: torch.Tensor, name: str) -> tuple:
     """(src, dst, rows, row_bytes, src_row_stride_bytes) of one collapse."""
     esz = src.element_size()
@@ -177,21 +200,7 @@ def process_input_for_thd(batch: dict, seq_lens_padding_value: int = -1000,
 
     has_padded = False
     if "seq_lens" in batch:
-        L = batch["seq_lens"]
-        Lp = batch.get("seq_lens_padded")
-        _require_gpu(L, "seq_lens")
-        lt = _int_dtype(L, "seq_lens")
-        if L.dim() != 2 or L.shape[0] != B or not L.is_contiguous():
-            raise ValueError("seq_lens must be a contiguous [B, num_packs] tensor")
-        P = int(L.shape[1])
-        if Lp is not None:
-            _require_gpu(Lp, "seq_lens_padded")
-            if Lp.shape != L.shape or Lp.dtype != L.dtype or not Lp.is_contiguous():
-                raise ValueError("seq_lens_padded must match seq_lens in shape and dtype")
-            has_padded = True
-        layout = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, L.data_ptr(),
-                                  Lp.data_ptr() if Lp is not None else None, lt, P,
-                                  seq_lens_padding_value)
+        layout, P, has_padded = _table_layout(batch, B, seq_lens_padding_value)
         cap = B * P + 1
     elif "doc_ids" in batch:
         d = batch["doc_ids"]
@@ -278,3 +287,181 @@ def pack_rows(src_tokens: torch.Tensor, src_offsets: torch.Tensor, real_len: tor
     return {"input_ids": packed, "token_mask": tmask, "cu_seqlens": cu_list,
             "cu_seqlens_padded": cp_list, "cu_seqlens_flat": cu[:used],
             "cu_seqlens_padded_flat": cp[:used]}
+
+
+def split_batch_into_thd_chunks(batch: dict, num_chunks: int, seq_lens_padding_value: int = -1000,
+                                padding_token_id: int = 0) -> dict:
+    """Split the batch along rows into ``num_chunks`` equal groups, convert
+    each group to THD as :func:`process_input_for_thd` does, and stack.
+
+    One kernel launch converts every group (each with its own boundaries,
+    absorption, ``max_seqlen`` and mask).  Returned tensors gain a leading
+    chunk axis: ``input_ids`` ``[num_chunks, B/num_chunks*S(, H)]``,
+    ``position_ids`` likewise (mRoPE: ``[num_chunks, n_rope, 1, ...]``),
+    ``cu_seqlens`` / ``cu_seqlens_padded`` ``[num_chunks, L]`` with every
+    chunk filled up to the longest with ``seq_lens_padding_value``,
+    ``max_seqlen`` int32 ``[num_chunks]``, ``pad_between_seqs`` bool
+    ``[num_chunks]``, ``padding_mask`` ``[num_chunks, B/num_chunks*S]``.
+    ``num_chunks <= 1`` returns :func:`process_input_for_thd` unchanged.
+    Needs the table layout (``seq_lens``).
+    """
+    if num_chunks <= 1:
+        return process_input_for_thd(batch, seq_lens_padding_value, padding_token_id)
+    input_ids = batch["input_ids"]
+    position_ids = batch["position_ids"]
+    labels = batch.get("labels")
+    _require_gpu(input_ids, "input_ids")
+    dev = input_ids.device
+    if input_ids.dim() not in (2, 3):
+        raise ValueError("input_ids must be [B, S] or [B, S, H]")
+    B, S = int(input_ids.shape[0]), int(input_ids.shape[1])
+    if B % num_chunks != 0:
+        raise ValueError(f"num_chunks ({num_chunks}) must evenly divide the batch size ({B})")
+    if "seq_lens" not in batch:
+        raise ValueError("split_batch_into_thd_chunks needs seq_lens (+ seq_lens_padded)")
+    G = int(num_chunks)
+    Bc = B // G
+    Tc = Bc * S
+    stream = _stream(dev)
+
+    out = {}
+    copies = []
+    ids_out = torch.empty((G, Tc) + tuple(input_ids.shape[2:]), dtype=input_ids.dtype,
+                          device=dev)
+    copies.append(_copy_desc(input_ids, ids_out, "input_ids"))
+    out["input_ids"] = ids_out
+    if labels is not None:
+        _require_gpu(labels, "labels")
+        if tuple(labels.shape[:2]) != (B, S):
+            raise ValueError("labels must be [B, S]")
+        lab_out = torch.empty((G, Tc) + tuple(labels.shape[2:]), dtype=labels.dtype, device=dev)
+        copies.append(_copy_desc(labels, lab_out, "labels"))
+        out["labels"] = lab_out
+    _require_gpu(position_ids, "position_ids")
+    if position_ids.dim() == 3:       # mRoPE [n_rope, B, S] -> [G, n_rope, 1, Tc]
+        n_rope = int(position_ids.shape[0])
+        if tuple(position_ids.shape[1:]) != (B, S) or not position_ids.is_contiguous():
+            raise ValueError("mRoPE position_ids must be a contiguous [n_rope, B, S] tensor")
+        pos_out = torch.empty((G, n_rope, 1, Tc), dtype=position_ids.dtype, device=dev)
+        esz = position_ids.element_size()
+        for k in range(n_rope):       # rope k of every group, written at a stride
+            copies.append((position_ids.data_ptr() + k * B * S * esz,
+                           pos_out.data_ptr() + k * Tc * esz, G, Tc * esz, Tc * esz,
+                           n_rope * Tc * esz))
+    else:
+        if tuple(position_ids.shape) != (B, S):
+            raise ValueError("position_ids must be [B, S]")
+        pos_out = torch.empty((G, Tc), dtype=position_ids.dtype, device=dev)
+        copies.append(_copy_desc(position_ids, pos_out, "position_ids"))
+    out["position_ids"] = pos_out
+    if len(copies) > _lib.MAX_COPIES:
+        raise ValueError(f"at most {_lib.MAX_COPIES} collapse copies per call")
+
+    layout, P, has_padded = _table_layout(batch, B, seq_lens_padding_value)
+    cap = G * (Bc * P + 1)
+    cu = torch.empty(cap, dtype=torch.int32, device=dev)
+    cp = torch.empty(cap, dtype=torch.int32, device=dev) if has_padded else None
+    mask = torch.empty((G, Tc), dtype=torch.bool, device=dev)
+    per = torch.empty((3, G), dtype=torch.int32, device=dev)    # n, max, pad_between
+    scal = torch.empty(2, dtype=torch.int32, device=dev)        # width, status
+    pp, sp = per.data_ptr(), scal.data_ptr()
+    arr, n_copies = _lib.make_copies(copies)
+    ws = workspace_for(dev, _lib.psq_split_thd_workspace(layout, B, S, G))
+    _lib.psq_split_thd(layout, B, S, G, cu.data_ptr(), cp.data_ptr() if cp is not None else None,
+                       sp, pp, pp + 4 * G, pp + 8 * G, mask.data_ptr(), arr, n_copies, sp + 4,
+                       ws.data_ptr(), ws.numel(), stream)
+    width, st = scal.cpu().tolist()
+    _raise_status(st, "split_batch_into_thd_chunks")
+    out["cu_seqlens"] = cu[: G * width].view(G, width)
+    if cp is not None:
+        out["cu_seqlens_padded"] = cp[: G * width].view(G, width)
+    out["pad_between_seqs"] = per[2].bool()
+    out["max_seqlen"] = per[1]
+    out["padding_mask"] = mask
+    for key, value in batch.items():
+        if not isinstance(value, torch.Tensor) and key not in out:
+            out[key] = value
+    return out
+
+
+def thd_padding_mask_from_token_ids(input_ids: torch.Tensor, padding_token_id: int) -> torch.Tensor:
+    """Padding mask by token value, for callers with no pack metadata.
+
+    ``input_ids`` ``[total_tokens]``; returns bool ``[total_tokens]``, True on
+    padding.  Raises ``ValueError`` when ``padding_token_id`` also occurs as
+    content, i.e. when the pad slots are not a right-padded tail.
+    """
+    _require_gpu(input_ids, "input_ids")
+    dt = _int_dtype(input_ids, "input_ids")
+    if input_ids.dim() != 1 or not input_ids.is_contiguous():
+        raise ValueError("input_ids must be a contiguous [total_tokens] tensor")
+    dev = input_ids.device
+    T = input_ids.numel()
+    mask = torch.empty(T, dtype=torch.bool, device=dev)
+    scal = torch.empty(2, dtype=torch.int32, device=dev)        # num_content, status
+    sp = scal.data_ptr()
+    ws = workspace_for(dev, _lib.psq_padding_mask_from_token_ids_workspace(T))
+    _lib.psq_padding_mask_from_token_ids(input_ids.data_ptr(), dt, T, int(padding_token_id),
+                                         mask.data_ptr(), sp, sp + 4, ws.data_ptr(), ws.numel(),
+                                         _stream(dev))
+    _raise_status(int(scal[1].item()), "thd_padding_mask_from_token_ids")
+    return mask
+
+
+def pack_padded_rows(input_ids: torch.Tensor, input_lengths, bins, pad_to: int,
+                     width: int | None = None, fold: bool = False, pad_token: int = 0) -> dict:
+    """Trainer packs: squeeze the padded rectangle ``input_ids [N, W]`` into bins.
+
+    ``bins`` lists each bin's row indices (chosen on the host, e.g. by token
+    budget).  Row ``i`` holds ``input_lengths[i]`` real tokens; each is padded
+    to a multiple of ``pad_to`` and a bin's rows are laid end to end.  The
+    output row width defaults to the widest bin's padded sum (the row is as
+    wide as the batch needs), computed on the host from ``input_lengths``;
+    the trainer path leaves ``fold`` off.  Returns the keys of
+    :func:`pack_rows` plus ``width``.
+    """
+    _require_gpu(input_ids, "input_ids")
+    if input_ids.dtype != torch.int64 or input_ids.dim() != 2 or not input_ids.is_contiguous():
+        raise TypeError("input_ids must be a contiguous int64 [N, W] tensor")
+    dev = input_ids.device
+    N, W = int(input_ids.shape[0]), int(input_ids.shape[1])
+    lens_host = torch.as_tensor(input_lengths, dtype=torch.int64).cpu()
+    if lens_host.numel() != N:
+        raise ValueError("input_lengths must hold one length per row")
+    bins = [list(map(int, b)) for b in bins]
+    if width is None:
+        lh = lens_host.tolist()
+        width = max((sum(-(-lh[i] // pad_to) * pad_to for i in b) for b in bins), default=0)
+    width = int(width)
+    if width < 1:
+        raise ValueError("the packed row width must be at least 1")
+    P = len(bins)
+    members = [i for b in bins for i in b]
+    order_host = torch.zeros(max(N, 1), dtype=torch.int32)
+    if len(members) > N:
+        raise ValueError("the bins hold more members than there are rows")
+    order_host[: len(members)] = torch.as_tensor(members, dtype=torch.int32)
+    ps_host = torch.zeros(P + 1, dtype=torch.int64)
+    ps_host[1:] = torch.as_tensor([len(b) for b in bins], dtype=torch.int64).cumsum(0)
+    order_dev = order_host.to(dev)
+    ps_dev = ps_host.to(dev)
+    lens_dev = lens_host.to(torch.int32).to(dev)
+    packed = torch.empty((P, width), dtype=torch.int64, device=dev)
+    tmask = torch.empty((P, width), dtype=torch.uint8, device=dev)
+    csr = max(N + P, 1)
+    cu = torch.empty(csr, dtype=torch.int32, device=dev)
+    cp = torch.empty(csr, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = workspace_for(dev, _lib.psq_pack_rows_workspace(N, P, width))
+    _lib.psq_pack_padded_rows(input_ids.data_ptr(), W, lens_dev.data_ptr(), N, pad_to,
+                              order_dev.data_ptr(), ps_dev.data_ptr(), P, width, int(bool(fold)),
+                              pad_token, packed.data_ptr(), tmask.data_ptr(), cu.data_ptr(),
+                              cp.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream(dev))
+    _raise_status(int(status.item()), "pack_padded_rows")
+    psl = ps_host.tolist()
+    used = (psl[-1] + P) if P > 0 else 0
+    return {"input_ids": packed, "token_mask": tmask, "width": width,
+            "cu_seqlens": [cu[psl[p] + p: psl[p + 1] + p + 1] for p in range(P)],
+            "cu_seqlens_padded": [cp[psl[p] + p: psl[p + 1] + p + 1] for p in range(P)],
+            "cu_seqlens_flat": cu[:used], "cu_seqlens_padded_flat": cp[:used]}

@@ -26,6 +26,7 @@ DATA_PACK_OVERFLOW = 16
 DATA_EMPTY_PACK = 32
 DATA_BAD_INDEX = 64
 DATA_WORKSPACE = 128
+DATA_PAD_IS_CONTENT = 256
 LAYOUT_SEQ_LENS, LAYOUT_DOC_IDS = 0, 1
 MAX_COPIES = 8
 
@@ -33,7 +34,8 @@ MAX_COPIES = 8
 class PsqCopy(ctypes.Structure):
     _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("row_bytes", ctypes.c_int64),
-                ("src_row_stride_bytes", ctypes.c_int64)]
+                ("src_row_stride_bytes", ctypes.c_int64),
+                ("dst_row_stride_bytes", ctypes.c_int64)]
 
 
 class PsqThdLayout(ctypes.Structure):
@@ -87,6 +89,18 @@ def load():
     lib.psq_process_thd.restype = ci
     lib.psq_process_thd.argtypes = [ctypes.POINTER(PsqThdLayout), i64, i64, vp, vp, vp, vp,
                                     vp, vp, ctypes.POINTER(PsqCopy), ci, vp, vp, sz, vp]
+    lib.psq_split_thd_workspace.restype = sz
+    lib.psq_split_thd_workspace.argtypes = [ctypes.POINTER(PsqThdLayout), i64, i64, i64]
+    lib.psq_split_thd.restype = ci
+    lib.psq_split_thd.argtypes = [ctypes.POINTER(PsqThdLayout), i64, i64, i64, vp, vp, vp, vp,
+                                  vp, vp, vp, ctypes.POINTER(PsqCopy), ci, vp, vp, sz, vp]
+    lib.psq_padding_mask_from_token_ids_workspace.restype = sz
+    lib.psq_padding_mask_from_token_ids_workspace.argtypes = [i64]
+    lib.psq_padding_mask_from_token_ids.restype = ci
+    lib.psq_padding_mask_from_token_ids.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.psq_pack_padded_rows.restype = ci
+    lib.psq_pack_padded_rows.argtypes = [vp, i64, vp, i64, i32, vp, vp, i64, i32, ci, i64,
+                                         vp, vp, vp, vp, vp, vp, sz, vp]
     lib.psq_pack_rows_workspace.restype = sz
     lib.psq_pack_rows_workspace.argtypes = [i64, i64, i32]
     lib.psq_pack_rows.restype = ci
@@ -130,10 +144,11 @@ def make_layout(kind, seq_lens=None, seq_lens_padded=None, lens_dtype=I64, P=0,
 
 
 def make_copies(copies) -> tuple:
-    """``copies``: list of (src, dst, rows, row_bytes, src_row_stride_bytes)."""
+    """``copies``: list of (src, dst, rows, row_bytes, src_row_stride_bytes
+    [, dst_row_stride_bytes]); a missing or 0 destination stride is dense."""
     arr = (PsqCopy * max(len(copies), 1))()
     for i, c in enumerate(copies):
-        arr[i] = PsqCopy(*c)
+        arr[i] = PsqCopy(*(tuple(c) + (0,) * (6 - len(c))))
     return arr, len(copies)
 
 
@@ -163,3 +178,40 @@ def psq_pack_rows(src_tokens, src_len, src_offsets, real_len, N, pad_to, pack_or
                               token_mask, cu_seqlens, cu_seqlens_padded, status, workspace,
                               workspace_bytes, stream)
     return _check(rc, "psq_pack_rows") if check else rc
+
+
+def psq_split_thd_workspace(layout: PsqThdLayout, B: int, S: int, num_chunks: int) -> int:
+    return load().psq_split_thd_workspace(ctypes.byref(layout), B, S, num_chunks)
+
+
+def psq_split_thd(layout, B, S, num_chunks, cu_seqlens, cu_seqlens_padded, cu_width, num_seqs,
+                  max_seqlen, pad_between_seqs, padding_mask, copies, n_copies, status,
+                  workspace, workspace_bytes, stream, check=True) -> int:
+    rc = load().psq_split_thd(ctypes.byref(layout), B, S, num_chunks, cu_seqlens,
+                              cu_seqlens_padded, cu_width, num_seqs, max_seqlen,
+                              pad_between_seqs, padding_mask, copies, n_copies, status,
+                              workspace, workspace_bytes, stream)
+    return _check(rc, "psq_split_thd") if check else rc
+
+
+def psq_padding_mask_from_token_ids_workspace(T: int) -> int:
+    return load().psq_padding_mask_from_token_ids_workspace(T)
+
+
+def psq_padding_mask_from_token_ids(input_ids, ids_dtype, T, pad_id, padding_mask, num_content,
+                                    status, workspace, workspace_bytes, stream,
+                                    check=True) -> int:
+    rc = load().psq_padding_mask_from_token_ids(input_ids, ids_dtype, T, pad_id, padding_mask,
+                                                num_content, status, workspace,
+                                                workspace_bytes, stream)
+    return _check(rc, "psq_padding_mask_from_token_ids") if check else rc
+
+
+def psq_pack_padded_rows(rows, W, real_len, N, pad_to, pack_order, pack_start, P, capacity,
+                         fold, pad_token, packed, token_mask, cu_seqlens, cu_seqlens_padded,
+                         status, workspace, workspace_bytes, stream, check=True) -> int:
+    rc = load().psq_pack_padded_rows(rows, W, real_len, N, pad_to, pack_order, pack_start, P,
+                                     capacity, fold, pad_token, packed, token_mask, cu_seqlens,
+                                     cu_seqlens_padded, status, workspace, workspace_bytes,
+                                     stream)
+    return _check(rc, "psq_pack_padded_rows") if check else rc

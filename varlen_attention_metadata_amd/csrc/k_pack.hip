@@ -21,6 +21,10 @@
 // status bits); the last of those to finish publishes *status.
 // Every access is bounds-checked against the caller's sizes, so bad data
 // can only produce wrong values and status bits, never a stray access.
+//
+// Trainer path from the padded rectangle (src_off == NULL): source i is row
+// i of an [N, src_stride] array, so its offset is i * src_stride and a length
+// beyond the row is a BAD_LENGTH.
 #include "psq_device.hpp"
 #include "psq_internal.hpp"
 
@@ -53,7 +57,7 @@ __device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
 
 __global__ __launch_bounds__(kThreads) void k_pack_rows(
     const int64_t *__restrict__ src, int64_t src_len, const int64_t *__restrict__ src_off,
-    const int32_t *__restrict__ real_len, int64_t N, int32_t q,
+    int64_t src_stride, const int32_t *__restrict__ real_len, int64_t N, int32_t q,
     const int32_t *__restrict__ order, const int64_t *__restrict__ pack_start, int64_t P,
     int32_t C, int fold, int64_t pad_token, int64_t *__restrict__ packed,
     uint8_t *__restrict__ tmask, int32_t *__restrict__ cu, int32_t *__restrict__ cp,
@@ -108,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
                 err |= PSQ_DATA_BAD_INDEX;
             } else {
                 int64_t r = real_len[i];
-                so = src_off[i];
-                if (r < 0) {
+                so = src_off ? src_off[i] : i * src_stride;
+                if (r < 0 || (!src_off && r > src_stride)) {
                     err |= PSQ_DATA_BAD_LENGTH;
                     r = 0;
                 }
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
 size_t pack_rows_workspace() { return 256; }
 
 hipError_t launch_pack_rows(const int64_t *src, int64_t src_len, const int64_t *src_off,
-                            const int32_t *real_len, int64_t N, int32_t q,
+                            int64_t src_stride, const int32_t *real_len, int64_t N, int32_t q,
                             const int32_t *order, const int64_t *pack_start, int64_t P,
                             int32_t C, int fold, int64_t pad_token, int64_t *packed,
                             uint8_t *tmask, int32_t *cu, int32_t *cp, int32_t *status,
@@ -290,7 +294,7 @@ hipError_t launch_pack_rows(const int64_t *src, int64_t src_len, const int64_t *
     const int vec_out = ((uintptr_t)packed % 16) == 0;
     const int vec_mask = ((uintptr_t)tmask % 16) == 0;
     hipLaunchKernelGGL(k_pack_rows, dim3((uint32_t)groups), dim3(kThreads), 0, stream, src,
-                       src_len, src_off, real_len, N, q, order, pack_start, P, C, fold,
+                       src_len, src_off, src_stride, real_len, N, q, order, pack_start, P, C, fold,
                        pad_token, packed, tmask, cu, cp, status, (WsHeader *)workspace,
                        n_chunks, vec_out, vec_mask);
     return hipGetLastError();

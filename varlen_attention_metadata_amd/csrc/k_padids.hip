@@ -1,0 +1,132 @@
+// k_padids.hip -- the metadata-free padding mask.
+//
+// NeMo AutoModel 0.5 API, nemo_automodel.components.distributed.thd_utils:
+// thd_padding_mask_from_token_ids.  A slot is padding when its id equals the
+// pad id; that is only a correct mask when the pad slots form a right-padded
+// tail, so the call also checks exactly that: the first pad slot must come
+// after the last non-pad slot, otherwise the pad id is also content and the
+// status bit PSQ_DATA_PAD_IS_CONTENT is set.
+//
+// One streaming pass: each workgroup reads a tile of ids with 16-byte loads,
+// writes the mask bytes, and reduces two indices over its tile (the first
+// pad slot, the last non-pad slot) with wave64 DPP max scans.  Each tile
+// folds them into the workspace header with one atomic max each; the last
+// workgroup to finish compares them and writes status and the content
+// length.
+#include "psq_device.hpp"
+#include "psq_internal.hpp"
+
+namespace psq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kIters = 8;
+
+template <typename TI>
+__global__ __launch_bounds__(kThreads) void k_pad_ids(const TI *__restrict__ ids, uint32_t T,
+                                                      int64_t pad, uint8_t *__restrict__ mask,
+                                                      int32_t *__restrict__ num_content,
+                                                      int32_t *__restrict__ status,
+                                                      WsHeader *__restrict__ ws, int vec_in,
+                                                      int vec_mask) {
+    constexpr int kV = 16 / (int)sizeof(TI);          // ids per 16-byte load
+    constexpr uint32_t kTile = (uint32_t)kThreads * kV * kIters;
+    __shared__ int32_t s_red[2][kWaves];
+    __shared__ uint32_t s_slot;
+
+    // fp: T - (first pad slot), 0 when none; ln: 1 + (last non-pad slot), 0 when none
+    int32_t fp = 0, ln = 0;
+    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const uint64_t t0 = base + ((uint64_t)it * kThreads + threadIdx.x) * kV;
+        if (t0 >= T) break;
+        TI v[kV];
+        const bool whole = t0 + kV <= T;
+        if (vec_in && whole) {
+            const u32x4 w = __builtin_nontemporal_load((const u32x4 *)(ids + t0));
+            __builtin_memcpy(v, &w, 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kV; ++e) v[e] = (t0 + e < T) ? ids[t0 + e] : (TI)0;
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) {
+            const uint32_t t = (uint32_t)t0 + (uint32_t)e;
+            if (t0 + e < T) {
+                const bool is_pad = (int64_t)v[e] == pad;
+                bits |= (is_pad ? 1u : 0u) << (8 * e);
+                if (is_pad)
+                    fp = max(fp, (int32_t)(T - t));
+                else
+                    ln = max(ln, (int32_t)(t + 1u));
+            }
+        }
+        if (vec_mask && whole) {
+            if constexpr (kV == 4)
+                *(uint32_t *)(mask + t0) = bits;
+            else
+                *(uint16_t *)(mask + t0) = (uint16_t)bits;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kV; ++e)
+                if (t0 + e < T) mask[t0 + e] = (uint8_t)(bits >> (8 * e));
+        }
+    }
+
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    fp = wave_incl_max(fp);
+    ln = wave_incl_max(ln);
+    if (lane == kWave - 1) {
+        s_red[0][w] = fp;
+        s_red[1][w] = ln;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t a = 0, b = 0;
+#pragma unroll
+        for (int q = 0; q < kWaves; ++q) {
+            a = max(a, s_red[0][q]);
+            b = max(b, s_red[1][q]);
+        }
+        if (a) max_relaxed(&ws->max, a);
+        if (b) max_relaxed(&ws->n, b);
+    }
+    if (finish_is_last(ws, gridDim.x, &s_slot) && threadIdx.x == 0) {
+        const uint32_t first_pad = T - ld_relaxed((const uint32_t *)&ws->max);
+        const uint32_t after_content = ld_relaxed((const uint32_t *)&ws->n);
+        *status = after_content > first_pad ? PSQ_DATA_PAD_IS_CONTENT : 0;
+        if (num_content) *num_content = (int32_t)first_pad;
+        st_relaxed((uint32_t *)&ws->max, 0u);
+        st_relaxed((uint32_t *)&ws->n, 0u);
+        st_relaxed(&ws->done, 0u);
+    }
+}
+
+}  // namespace
+
+size_t pad_ids_workspace() { return 256; }
+
+hipError_t launch_pad_ids(const void *ids, int ids_dtype, int64_t T, int64_t pad,
+                          uint8_t *mask, int32_t *num_content, int32_t *status,
+                          void *workspace, hipStream_t stream) {
+    const int per = ids_dtype == PSQ_I64 ? 2 : 4;
+    const uint64_t tile = (uint64_t)kThreads * per * kIters;
+    const uint64_t grid = T > 0 ? ((uint64_t)T + tile - 1) / tile : 1;
+    const int vec_in = ((uintptr_t)ids % 16) == 0;
+    const int vec_mask = ((uintptr_t)mask % (uintptr_t)per) == 0;
+    WsHeader *ws = (WsHeader *)workspace;
+    if (ids_dtype == PSQ_I64)
+        hipLaunchKernelGGL(k_pad_ids<int64_t>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                           (const int64_t *)ids, (uint32_t)T, pad, mask, num_content, status,
+                           ws, vec_in, vec_mask);
+    else
+        hipLaunchKernelGGL(k_pad_ids<int32_t>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                           (const int32_t *)ids, (uint32_t)T, pad, mask, num_content, status,
+                           ws, vec_in, vec_mask);
+    return hipGetLastError();
+}
+
+}  // namespace psq

@@ -26,6 +26,16 @@
 // carrying (sequence count, real-token sum) and writes the row's entries of
 // cu_seqlens / cu_seqlens_padded.  The last workgroup to finish applies the
 // absorption and writes the scalars.
+//
+// The same kernel serves split_batch_into_thd_chunks (same page): the rows
+// fall into G equal groups and each group is an independent
+// process_input_for_thd call.  The look-back restarts at every group's first
+// row (that row publishes an inclusive prefix at once), every group keeps its
+// own record (count, sums, flags, max) in the workspace, and the last
+// workgroup finishes each group.  With G > 1 the boundaries are staged per
+// group at a fixed stride and the last workgroup writes them out as one
+// [G, L] array, L the longest group's length, shorter groups filled with the
+// sentinel.
 #include "psq_copy.hpp"
 #include "psq_device.hpp"
 #include "psq_internal.hpp"
@@ -148,6 +158,33 @@ __device__ __forceinline__ uint32_t row_batch(RowLds &s, const TL *__restrict__ 
     return tot[0];
 }
 
+// Per-group record in the workspace (zero between calls).
+struct GroupRec {
+    uint32_t flags;     // 1: some interior real boundary departs from the physical one
+    int32_t max;        // largest real length
+    uint32_t n;         // sequences of the group (published by its last row)
+    uint32_t total;     // real tokens of the group
+    uint32_t cu_last;   // cu_seqlens[n-1] of the group
+    uint32_t pad_[3];
+};
+static_assert(sizeof(GroupRec) == 32, "group record size");
+
+// Workspace layout: header | row descriptors [B] | group records [G] |
+// (G > 1) staged cu [G*ld] | staged cp [G*ld].
+struct ThdWsLayout {
+    size_t recs, stage_cu, stage_cp, bytes;
+};
+inline ThdWsLayout thd_ws_layout(int64_t B, int64_t G, int64_t ld) {
+    ThdWsLayout w;
+    w.recs = round_up(kWsDescOffset + 8 * (size_t)(B > 0 ? B : 1), 256);
+    const size_t after = round_up(w.recs + sizeof(GroupRec) * (size_t)(G > 0 ? G : 1), 256);
+    const size_t stage = G > 1 ? round_up(4 * (size_t)G * (size_t)ld, 256) : 0;
+    w.stage_cu = after;
+    w.stage_cp = after + stage;
+    w.bytes = after + 2 * stage;
+    return w;
+}
+
 template <typename TL>
 struct ThdArgs {
     const TL *L, *Lp;
@@ -155,7 +192,10 @@ struct ThdArgs {
     int64_t pad_value;
     uint32_t n_chunks;
     int vec_mask;
-    int32_t *cu, *cp, *num_seqs, *max_seqlen, *pad_between;
+    uint32_t G, Bc, ld;          // groups, rows per group, staged stride
+    int32_t *cu, *cp, *num_seqs, *max_seqlen, *pad_between, *cu_width;
+    int32_t *cu_st, *cp_st;      // where leaders write (the outputs when G == 1)
+    GroupRec *recs;
     uint8_t *mask;
     int32_t *status;
     WsHeader *ws;
@@ -164,12 +204,21 @@ struct ThdArgs {
 // One (row, chunk) per workgroup; `n_groups` is the number of workgroups
 // running this body (the launch may append copy workgroups after them).
 template <typename TL>
-__device__ __forceinline__ void thd_tables_body(
-    const TL *__restrict__ L, const TL *__restrict__ Lp, uint32_t B, uint32_t P, uint32_t S,
-    int64_t pad_value, uint32_t n_chunks, int vec_mask, int32_t *__restrict__ cu,
-    int32_t *__restrict__ cp, int32_t *__restrict__ num_seqs, int32_t *__restrict__ max_seqlen,
-    int32_t *__restrict__ pad_between, uint8_t *__restrict__ mask, int32_t *__restrict__ status,
-    WsHeader *__restrict__ ws, uint32_t n_groups) {
+__device__ __forceinline__ void thd_tables_body(const ThdArgs<TL> &args, uint32_t n_groups) {
+    const TL *__restrict__ L = args.L;
+    const TL *__restrict__ Lp = args.Lp;
+    const uint32_t B = args.B, P = args.P, S = args.S;
+    const int64_t pad_value = args.pad_value;
+    const uint32_t n_chunks = args.n_chunks;
+    const int vec_mask = args.vec_mask;
+    const uint32_t G = args.G, Bc = args.Bc, ld = args.ld;
+    int32_t *__restrict__ cu = args.cu;
+    int32_t *__restrict__ cp = args.cp;
+    int32_t *__restrict__ cu_st = args.cu_st;
+    int32_t *__restrict__ cp_st = args.cp_st;
+    GroupRec *__restrict__ recs = args.recs;
+    uint8_t *__restrict__ mask = args.mask;
+    WsHeader *__restrict__ ws = args.ws;
     __shared__ RowLds s;
     __shared__ __attribute__((aligned(16))) uint8_t s_mask[kSlots];
     __shared__ uint32_t s_slot;
@@ -186,13 +235,15 @@ __device__ __forceinline__ void thd_tables_body(
         s_wserr = 0;
     }
     const uint32_t ticket = claim_tile(ws, &s_slot);
-    const uint64_t T = (uint64_t)B * S;
+    const uint32_t Tc = Bc * S;     // tokens of one group (< 2^31)
     const int lane = lane_id();
 
     if ((uint64_t)ticket < (uint64_t)B * n_chunks) {
         const uint32_t r = ticket / n_chunks;
         const uint32_t c = ticket % n_chunks;
         const bool leader = (c == 0);
+        const uint32_t g = r / Bc;           // group of the row
+        const uint32_t rg = r - g * Bc;      // row inside its group
         const uint32_t lo = c * kSlots;
         const uint32_t hi = min(S, lo + kSlots);
         const uint64_t row_off = (uint64_t)r * P;
@@ -251,13 +302,15 @@ __device__ __forceinline__ void thd_tables_body(
             const bool last_untight_folded =
                 (uint32_t)s.last_real != (uint32_t)s.last_pad + (S - carry[1]);
             bool disagree = untight_nonlast > 0;
-            if (r + 1 < B && count) disagree = disagree || last_untight_folded;
+            if (rg + 1 < Bc && count) disagree = disagree || last_untight_folded;
 
-            // look-back over rows: (sequence count, real-token sum)
+            // look-back over the rows of the group: (sequence count, real-token
+            // sum); a group's first row publishes an inclusive prefix at once,
+            // so no look-back crosses into the previous group
             if (threadIdx.x < kWave) {
                 uint32_t ex_a = 0, ex_b = 0;
-                if (r == 0) {
-                    if (lane == 0) st_relaxed(desc, desc_pack(kDescIncl, count, realsum));
+                if (rg == 0) {
+                    if (lane == 0) st_relaxed(desc + r, desc_pack(kDescIncl, count, realsum));
                 } else {
                     if (lane == 0) st_relaxed(desc + r, desc_pack(kDescAgg, count, realsum));
                     bool timed_out;
@@ -274,8 +327,10 @@ __device__ __forceinline__ void thd_tables_body(
             }
             __syncthreads();
             const uint32_t ex_a = s_ex_a, ex_b = s_ex_b;
-            const uint64_t cap = (uint64_t)B * P;     // caller capacity is B*P+1
+            const uint64_t cap = (uint64_t)Bc * P;    // a group holds at most Bc*P+1 entries
             bool oob = (uint64_t)ex_a + count > cap;
+            int32_t *__restrict__ cu_g = cu_st + (uint64_t)g * ld;
+            int32_t *__restrict__ cp_g = cp_st ? cp_st + (uint64_t)g * ld : nullptr;
 
             // write the row's boundaries (a second pass over the table when
             // the row did not fit one LDS batch)
@@ -291,8 +346,8 @@ __device__ __forceinline__ void thd_tables_body(
                 }
                 for (uint32_t k = threadIdx.x; k < nb; k += kThreads) {
                     const uint32_t idx = ex_a + base + k;
-                    cu[idx] = (int32_t)(ex_b + (uint32_t)s.rpre[k]);
-                    if (cp) cp[idx] = (int32_t)(r * S + (uint32_t)s.start[k]);
+                    cu_g[idx] = (int32_t)(ex_b + (uint32_t)s.rpre[k]);
+                    if (cp_g) cp_g[idx] = (int32_t)(rg * S + (uint32_t)s.start[k]);
                 }
                 __syncthreads();
                 if (one_batch || j0 + kBatch >= P) break;
@@ -302,14 +357,14 @@ __device__ __forceinline__ void thd_tables_body(
                 if (oob) err |= PSQ_DATA_WORKSPACE;
                 err |= s_wserr;
                 if (err) or_relaxed(&ws->status, err);
-                if (disagree) or_relaxed(&ws->flags, 1u);
-                if (s.max_real > 0) max_relaxed(&ws->max, s.max_real);
-                if (r == B - 1 && !oob) {
+                if (disagree) or_relaxed(&recs[g].flags, 1u);
+                if (s.max_real > 0) max_relaxed(&recs[g].max, s.max_real);
+                if (rg == Bc - 1 && !oob) {
                     const uint32_t n = ex_a + count;
                     const uint32_t total = ex_b + realsum;
-                    st_relaxed((uint32_t *)&ws->n, n);
-                    st_relaxed((uint32_t *)&ws->total, total);
-                    st_relaxed((uint32_t *)&ws->cu_last, total - (uint32_t)s.last_real);
+                    st_relaxed(&recs[g].n, n);
+                    st_relaxed(&recs[g].total, total);
+                    st_relaxed(&recs[g].cu_last, total - (uint32_t)s.last_real);
                 }
             }
         }
@@ -318,48 +373,99 @@ __device__ __forceinline__ void thd_tables_body(
     }
 
     if (finish_is_last(ws, n_groups, &s_slot)) {
-        if (threadIdx.x == 0) {
-            const uint32_t st = ld_relaxed(&ws->status);
-            const uint32_t n = ld_relaxed((const uint32_t *)&ws->n);
-            const uint32_t total = ld_relaxed((const uint32_t *)&ws->total);
-            const uint32_t cu_last = ld_relaxed((const uint32_t *)&ws->cu_last);
-            const bool disagree = ld_relaxed(&ws->flags) != 0;
-            int32_t mx = (int32_t)ld_relaxed((const uint32_t *)&ws->max);
-            if (st == 0 && (uint64_t)n <= (uint64_t)B * P) {
-                const bool absorbed = !disagree && (uint64_t)total < T;
-                cu[n] = (int32_t)(absorbed ? (uint32_t)T : total);
-                if (cp) cp[n] = (int32_t)T;
-                if (absorbed) mx = max(mx, (int32_t)((uint32_t)T - cu_last));
-                *num_seqs = (int32_t)n;
-                *max_seqlen = mx;
-                *pad_between = disagree ? 1 : 0;
+        __shared__ uint32_t s_width;
+        const uint32_t st = ld_relaxed(&ws->status);
+        if (threadIdx.x == 0) s_width = 0;
+        __syncthreads();
+        // finish every group: absorption, scalars, the closing boundaries
+        uint32_t width = 0;
+        for (uint32_t g = threadIdx.x; g < G; g += kThreads) {
+            const uint32_t n = ld_relaxed(&recs[g].n);
+            const uint32_t total = ld_relaxed(&recs[g].total);
+            const uint32_t cu_last = ld_relaxed(&recs[g].cu_last);
+            const bool disagree = ld_relaxed(&recs[g].flags) != 0;
+            int32_t mx = (int32_t)ld_relaxed((const uint32_t *)&recs[g].max);
+            if (st == 0 && (uint64_t)n <= (uint64_t)Bc * P) {
+                const bool absorbed = !disagree && total < Tc;
+                if (G == 1) {
+                    cu[n] = (int32_t)(absorbed ? Tc : total);
+                    if (cp) cp[n] = (int32_t)Tc;
+                }
+                if (absorbed) mx = max(mx, (int32_t)(Tc - cu_last));
+                args.num_seqs[g] = (int32_t)n;
+                args.max_seqlen[g] = mx;
+                args.pad_between[g] = disagree ? 1 : 0;
+                width = max(width, n + 1u);
             } else {
-                *num_seqs = 0;
-                *max_seqlen = 0;
-                *pad_between = 0;
+                args.num_seqs[g] = 0;
+                args.max_seqlen[g] = 0;
+                args.pad_between[g] = 0;
             }
-            *status = (int32_t)st;
-            st_relaxed(&ws->status, 0u);
-            st_relaxed(&ws->flags, 0u);
-            st_relaxed((uint32_t *)&ws->max, 0u);
-            st_relaxed((uint32_t *)&ws->n, 0u);
-            st_relaxed((uint32_t *)&ws->total, 0u);
-            st_relaxed((uint32_t *)&ws->cu_last, 0u);
-            st_relaxed(&ws->ticket, 0u);
+        }
+        if (width) atomicMax(&s_width, width);
+        __syncthreads();
+        width = st == 0 ? s_width : 0u;
+        if (threadIdx.x == 0) {
+            *args.status = (int32_t)st;
+            if (args.cu_width) *args.cu_width = (int32_t)width;
+        }
+        // G > 1: staged groups -> one [G, width] array, short rows filled
+        // with the sentinel.  Each staged entry is cleared once read (the
+        // workspace is zero again after every call); after a data error the
+        // whole staging area is cleared instead.
+        if (G > 1 && width > 0) {
+            const uint64_t total_out = (uint64_t)G * width;
+            const int32_t fill = (int32_t)pad_value;
+            for (uint64_t e = threadIdx.x; e < total_out; e += kThreads) {
+                const uint32_t g = (uint32_t)(e / width);
+                const uint32_t j = (uint32_t)(e - (uint64_t)g * width);
+                const uint32_t n = ld_relaxed(&recs[g].n);
+                int32_t vu = fill, vp = fill;
+                if (j < n) {
+                    const uint64_t at = (uint64_t)g * ld + j;
+                    vu = cu_st[at];
+                    cu_st[at] = 0;
+                    if (cp) {
+                        vp = cp_st[at];
+                        cp_st[at] = 0;
+                    }
+                } else if (j == n) {
+                    const uint32_t total = ld_relaxed(&recs[g].total);
+                    const bool disagree = ld_relaxed(&recs[g].flags) != 0;
+                    vu = (int32_t)((!disagree && total < Tc) ? Tc : total);
+                    vp = (int32_t)Tc;
+                }
+                cu[e] = vu;
+                if (cp) cp[e] = vp;
+            }
+        } else if (G > 1) {
+            const uint64_t staged = (uint64_t)G * ld;
+            for (uint64_t e = threadIdx.x; e < staged; e += kThreads) {
+                cu_st[e] = 0;
+                if (cp_st) cp_st[e] = 0;
+            }
+        }
+        __syncthreads();
+        for (uint32_t g = threadIdx.x; g < G; g += kThreads) {
+            st_relaxed(&recs[g].flags, 0u);
+            st_relaxed((uint32_t *)&recs[g].max, 0u);
+            st_relaxed(&recs[g].n, 0u);
+            st_relaxed(&recs[g].total, 0u);
+            st_relaxed(&recs[g].cu_last, 0u);
         }
         for (uint32_t i = threadIdx.x; i < B; i += kThreads) st_relaxed(desc + i, 0ull);
+        if (threadIdx.x == 0) {
+            st_relaxed(&ws->status, 0u);
+            st_relaxed(&ws->ticket, 0u);
+        }
         __syncthreads();
         if (threadIdx.x == 0) st_relaxed(&ws->done, 0u);
     }
 }
 
-#define PSQ_THD_ARGS(a)                                                                       \
-    a.L, a.Lp, a.B, a.P, a.S, a.pad_value, a.n_chunks, a.vec_mask, a.cu, a.cp, a.num_seqs,    \
-        a.max_seqlen, a.pad_between, a.mask, a.status, a.ws
-
 template <typename TL>
 __global__ __launch_bounds__(kThreads) void k_thd_tables(ThdArgs<TL> a) {
-    thd_tables_body<TL>(PSQ_THD_ARGS(a), gridDim.x);
+    thd_tables_body<TL>(a, gridDim.x);
 }
 
 // The same workgroups followed, in one grid, by the 16-byte dense copies of
@@ -368,11 +474,10 @@ template <typename TL>
 __global__ __launch_bounds__(kThreads) void k_thd_tables_copy(ThdArgs<TL> a, uint32_t n_meta,
                                                               CopyBatch batch) {
     if (blockIdx.x < n_meta)
-        thd_tables_body<TL>(PSQ_THD_ARGS(a), n_meta);
+        thd_tables_body<TL>(a, n_meta);
     else
         copy_group<u32x4, true>(batch, (int64_t)blockIdx.x - n_meta);
 }
-#undef PSQ_THD_ARGS
 
 template <typename TL>
 hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, int n_copies,
@@ -393,30 +498,40 @@ hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, 
 
 }  // namespace
 
-size_t thd_tables_workspace(int64_t B, int64_t /*S*/) {
-    return round_up(kWsDescOffset + 8 * (size_t)(B > 0 ? B : 1), 256);
+size_t thd_tables_workspace(int64_t B, int64_t P, int64_t G) {
+    const int64_t Bc = G > 0 ? B / G : 0;
+    return thd_ws_layout(B, G, Bc * P + 1).bytes;
 }
 
 hipError_t launch_thd_tables(const void *L, const void *Lp, int lens_dtype, int64_t B,
-                             int64_t P, int64_t S, int64_t pad_value, int32_t *cu,
+                             int64_t P, int64_t S, int64_t G, int64_t pad_value, int32_t *cu,
                              int32_t *cp, int32_t *num_seqs, int32_t *max_seqlen,
-                             int32_t *pad_between, uint8_t *mask, int32_t *status,
-                             void *workspace, const psq_copy *copies, int n_copies,
-                             hipStream_t stream) {
+                             int32_t *pad_between, int32_t *cu_width, uint8_t *mask,
+                             int32_t *status, void *workspace, const psq_copy *copies,
+                             int n_copies, hipStream_t stream) {
     const uint32_t n_chunks = S > 0 ? (uint32_t)((S + kSlots - 1) / kSlots) : 1u;
     const uint64_t groups = (uint64_t)B * n_chunks;
     const uint32_t n_meta = (uint32_t)(groups > 0 ? groups : 1);
     const int vec_mask = ((uintptr_t)mask % 16) == 0;
+    const int64_t Bc = B / G;
+    const int64_t ld = Bc * P + 1;
+    const ThdWsLayout lay = thd_ws_layout(B, G, ld);
+    char *wsb = (char *)workspace;
+    int32_t *cu_st = G > 1 ? (int32_t *)(wsb + lay.stage_cu) : cu;
+    int32_t *cp_st = G > 1 ? (cp ? (int32_t *)(wsb + lay.stage_cp) : nullptr) : cp;
+    GroupRec *recs = (GroupRec *)(wsb + lay.recs);
     WsHeader *ws = (WsHeader *)workspace;
     if (lens_dtype == PSQ_I64) {
         ThdArgs<int64_t> a{(const int64_t *)L, (const int64_t *)Lp, (uint32_t)B, (uint32_t)P,
-                           (uint32_t)S, pad_value, n_chunks, vec_mask, cu, cp, num_seqs,
-                           max_seqlen, pad_between, mask, status, ws};
+                           (uint32_t)S, pad_value, n_chunks, vec_mask, (uint32_t)G,
+                           (uint32_t)Bc, (uint32_t)ld, cu, cp, num_seqs, max_seqlen,
+                           pad_between, cu_width, cu_st, cp_st, recs, mask, status, ws};
         return launch_typed(a, n_meta, copies, n_copies, stream);
     }
     ThdArgs<int32_t> a{(const int32_t *)L, (const int32_t *)Lp, (uint32_t)B, (uint32_t)P,
-                       (uint32_t)S, pad_value, n_chunks, vec_mask, cu, cp, num_seqs,
-                       max_seqlen, pad_between, mask, status, ws};
+                       (uint32_t)S, pad_value, n_chunks, vec_mask, (uint32_t)G, (uint32_t)Bc,
+                       (uint32_t)ld, cu, cp, num_seqs, max_seqlen, pad_between, cu_width,
+                       cu_st, cp_st, recs, mask, status, ws};
     return launch_typed(a, n_meta, copies, n_copies, stream);
 }
 

@@ -26,9 +26,13 @@ int check_copies(const psq_copy *copies, int n_copies) {
         if (c.rows == 0 || c.row_bytes == 0) continue;
         if (c.src == nullptr || c.dst == nullptr) return PSQ_ERR_ARG;
         if (c.rows > 1 && c.src_row_stride_bytes < c.row_bytes) return PSQ_ERR_ARG;
-        const int64_t dst_bytes = c.rows * c.row_bytes;
+        if (c.dst_row_stride_bytes < 0 ||
+            (c.rows > 1 && c.dst_row_stride_bytes != 0 && c.dst_row_stride_bytes < c.row_bytes))
+            return PSQ_ERR_ARG;
+        const int64_t dst_stride = c.dst_row_stride_bytes ? c.dst_row_stride_bytes : c.row_bytes;
+        const int64_t dst_span = (c.rows - 1) * dst_stride + c.row_bytes;
         const int64_t src_span = (c.rows - 1) * c.src_row_stride_bytes + c.row_bytes;
-        if (overlaps(c.src, src_span, c.dst, dst_bytes)) return PSQ_ERR_ARG;
+        if (overlaps(c.src, src_span, c.dst, dst_span)) return PSQ_ERR_ARG;
     }
     return PSQ_OK;
 }
@@ -60,6 +64,8 @@ const char *psq_status_string(int code, int is_status) {
     if (code & PSQ_DATA_EMPTY_PACK) return "a pack has no member";
     if (code & PSQ_DATA_BAD_INDEX) return "member, pack or source index out of range";
     if (code & PSQ_DATA_WORKSPACE) return "workspace was not zero-filled before use";
+    if (code & PSQ_DATA_PAD_IS_CONTENT)
+        return "padding_token_id also occurs as content (pad slots are not a right-padded tail)";
     return "unknown status bits";
 }
 
@@ -93,7 +99,7 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
 size_t psq_process_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S) {
     if (layout == nullptr || B < 0 || S < 0) return 0;
     if (layout->kind == PSQ_LAYOUT_DOC_IDS) return psq::doc_segments_workspace(B, S);
-    return psq::thd_tables_workspace(B, S);
+    return psq::thd_tables_workspace(B, layout->P > 0 ? layout->P : 0, 1);
 }
 
 int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t *cu_seqlens,
@@ -125,14 +131,71 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t 
     if (!valid_dtype(layout->lens_dtype) || layout->P < 0) return PSQ_ERR_ARG;
     if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
     if (layout->P > 0 && B > (kI32Limit - 2) / layout->P) return PSQ_ERR_OVERFLOW;
-    if (workspace == nullptr || workspace_bytes < psq::thd_tables_workspace(B, S))
+    if (workspace == nullptr || workspace_bytes < psq::thd_tables_workspace(B, layout->P, 1))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
-                                           layout->lens_dtype, B, layout->P, S,
+                                           layout->lens_dtype, B, layout->P, S, 1,
                                            layout->pad_value, cu_seqlens, cu_seqlens_padded,
-                                           num_seqs, max_seqlen, pad_between_seqs,
+                                           num_seqs, max_seqlen, pad_between_seqs, nullptr,
                                            padding_mask, status, workspace, copies, n_copies,
                                            st));
+}
+
+size_t psq_split_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S,
+                               int64_t num_chunks) {
+    if (layout == nullptr || B < 0 || S < 0 || num_chunks < 1 || B % num_chunks != 0 ||
+        layout->kind != PSQ_LAYOUT_SEQ_LENS || layout->P < 0)
+        return 0;
+    if (layout->P > 0 && B > (kI32Limit - 2) / layout->P) return 0;
+    return psq::thd_tables_workspace(B, layout->P, num_chunks);
+}
+
+int psq_split_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int64_t num_chunks,
+                  int32_t *cu_seqlens, int32_t *cu_seqlens_padded, int32_t *cu_width,
+                  int32_t *num_seqs, int32_t *max_seqlen, int32_t *pad_between_seqs,
+                  uint8_t *padding_mask, const psq_copy *copies, int n_copies,
+                  int32_t *status, void *workspace, size_t workspace_bytes, void *stream) {
+    if (layout == nullptr || B < 0 || S < 0) return PSQ_ERR_ARG;
+    if (num_chunks < 1 || B % num_chunks != 0) return PSQ_ERR_ARG;
+    if (layout->kind != PSQ_LAYOUT_SEQ_LENS) return PSQ_ERR_ARG;
+    if (S > 0 && B > (kI32Limit - 1) / S) return PSQ_ERR_OVERFLOW;
+    if (cu_seqlens == nullptr || cu_width == nullptr || num_seqs == nullptr ||
+        max_seqlen == nullptr || pad_between_seqs == nullptr || status == nullptr)
+        return PSQ_ERR_ARG;
+    const int cc = check_copies(copies, n_copies);
+    if (cc != PSQ_OK) return cc;
+    if (!valid_dtype(layout->lens_dtype) || layout->P < 0) return PSQ_ERR_ARG;
+    if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
+    // every staged / stacked boundary array holds at most B*P + num_chunks entries
+    if (layout->P > 0 && B > (kI32Limit - 2 - num_chunks) / layout->P) return PSQ_ERR_OVERFLOW;
+    if (workspace == nullptr ||
+        workspace_bytes < psq::thd_tables_workspace(B, layout->P, num_chunks))
+        return PSQ_ERR_WORKSPACE;
+    return from_hip(psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
+                                           layout->lens_dtype, B, layout->P, S, num_chunks,
+                                           layout->pad_value, cu_seqlens, cu_seqlens_padded,
+                                           num_seqs, max_seqlen, pad_between_seqs, cu_width,
+                                           padding_mask, status, workspace, copies, n_copies,
+                                           (hipStream_t)stream));
+}
+
+size_t psq_padding_mask_from_token_ids_workspace(int64_t T) {
+    (void)T;
+    return psq::pad_ids_workspace();
+}
+
+int psq_padding_mask_from_token_ids(const void *input_ids, int ids_dtype, int64_t T,
+                                    int64_t pad_id, uint8_t *padding_mask,
+                                    int32_t *num_content, int32_t *status, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (T < 0 || !valid_dtype(ids_dtype)) return PSQ_ERR_ARG;
+    if (T >= kI32Limit) return PSQ_ERR_OVERFLOW;
+    if (status == nullptr) return PSQ_ERR_ARG;
+    if (T > 0 && (input_ids == nullptr || padding_mask == nullptr)) return PSQ_ERR_ARG;
+    if (workspace == nullptr || workspace_bytes < psq::pad_ids_workspace())
+        return PSQ_ERR_WORKSPACE;
+    return from_hip(psq::launch_pad_ids(input_ids, ids_dtype, T, pad_id, padding_mask,
+                                        num_content, status, workspace, (hipStream_t)stream));
 }
 
 size_t psq_pack_rows_workspace(int64_t N, int64_t P, int32_t capacity) {
@@ -159,11 +222,35 @@ int psq_pack_rows(const int64_t *src_tokens, int64_t src_len, const int64_t *src
     if (src_len > 0 && src_tokens == nullptr) return PSQ_ERR_ARG;
     if (workspace == nullptr || workspace_bytes < psq::pack_rows_workspace())
         return PSQ_ERR_WORKSPACE;
-    return from_hip(psq::launch_pack_rows(src_tokens, src_len, src_offsets, real_len, N,
+    return from_hip(psq::launch_pack_rows(src_tokens, src_len, src_offsets, 0, real_len, N,
                                           pad_to, pack_order, pack_start, P, capacity, fold,
                                           pad_token, packed, token_mask, cu_seqlens,
                                           cu_seqlens_padded, status, workspace,
                                           (hipStream_t)stream));
+}
+
+int psq_pack_padded_rows(const int64_t *rows, int64_t W, const int32_t *real_len, int64_t N,
+                         int32_t pad_to, const int32_t *pack_order, const int64_t *pack_start,
+                         int64_t P, int32_t capacity, int fold, int64_t pad_token,
+                         int64_t *packed, uint8_t *token_mask, int32_t *cu_seqlens,
+                         int32_t *cu_seqlens_padded, int32_t *status, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (N < 0 || P < 0 || W < 0 || pad_to < 1 || capacity < 1) return PSQ_ERR_ARG;
+    if (capacity > (1 << 30)) return PSQ_ERR_ARG;
+    if (N + P >= kI32Limit) return PSQ_ERR_OVERFLOW;
+    if (W > 0 && N > ((int64_t)1 << 62) / W) return PSQ_ERR_OVERFLOW;
+    if (pack_start == nullptr || status == nullptr) return PSQ_ERR_ARG;
+    if (P > 0 && (packed == nullptr || token_mask == nullptr || cu_seqlens == nullptr ||
+                  cu_seqlens_padded == nullptr))
+        return PSQ_ERR_ARG;
+    if (N > 0 && real_len == nullptr) return PSQ_ERR_ARG;
+    if (N * W > 0 && rows == nullptr) return PSQ_ERR_ARG;
+    if (workspace == nullptr || workspace_bytes < psq::pack_rows_workspace())
+        return PSQ_ERR_WORKSPACE;
+    return from_hip(psq::launch_pack_rows(rows, N * W, nullptr, W, real_len, N, pad_to,
+                                          pack_order, pack_start, P, capacity, fold, pad_token,
+                                          packed, token_mask, cu_seqlens, cu_seqlens_padded,
+                                          status, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

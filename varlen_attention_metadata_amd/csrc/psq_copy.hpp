@@ -8,7 +8,7 @@
 // THD buffer.
 //
 // Each copy is cut into units of g bytes, g the largest of 16/8/4/1 dividing
-// both addresses, the row length and the source stride.  A workgroup moves
+// both addresses, the row length and both row strides.  A workgroup moves
 // 256 threads x 1 unit (4 KiB at g = 16): on MI355X many short workgroups
 // streamed faster than fewer long ones with several loads in flight per
 // thread (8 GiB copies: 6.4 TB/s at 4 KiB per workgroup, 5.5 TB/s at 16 KiB,
@@ -30,10 +30,11 @@ struct CopyJob {
     uint8_t *dst;
     int64_t units;           // total units of this copy
     int64_t units_per_row;   // units in one row
-    int64_t src_stride;      // bytes between source rows (== row bytes: dense)
+    int64_t src_stride;      // bytes between source rows
+    int64_t dst_stride;      // bytes between destination rows
     int64_t group_begin;     // first workgroup of this copy
     int32_t shift;           // log2 of the unit size
-    int32_t dense;           // 1: rows are back to back in the source
+    int32_t dense;           // 1: rows are back to back on both sides
 };
 
 struct CopyBatch {
@@ -58,15 +59,18 @@ __device__ __forceinline__ void copy_units(const CopyJob &jb, int64_t u0) {
     // ragged tail or strided rows: one unit at a time (kept register-light,
     // since a kernel's register budget is the maximum over all its paths)
     const int64_t stride_units = jb.src_stride >> jb.shift;
+    const int64_t dst_stride_units = jb.dst_stride >> jb.shift;
     for (int k = 0; k < kCopyUnroll; ++k) {
         const int64_t u = u0 + (int64_t)k * kCopyThreads + threadIdx.x;
         if (u >= jb.units) break;
-        int64_t at = u;
+        int64_t at = u, to = u;
         if (!kDense) {
             const int64_t row = u / jb.units_per_row;
-            at = row * stride_units + (u - row * jb.units_per_row);
+            const int64_t col = u - row * jb.units_per_row;
+            at = row * stride_units + col;
+            to = row * dst_stride_units + col;
         }
-        d[u] = __builtin_nontemporal_load(s + at);
+        d[to] = __builtin_nontemporal_load(s + at);
     }
 }
 
@@ -89,10 +93,17 @@ struct CopyPlan {
     int dense[8];
 };
 
+// Destination row stride of a copy (0 in the struct means dense rows).
+inline int64_t copy_dst_stride(const psq_copy &c) {
+    return c.dst_row_stride_bytes != 0 ? c.dst_row_stride_bytes : c.row_bytes;
+}
+
 inline int copy_unit_shift(const psq_copy &c) {
     const uint64_t bits = (uint64_t)(uintptr_t)c.src | (uint64_t)(uintptr_t)c.dst |
                           (uint64_t)c.row_bytes |
-                          (c.rows > 1 ? (uint64_t)c.src_row_stride_bytes : 0ull);
+                          (c.rows > 1 ? (uint64_t)c.src_row_stride_bytes |
+                                            (uint64_t)copy_dst_stride(c)
+                                      : 0ull);
     if ((bits & 15) == 0) return 4;
     if ((bits & 7) == 0) return 3;
     if ((bits & 3) == 0) return 2;
@@ -112,7 +123,10 @@ inline void plan_copies(const psq_copy *copies, int n_copies, CopyPlan *plan) {
             const int64_t bytes = c.rows * c.row_bytes;
             if (bytes == 0) continue;
             const int shift = copy_unit_shift(c);
-            const int dense = (c.rows <= 1 || c.src_row_stride_bytes == c.row_bytes) ? 1 : 0;
+            const int dense = (c.rows <= 1 || (c.src_row_stride_bytes == c.row_bytes &&
+                                               copy_dst_stride(c) == c.row_bytes))
+                                  ? 1
+                                  : 0;
             if (shift != want_shift || dense != want_dense) continue;
             CopyJob &jb = batch.job[n++];
             jb.shift = shift;
@@ -121,6 +135,7 @@ inline void plan_copies(const psq_copy *copies, int n_copies, CopyPlan *plan) {
             jb.units = bytes >> shift;
             jb.units_per_row = c.row_bytes >> shift;
             jb.src_stride = c.src_row_stride_bytes;
+            jb.dst_stride = copy_dst_stride(c);
             jb.dense = dense;
             jb.group_begin = groups;
             groups += (jb.units + kCopyUnitsPerGroup - 1) / kCopyUnitsPerGroup;

@@ -18,14 +18,15 @@ hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_
                                int32_t *pad_between, void *workspace, const psq_copy *copies,
                                int n_copies, hipStream_t stream);
 
-// k_thd.hip -- length tables -> THD metadata and layout mask (+ fused copies).
-size_t thd_tables_workspace(int64_t B, int64_t S);
+// k_thd.hip -- length tables -> THD metadata and layout mask (+ fused copies),
+// for G equal row groups (G == 1: one process_input_for_thd call).
+size_t thd_tables_workspace(int64_t B, int64_t P, int64_t G);
 hipError_t launch_thd_tables(const void *L, const void *Lp, int lens_dtype, int64_t B,
-                             int64_t P, int64_t S, int64_t pad_value, int32_t *cu,
+                             int64_t P, int64_t S, int64_t G, int64_t pad_value, int32_t *cu,
                              int32_t *cp, int32_t *num_seqs, int32_t *max_seqlen,
-                             int32_t *pad_between, uint8_t *mask, int32_t *status,
-                             void *workspace, const psq_copy *copies, int n_copies,
-                             hipStream_t stream);
+                             int32_t *pad_between, int32_t *cu_width, uint8_t *mask,
+                             int32_t *status, void *workspace, const psq_copy *copies,
+                             int n_copies, hipStream_t stream);
 
 // k_copy.hip -- batched byte copies (the BSHD -> THD collapse).
 hipError_t launch_copies(const psq_copy *copies, int n_copies, hipStream_t stream);
@@ -34,11 +35,17 @@ hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 // k_pack.hip -- the squeeze into fixed-capacity packs.
 size_t pack_rows_workspace();
 hipError_t launch_pack_rows(const int64_t *src, int64_t src_len, const int64_t *src_off,
-                            const int32_t *real_len, int64_t N, int32_t q,
+                            int64_t src_stride, const int32_t *real_len, int64_t N, int32_t q,
                             const int32_t *order, const int64_t *pack_start, int64_t P,
                             int32_t C, int fold, int64_t pad_token, int64_t *packed,
                             uint8_t *tmask, int32_t *cu, int32_t *cp, int32_t *status,
                             void *workspace, hipStream_t stream);
+
+// k_padids.hip -- the metadata-free padding mask from token ids.
+size_t pad_ids_workspace();
+hipError_t launch_pad_ids(const void *ids, int ids_dtype, int64_t T, int64_t pad,
+                          uint8_t *mask, int32_t *num_content, int32_t *status,
+                          void *workspace, hipStream_t stream);
 
 inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
