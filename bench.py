@@ -9,7 +9,10 @@ max_seqlen and the padding mask -- one fused kernel launch.  Inputs are
 resident in HBM before timing starts.  The other four workloads are timed
 too and reported under ``per_config`` (the document maps [4, 64] and
 [8, 4096], the length tables with 3 collapsed int64 tensors, and the
-squeeze of 65536 sources into 16384-slot packs).
+squeeze of 65536 sources into 16384-slot packs), and so are the steps around
+them: the length tables split into 4 row groups, the metadata-free padding
+mask of a 131072-id stream, and the trainer's squeeze of a 256-row padded
+rectangle into token-budget bins.
 
 Prints one JSON line.  ``roofline`` relates the algorithmic bytes of one
 launch (each input read once, each output written once) to the launch's
@@ -65,7 +68,9 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
             if "psq::" not in name:
                 continue
             short = name.split("(")[0].replace("void ", "")
-            key = "calibration_copy_1GiB" if r["Grid_Size"] == calib_grid else short
+            # one kernel can serve several workloads: the grid tells them apart
+            key = ("calibration_copy_1GiB" if r["Grid_Size"] == calib_grid
+                   else f"{short} [grid {r['Grid_Size']}]")
             per.setdefault(key, []).append(float(r["Counter_Value"]))
         return {k: statistics.median(v) for k, v in per.items()}
 
@@ -260,6 +265,105 @@ def setup_pack(torch, psq, lib, synth, dev):
     return call, P * C, algo, info, (src, off, rl, ps, packed, tm, cu, cp, st, ws)
 
 
+def setup_split(torch, psq, lib, synth, dev, G=4):
+    """Workload 3 through split_batch_into_thd_chunks with G row groups."""
+    w = synth.thd_tables()
+    S = w["S"]
+    B, P = w["seq_lens"].shape
+    T = B * S
+    t = {k: torch.from_numpy(w[k]).to(dev) for k in
+         ("input_ids", "labels", "position_ids", "seq_lens", "seq_lens_padded")}
+    outs = {k: torch.empty(T, dtype=torch.int64, device=dev) for k in ("input_ids", "labels", "position_ids")}
+    cap = G * (B // G * P + 1)
+    cu = torch.empty(cap, dtype=torch.int32, device=dev)
+    cp = torch.empty(cap, dtype=torch.int32, device=dev)
+    mask = torch.empty(T, dtype=torch.bool, device=dev)
+    per = torch.zeros((3, G), dtype=torch.int32, device=dev)
+    scal = torch.zeros(2, dtype=torch.int32, device=dev)
+    layout = lib.make_layout(lib.LAYOUT_SEQ_LENS, t["seq_lens"].data_ptr(),
+                             t["seq_lens_padded"].data_ptr(), lib.I64, P, -1000)
+    copies, n_c = lib.make_copies([(t[k].data_ptr(), outs[k].data_ptr(), 1, T * 8, T * 8)
+                                   for k in ("input_ids", "labels", "position_ids")])
+    ws = psq.workspace_for(dev, lib.psq_split_thd_workspace(layout, B, S, G))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pp, sp = per.data_ptr(), scal.data_ptr()
+
+    def call():
+        lib.psq_split_thd(layout, B, S, G, cu.data_ptr(), cp.data_ptr(), sp, pp, pp + 4 * G,
+                          pp + 8 * G, mask.data_ptr(), copies, n_c, sp + 4, ws.data_ptr(),
+                          ws.numel(), stream)
+
+    call()
+    width, st = scal.cpu().tolist()
+    assert st == 0, st
+    algo = 16 * B * P + 48 * T + T + 8 * G * width + 12 * G + 8
+    info = {"workload": f"thd_tables split into {G} row groups", "B": B, "S": S, "P": P,
+            "num_chunks": G, "cu_width": width}
+    return call, T, algo, info, (t, outs, cu, cp, mask, per, scal, ws)
+
+
+def setup_padids(torch, psq, lib, synth, dev):
+    """The metadata-free padding mask of a 131072-id stream with a pad tail."""
+    w = synth.pad_tail_stream()
+    ids = torch.from_numpy(w["input_ids"]).to(dev)
+    T = ids.numel()
+    mask = torch.empty(T, dtype=torch.bool, device=dev)
+    scal = torch.zeros(2, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, lib.psq_padding_mask_from_token_ids_workspace(T))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    sp = scal.data_ptr()
+
+    def call():
+        lib.psq_padding_mask_from_token_ids(ids.data_ptr(), lib.I64, T, w["pad_id"],
+                                            mask.data_ptr(), sp, sp + 4, ws.data_ptr(),
+                                            ws.numel(), stream)
+
+    call()
+    nc, st = scal.cpu().tolist()
+    assert st == 0 and nc == T - w["tail"], (nc, st)
+    algo = 8 * T + T + 8
+    info = {"workload": "pad_tail_stream", "T": T, "tail": w["tail"]}
+    return call, T, algo, info, (ids, mask, scal, ws)
+
+
+def setup_rect(torch, psq, lib, synth, dev):
+    """Trainer packs: a 256-row padded rectangle squeezed into token-budget bins."""
+    w = synth.trainer_rectangle()
+    rows_np, rl_np, bins, q = w["rows"], w["real_len"], w["bins"], w["q"]
+    N, W = rows_np.shape
+    P = len(bins)
+    C = max(sum(-(-int(rl_np[i]) // q) * q for i in b) for b in bins)
+    members = [i for b in bins for i in b]
+    order = torch.zeros(N, dtype=torch.int32)
+    order[: len(members)] = torch.tensor(members, dtype=torch.int32)
+    starts = torch.zeros(P + 1, dtype=torch.int64)
+    starts[1:] = torch.tensor([len(b) for b in bins]).cumsum(0)
+    rows = torch.from_numpy(rows_np).to(dev)
+    rl = torch.from_numpy(rl_np).to(dev)
+    order, starts = order.to(dev), starts.to(dev)
+    packed = torch.empty((P, C), dtype=torch.int64, device=dev)
+    tm = torch.empty((P, C), dtype=torch.uint8, device=dev)
+    cu = torch.empty(N + P, dtype=torch.int32, device=dev)
+    cp = torch.empty(N + P, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, lib.psq_pack_rows_workspace(N, P, C))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        lib.psq_pack_padded_rows(rows.data_ptr(), W, rl.data_ptr(), N, q, order.data_ptr(),
+                                 starts.data_ptr(), P, C, 0, 0, packed.data_ptr(), tm.data_ptr(),
+                                 cu.data_ptr(), cp.data_ptr(), st.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), stream)
+
+    call()
+    assert int(st.item()) == 0
+    real = int(rl_np.sum())
+    algo = 8 * real + 4 * N + 4 * N + 8 * (P + 1) + 9 * P * C + 8 * (N + P) + 4
+    info = {"workload": "trainer_rectangle", "N": N, "W": W, "bins": P, "width": C,
+            "pad_to": q, "real_tokens": real}
+    return call, P * C, algo, info, (rows, rl, order, starts, packed, tm, cu, cp, st, ws)
+
+
 def measure(torch, call, iters, flush=None):
     timer = Timer(torch)
     for _ in range(iters):
@@ -298,7 +402,10 @@ def profile_launches(torch, psq, lib, synth, dev, n):
     for name, setup in (("stage_embedding", lambda: setup_stage_embedding(torch, psq, lib, synth, dev)),
                         ("pack_sources", lambda: setup_pack(torch, psq, lib, synth, dev)),
                         ("thd_tables", lambda: setup_thd(torch, psq, lib, synth, dev)),
-                        ("doc_map_medium", lambda: setup_doc_map(torch, psq, lib, synth, dev, 2))):
+                        ("doc_map_medium", lambda: setup_doc_map(torch, psq, lib, synth, dev, 2)),
+                        ("thd_split_4", lambda: setup_split(torch, psq, lib, synth, dev)),
+                        ("pad_tail_stream", lambda: setup_padids(torch, psq, lib, synth, dev)),
+                        ("trainer_rectangle", lambda: setup_rect(torch, psq, lib, synth, dev))):
         runs.append((name, (lambda st: (lambda: st()[::4]))(setup)))
     for name, setup in runs:
         call, keep = setup()
@@ -347,27 +454,56 @@ def cpu_baseline(torch, keep):
 WORKLOAD_OF = {
     "k_doc_segments_copy": "stage_embedding: doc map [32,32768] + bf16 [32,32768,4096] collapse "
                            "(and the 1 GiB calibration copy when present)",
-    "k_pack_rows": "pack_sources: 65536 sources -> 16384-slot packs",
-    "k_thd_tables_copy": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses",
+    "k_pack_rows": "pack_sources: 65536 sources -> 16384-slot packs; trainer_rectangle: "
+                   "256 rows -> token-budget bins",
+    "k_thd_tables_copy": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses "
+                         "(whole batch, and split into 4 row groups)",
     "k_doc_segments": "doc_map_small [4,64] and doc_map_medium [8,4096]",
+    "k_pad_ids": "pad_tail_stream: 131072 int64 ids with a pad tail",
     "k_zero_fill": "workspace zero fill (once per workspace)",
 }
 
 
+# (kernel, grid size in threads) -> workload, for kernels that serve several
+GRID_LABEL = {
+    ("k_pack_rows", "3590144"): "pack_sources: 65536 sources -> 3506 packs of 16384 slots",
+    ("k_pack_rows", "15360"): "trainer_rectangle: 256 rows -> 15 token-budget bins",
+    ("k_doc_segments", "256"): "doc_map_small [4,64]",
+    ("k_doc_segments", "2048"): "doc_map_medium [8,4096]",
+}
+
+
 def summarize_trace(stats_csv: str, out_md: str, command: str) -> None:
-    """Markdown summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run: the
+    kernel_stats.csv totals, split per launch grid with the sibling
+    kernel_trace.csv (one kernel can serve several workloads)."""
     import csv
-    rows = [r for r in csv.DictReader(open(stats_csv)) if "psq::" in r["Name"]]
+    import statistics
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
     lines = ["# Kernel trace: " + os.path.basename(out_md)[:-3], "",
              "Command (GPU box, repository root):", "", "```", command, "```", "",
-             "| kernel | workload | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+             "| kernel | grid (threads) | workload | calls | avg us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        if "psq::" not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "")
         short = name.split("(")[0]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault((short, r["Grid_Size_X"]), []).append(dur)
+    for (short, grid), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         base = short.split("<")[0].replace("psq::", "")
-        lines.append(f"| `{short}` | {WORKLOAD_OF.get(base, '')} | {r['Calls']} | "
-                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
-                     f"{float(r['MaxNs']) / 1e3:.1f} |")
+        label = GRID_LABEL.get((base, grid), WORKLOAD_OF.get(base, ""))
+        lines.append(f"| `{short}` | {grid} | {label} | {len(v)} | {statistics.mean(v):.1f} | "
+                     f"{min(v):.1f} | {max(v):.1f} |")
+    lines += ["", "Per-kernel totals from kernel_stats.csv:", "",
+              "| kernel | calls | avg us |", "|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        if "psq::" in r["Name"]:
+            short = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+            lines.append(f"| `{short.split('(')[0]}` | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.1f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -457,7 +593,10 @@ def main():
                 ("doc_map_small", lambda: setup_doc_map(torch, psq, lib, synth, dev, 1), False),
                 ("doc_map_medium", lambda: setup_doc_map(torch, psq, lib, synth, dev, 2), False),
                 ("thd_tables", lambda: setup_thd(torch, psq, lib, synth, dev), False),
-                ("pack_sources", lambda: setup_pack(torch, psq, lib, synth, dev), True)):
+                ("pack_sources", lambda: setup_pack(torch, psq, lib, synth, dev), True),
+                ("thd_split_4", lambda: setup_split(torch, psq, lib, synth, dev), False),
+                ("pad_tail_stream", lambda: setup_padids(torch, psq, lib, synth, dev), False),
+                ("trainer_rectangle", lambda: setup_rect(torch, psq, lib, synth, dev), True)):
             c_call, c_tok, c_algo, c_info, c_keep = setup()
             for _ in range(5):
                 c_call()
