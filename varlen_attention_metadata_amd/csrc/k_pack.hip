@@ -8,17 +8,24 @@
 // counts, and the last padded boundary is set to the capacity
 // (cu_seqlens_padded [0,8,36]).
 //
-// Work layout: one 256-thread workgroup per (pack, chunk of 4096 slots).
-// The workgroup scans its pack's member lengths into LDS (256 members per
-// batch; a saturating scan so an overfull pack is detected exactly), marks
-// each member's start slot in a per-chunk owner map and fills the map with
-// one block-wide max scan, so every slot finds its member with one LDS read
-// and takes either the member's token or the pad token.  Token-mask bytes
-// are staged in LDS and leave as 16-byte stores.  Stores are plain (not
-// non-temporal): on gfx950 the non-temporal form measured slower here.  The
-// chunk-0 workgroup of each pack also writes the pack's boundary arrays and
-// reports data errors through one relaxed 64-bit word (finished count |
-// status bits); the last of those to finish publishes *status.
+// Work layout: one single-wave workgroup (64 threads) per (pack, chunk of
+// 1024 slots).  The wave scans its pack's member lengths into LDS (64
+// members per batch; a saturating scan so an overfull pack is detected
+// exactly), marks each member's start slot in a per-chunk owner map and
+// fills the map with one max scan, so every slot finds its member with one
+// LDS read and takes either the member's token or the pad token.  Lane l
+// owns slots l, l+64, l+128, ... of the chunk, so every load and store
+// instruction of the wave covers 64 consecutive slots.  Every slot issues
+// its load (a pad slot re-reads a token of its own member, which is already
+// in flight), so the loads are straight-line code and the stores wait only
+// for the loads they need.  On MI355X this shape beat 256-thread workgroups
+// over 4096 slots by 4 %: a one-wave workgroup synchronizes cheaply, and more
+// of them stay resident.  Token-mask bytes are staged in LDS and leave as
+// 16-byte stores.  Stores are plain (not non-temporal): on gfx950 the
+// non-temporal form measured slower here.  The chunk-0 workgroup of each
+// pack also writes the pack's boundary arrays and reports data errors
+// through one relaxed 64-bit word (finished count | status bits); the last
+// of those to finish publishes *status.
 // Every access is bounds-checked against the caller's sizes, so bad data
 // can only produce wrong values and status bits, never a stray access.
 //
@@ -31,13 +38,14 @@
 namespace psq {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMembers = kThreads;       // members per LDS batch
-constexpr uint32_t kSlots = 4096;        // slots per workgroup
-constexpr int kPairs = 8;                // slot pairs per thread: one round per chunk
+constexpr uint32_t kSlots = 1024;        // slots per workgroup
+constexpr int kPerThread = 16;           // slots per thread: one round per chunk
 constexpr int kOwnWords = kSlots / kThreads / 2;   // owner-map words per thread
 static_assert(kSlots % (kThreads * 8) == 0, "chunk must cover whole 16-byte LDS stores");
+static_assert(kSlots == (uint32_t)kThreads * kPerThread, "one round covers the chunk");
 
 __device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat) {
     const uint32_t s = a + b;
@@ -55,14 +63,14 @@ __device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
     return x;
 }
 
-__global__ __launch_bounds__(kThreads) void k_pack_rows(
+// At most 128 VGPRs (4 waves per SIMD): the register budget it was tuned at.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_pack_rows(
     const int64_t *__restrict__ src, int64_t src_len, const int64_t *__restrict__ src_off,
     int64_t src_stride, const int32_t *__restrict__ real_len, int64_t N, int32_t q,
     const int32_t *__restrict__ order, const int64_t *__restrict__ pack_start, int64_t P,
     int32_t C, int fold, int64_t pad_token, int64_t *__restrict__ packed,
     uint8_t *__restrict__ tmask, int32_t *__restrict__ cu, int32_t *__restrict__ cp,
-    int32_t *__restrict__ status, WsHeader *__restrict__ ws, uint32_t n_chunks, int vec_out,
-    int vec_mask) {
+    int32_t *__restrict__ status, WsHeader *__restrict__ ws, uint32_t n_chunks, int vec_mask) {
     __shared__ uint32_t m_start[kMembers];
     __shared__ uint32_t m_real[kMembers];
     __shared__ int64_t m_so[kMembers];
@@ -85,6 +93,9 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
 
     const int64_t a = pack_start[p];
     const int64_t b = pack_start[p + 1];
+    // every slot loads from here; without any source tokens the loads go to
+    // pack_start (never empty) and are discarded
+    const int64_t *__restrict__ srcp = src_len > 0 ? src : pack_start;
     const bool range_ok = a >= 0 && b <= N && a <= b;
     const int64_t k = range_ok ? b - a : 0;
     if (threadIdx.x == 0) s_err = range_ok ? (k == 0 ? PSQ_DATA_EMPTY_PACK : 0u) : PSQ_DATA_BAD_INDEX;
@@ -208,51 +219,35 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
             }
             __syncthreads();
 
-            const uint32_t base = r_lo & ~1u;
-            for (uint32_t u0 = base + 2u * threadIdx.x; u0 < r_hi; u0 += 2u * kThreads * kPairs) {
-                int64_t val[kPairs][2];
-                bool in[kPairs][2];
+            for (uint32_t ub = r_lo; ub < r_hi; ub += kSlots) {
+                int64_t val[kPerThread];
+                bool in[kPerThread];
 #pragma unroll
-                for (int t = 0; t < kPairs; ++t) {
-                    const uint32_t u = u0 + 2u * kThreads * (uint32_t)t;
-                    const uint32_t own = (u < hi) ? *(const uint32_t *)(s_own + (u - lo)) : 0u;
-                    bool tok[2];
-                    int64_t idx[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const uint32_t s = u + (uint32_t)e;
-                        const uint32_t o1 = (own >> (16 * e)) & 0xffffu;
-                        in[t][e] = s >= r_lo && s < r_hi;
-                        tok[e] = false;
-                        idx[e] = 0;
-                        val[t][e] = pad_token;
-                        if (in[t][e] && o1 != 0u) {     // o1 >= 1 for every slot in range
-                            const uint32_t x = o1 - 1u;
-                            const uint32_t off = s - m_start[x];
-                            tok[e] = off < m_real[x];
-                            idx[e] = m_so[x] + off;
-                        }
+                for (int t = 0; t < kPerThread; ++t) {
+                    const uint32_t s = ub + threadIdx.x + (uint32_t)kThreads * (uint32_t)t;
+                    in[t] = s < r_hi;
+                    // o1 >= 1 for every slot in [r_lo, r_hi)
+                    const uint32_t o1 = in[t] ? (uint32_t)s_own[s - lo] : 0u;
+                    bool tok = false;
+                    int64_t idx = 0;
+                    if (o1 != 0u) {
+                        const uint32_t x = o1 - 1u;
+                        const uint32_t off = s - m_start[x];
+                        const uint32_t rl = m_real[x];
+                        tok = off < rl;
+                        // a pad slot re-reads its member's last token (none:
+                        // the first element), always inside the buffer
+                        idx = m_so[x] + (tok ? off : (rl ? rl - 1u : 0u));
+                        if (!tok && !rl) idx = 0;
                     }
-                    // two 8-byte loads (a paired 16-byte load measured slower)
-                    if (tok[0]) val[t][0] = src[idx[0]];
-                    if (tok[1]) val[t][1] = src[idx[1]];
-                    const uint32_t mk = (tok[0] ? 1u : 0u) | (tok[1] ? 0x100u : 0u);
-                    if (in[t][0] && in[t][1])
-                        *(uint16_t *)(s_mask + (u - lo)) = (uint16_t)mk;
-                    else if (in[t][0])
-                        s_mask[u - lo] = (uint8_t)mk;
-                    else if (in[t][1])
-                        s_mask[u + 1 - lo] = (uint8_t)(mk >> 8);
+                    const int64_t v = srcp[idx];
+                    val[t] = tok ? v : pad_token;
+                    if (in[t]) s_mask[s - lo] = tok ? 1 : 0;
                 }
 #pragma unroll
-                for (int t = 0; t < kPairs; ++t) {
-                    const uint32_t u = u0 + 2u * kThreads * (uint32_t)t;
-                    if (in[t][0] && in[t][1] && vec_out && ((p * (int64_t)C + u) & 1) == 0) {
-                        *(i64x2 *)(row + u) = i64x2{val[t][0], val[t][1]};
-                    } else {
-                        if (in[t][0]) row[u] = val[t][0];
-                        if (in[t][1]) row[u + 1] = val[t][1];
-                    }
+                for (int t = 0; t < kPerThread; ++t) {
+                    const uint32_t s = ub + threadIdx.x + (uint32_t)kThreads * (uint32_t)t;
+                    if (in[t]) row[s] = val[t];
                 }
             }
         }
@@ -291,12 +286,11 @@ hipError_t launch_pack_rows(const int64_t *src, int64_t src_len, const int64_t *
                             void *workspace, hipStream_t stream) {
     const uint32_t n_chunks = (uint32_t)(((int64_t)C + kSlots - 1) / kSlots);
     const uint64_t groups = P > 0 ? (uint64_t)P * n_chunks : 1ull;
-    const int vec_out = ((uintptr_t)packed % 16) == 0;
     const int vec_mask = ((uintptr_t)tmask % 16) == 0;
     hipLaunchKernelGGL(k_pack_rows, dim3((uint32_t)groups), dim3(kThreads), 0, stream, src,
                        src_len, src_off, src_stride, real_len, N, q, order, pack_start, P, C, fold,
                        pad_token, packed, tmask, cu, cp, status, (WsHeader *)workspace,
-                       n_chunks, vec_out, vec_mask);
+                       n_chunks, vec_mask);
     return hipGetLastError();
 }
 
