@@ -102,6 +102,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the bit-exact comparison of outputs with the CPU oracle")
     ap.add_argument("--per-config-iters", type=int, default=50)
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
                     help="write a markdown summary of a rocprofv3 kernel_stats.csv")
@@ -136,6 +138,11 @@ class Timer:
         self.torch.cuda.synchronize()
         v = [a.elapsed_time(b) for a, b in self.pairs]
         return sum(v) / len(v), min(v)
+
+    def median_ms(self):
+        self.torch.cuda.synchronize()
+        v = sorted(a.elapsed_time(b) for a, b in self.pairs)
+        return v[len(v) // 2]
 
 
 # ---------------------------------------------------------------------------
@@ -365,13 +372,143 @@ def setup_rect(torch, psq, lib, synth, dev):
 
 
 def measure(torch, call, iters, flush=None):
+    """(mean, min, median) ms of `iters` launches, HIP events on the launch stream."""
     timer = Timer(torch)
     for _ in range(iters):
         if flush is not None:
             flush()
         with timer:
             call()
-    return timer.mean_ms()
+    m, mn = timer.mean_ms()
+    return m, mn, timer.median_ms()
+
+
+# ---------------------------------------------------------------------------
+# parity in the same run: the outputs of the last timed call against the CPU
+# oracle on the same seeded inputs (every output is an integer or a byte copy)
+# ---------------------------------------------------------------------------
+
+def _eq(a, b, what):
+    import numpy as np
+    if not np.array_equal(np.asarray(a), np.asarray(b)):
+        raise AssertionError(f"parity: {what} differs from the oracle")
+
+
+def check_outputs(torch, name, keep):
+    import numpy as np
+
+    import oracle
+    import synth
+    if name in ("doc_map_small", "doc_map_medium"):
+        doc, cu, scal, _ = keep
+        ref = oracle.doc_segments(doc.cpu().numpy(), want_mask=False)
+        n = int(scal[0].item())
+        _eq(n, ref["num_segments"], "num_segments")
+        _eq(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"], "cu_seqlens")
+        _eq(int(scal[1].item()), ref["max_seqlen"], "max_seqlen")
+    elif name == "thd_tables":
+        t, outs, cu, cp, mask, scal, _ = keep
+        S = t["input_ids"].shape[1]
+        ref = oracle.thd_tables(t["seq_lens"].cpu().numpy(), t["seq_lens_padded"].cpu().numpy(), S)
+        n, mx, pb, st = scal.cpu().tolist()
+        _eq(st, ref["status"], "status")
+        _eq((n, mx, pb), (ref["num_seqs"], ref["max_seqlen"], ref["pad_between_seqs"]), "scalars")
+        _eq(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"], "cu_seqlens")
+        _eq(cp[: n + 1].cpu().numpy(), ref["cu_seqlens_padded"], "cu_seqlens_padded")
+        _eq(mask.cpu().numpy().astype(np.uint8), ref["padding_mask"], "padding_mask")
+        for k, o in outs.items():
+            src = t[k].cpu().numpy()
+            _eq(o.cpu().numpy().view(np.uint8),
+                oracle.copy_rows(src, 1, src.nbytes, src.nbytes), k)
+    elif name == "thd_split_4":
+        t, outs, cu, cp, mask, per, scal, _ = keep
+        S = t["input_ids"].shape[1]
+        G = per.shape[1]
+        ref = oracle.split_thd(t["seq_lens"].cpu().numpy(), t["seq_lens_padded"].cpu().numpy(),
+                               S, G)
+        width, st = scal.cpu().tolist()
+        _eq(st, ref["status"], "status")
+        _eq(cu[: G * width].view(G, width).cpu().numpy(), ref["cu_seqlens"], "cu_seqlens")
+        _eq(cp[: G * width].view(G, width).cpu().numpy(), ref["cu_seqlens_padded"],
+            "cu_seqlens_padded")
+        _eq(per.cpu().numpy(), np.stack([ref["num_seqs"], ref["max_seqlen"],
+                                         ref["pad_between_seqs"]]), "per-chunk scalars")
+        _eq(mask.cpu().numpy().astype(np.uint8).reshape(G, -1), ref["padding_mask"], "mask")
+    elif name == "pack_sources":
+        src, off, rl, ps, packed, tm, cu, cp, st, _ = keep
+        w = synth.pack_sources()
+        ref = oracle.pack(w["src"], w["src_off"], w["real_len"], w["q"], w["pack_start"],
+                          w["capacity"], fold=True)
+        _eq(int(st.item()), ref["status"], "status")
+        used = ref["cu_seqlens"].size
+        _eq(packed.cpu().numpy(), ref["packed"], "packed")
+        _eq(tm.cpu().numpy(), ref["token_mask"], "token_mask")
+        _eq(cu[:used].cpu().numpy(), ref["cu_seqlens"], "cu_seqlens")
+        _eq(cp[:used].cpu().numpy(), ref["cu_seqlens_padded"], "cu_seqlens_padded")
+    elif name == "pad_tail_stream":
+        ids, mask, scal, _ = keep
+        ref = oracle.pad_mask_from_ids(ids.cpu().numpy(), synth.pad_tail_stream()["pad_id"])
+        nc, st = scal.cpu().tolist()
+        _eq((nc, st), (ref["num_content"], ref["status"]), "num_content / status")
+        _eq(mask.cpu().numpy().astype(np.uint8), ref["padding_mask"], "padding_mask")
+    elif name == "trainer_rectangle":
+        rows, rl, order, starts, packed, tm, cu, cp, st, _ = keep
+        w = synth.trainer_rectangle()
+        ref = oracle.pack_rect(w["rows"], w["real_len"], w["q"], w["bins"])
+        used = ref["cu_seqlens"].size
+        _eq(int(st.item()), ref["status"], "status")
+        _eq(packed.cpu().numpy(), ref["packed"], "packed")
+        _eq(tm.cpu().numpy(), ref["token_mask"], "token_mask")
+        _eq(cu[:used].cpu().numpy(), ref["cu_seqlens"], "cu_seqlens")
+        _eq(cp[:used].cpu().numpy(), ref["cu_seqlens_padded"], "cu_seqlens_padded")
+    elif name == "stage_embedding":
+        out_h, out_p, cu, cp, mask, scal, _ = keep["out"]
+        ref = oracle.doc_segments(keep["host"]["doc_ids"])
+        n, mx, pb, st = scal.cpu().tolist()
+        _eq((n, mx, pb, st), (ref["num_segments"], ref["max_seqlen"], 0, 0), "scalars")
+        _eq(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"], "cu_seqlens")
+        _eq(cp[: n + 1].cpu().numpy(), ref["cu_seqlens"], "cu_seqlens_padded")
+        _eq(mask.cpu().numpy().astype(np.uint8), ref["padding_mask"], "padding_mask")
+        pos = keep["host"]["position_ids"]
+        _eq(out_p.cpu().numpy().view(np.uint8), oracle.copy_rows(pos, 1, pos.nbytes, pos.nbytes),
+            "position_ids")
+        # the 8 GiB hidden copy: identity, checked on the device in 64 MiB slices
+        h = keep["hidden"].view(-1, out_h.shape[1])
+        for r0 in range(0, h.shape[0], 8192):
+            if not torch.equal(out_h[r0:r0 + 8192].view(torch.int16), h[r0:r0 + 8192].view(torch.int16)):
+                raise AssertionError("parity: hidden differs from its input")
+    return "bit-exact"
+
+
+def copy_ceiling(torch, dev, nbytes=4 << 30):
+    """A device-to-device hipMemcpyAsync (torch copy_ of contiguous tensors) of
+    4 GiB: context for the collapse copy's rate."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    timer = Timer(torch)
+    for _ in range(10):
+        with timer:
+            dst.copy_(src)
+    m, mn = timer.mean_ms()
+    del src, dst
+    return {"what": "hipMemcpyAsync device to device, 4 GiB (torch copy_)",
+            "gbs_mean": round(2 * nbytes / (m * 1e-3) / 1e9, 1),
+            "gbs_best": round(2 * nbytes / (mn * 1e-3) / 1e9, 1)}
+
+
+def host_cpu():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "os_cpu_count": os.cpu_count()}
 
 
 def setup_calibration_copy(torch, psq, lib, dev, nbytes=1 << 30):
@@ -448,7 +585,7 @@ def cpu_baseline(torch, keep):
             "sample": f"{rows} of 32 rows ({tokens} tokens, {rows * doc_np.shape[1] * H * 2 >> 20} MiB "
                       f"of bf16 hidden): segmentation + mask + both collapses, median of 3, "
                       f"single-threaded C at -O2",
-            "seconds": round(t, 3), "host_cpus": os.cpu_count()}
+            "seconds": round(t, 3), "host": host_cpu()}
 
 
 WORKLOAD_OF = {
@@ -554,6 +691,8 @@ def main():
     k_mean, k_min = timer.mean_ms()
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, kernel {k_mean:.3f} ms",
           file=sys.stderr, flush=True)
+    parity = check_outputs(torch, "stage_embedding", keep) if not args.no_check else "not checked"
+    print(f"[bench] stage_embedding parity: {parity}", file=sys.stderr, flush=True)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -575,6 +714,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic (seeded generators; bf16 hidden N(0,1) drawn on the device)",
+        "parity": parity,
         "config": dict(info, **{"algorithmic_bytes_per_step": algo,
                                 "hbm_gbs_per_step": round(algo / (ms_per_step * 1e-3) / 1e9, 1)}),
         "roofline": dict(roofline(algo, k_mean, traffic),
@@ -600,17 +740,22 @@ def main():
             c_call, c_tok, c_algo, c_info, c_keep = setup()
             for _ in range(5):
                 c_call()
-            m, mn = measure(torch, c_call, args.per_config_iters, flush if do_flush else None)
+            m, mn, med = measure(torch, c_call, args.per_config_iters,
+                                 flush if do_flush else None)
+            parity = check_outputs(torch, name, c_keep) if not args.no_check else "not checked"
             per[name] = dict(c_info, **{
-                "us_mean": round(m * 1e3, 2), "us_min": round(mn * 1e3, 2),
+                "us_mean": round(m * 1e3, 2), "us_median": round(med * 1e3, 2),
+                "us_min": round(mn * 1e3, 2),
                 "gtok_s": round(c_tok / (m * 1e-3) / 1e9, 4), "tokens_per_call": c_tok,
-                "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m)})
-            print(f"[bench] {name}: {m * 1e3:.2f} us", file=sys.stderr, flush=True)
+                "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m), "parity": parity})
+            print(f"[bench] {name}: {m * 1e3:.2f} us, parity {parity}", file=sys.stderr, flush=True)
             del c_keep
         per["stage_embedding"] = {"us_mean": round(k_mean * 1e3, 2), "gtok_s": result["value"],
-                                  "roofline": roofline(algo, k_mean, traffic)}
+                                  "roofline": roofline(algo, k_mean, traffic),
+                                  "parity": result["parity"]}
         result["per_config"] = per
         del flush_buf
+        result["copy_ceiling"] = copy_ceiling(torch, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(torch, keep)
