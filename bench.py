@@ -37,8 +37,16 @@ METRIC = "packed tokens/sec (G tok/s) + achieved HBM GB/s vs MI355X peak, per co
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stage_embedding.json")
 
 
-# the sources the stage-embedding kernel (k_doc_segments_copy) is built from
-STAGE_KERNEL_SOURCES = ("k_segments.hip", "psq_copy.hpp", "psq_device.hpp")
+# the sources of the stage-embedding step's two kernels (k_doc_segments, then
+# the collapse copy k_copies)
+STAGE_KERNEL_SOURCES = ("k_segments.hip", "k_copy.hip", "psq_copy.hpp", "psq_device.hpp")
+
+# launch grids (work-items) of the stage step's kernels: 256 metadata tiles of
+# 256 threads, and one 64-lane workgroup per KiB of the 8 GiB + 8 MiB collapse
+STAGE_GRIDS = {"psq::k_doc_segments<int>": "65536",
+               "psq::k_copies<unsigned int __attribute__((ext_vector_type(4))), true>": "537395200"}
+# the 1 GiB calibration copy: a one-token map, then 2^26 copy lanes
+CALIB_GRID = str((1 << 30) // 16)
 
 
 def source_hash(names=STAGE_KERNEL_SOURCES) -> str:
@@ -59,7 +67,6 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     import csv
     import statistics
 
-    calib_grid = str((1 + (1 << 30) // 4096) * 256)      # 1 GiB copy + one metadata tile
 
     def load(path):
         per = {}
@@ -69,7 +76,7 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
                 continue
             short = name.split("(")[0].replace("void ", "")
             # one kernel can serve several workloads: the grid tells them apart
-            key = ("calibration_copy_1GiB" if r["Grid_Size"] == calib_grid
+            key = ("calibration_copy_1GiB" if r["Grid_Size"] == CALIB_GRID and "k_copies" in short
                    else f"{short} [grid {r['Grid_Size']}]")
             per.setdefault(key, []).append(float(r["Counter_Value"]))
         return {k: statistics.median(v) for k, v in per.items()}
@@ -84,9 +91,9 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
             rows[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
                        "read_bytes": round(rb), "write_bytes": round(wb),
                        "bytes_per_launch": round(rb + wb)}
-    stage = next(v for k, v in rows.items() if k.startswith("psq::k_doc_segments_copy"))
-    out = {"source_hash": source_hash(), "kernel": "psq::k_doc_segments_copy<int>",
-           "workload": "stage_embedding", "bytes_per_launch": stage["bytes_per_launch"],
+    stage = [rows[f"{k} [grid {g}]"]["bytes_per_launch"] for k, g in STAGE_GRIDS.items()]
+    out = {"source_hash": source_hash(), "kernel": " + ".join(STAGE_GRIDS),
+           "workload": "stage_embedding", "bytes_per_launch": sum(stage),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "kernels": rows}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -589,8 +596,7 @@ def cpu_baseline(torch, keep):
 
 
 WORKLOAD_OF = {
-    "k_doc_segments_copy": "stage_embedding: doc map [32,32768] + bf16 [32,32768,4096] collapse "
-                           "(and the 1 GiB calibration copy when present)",
+    "k_copies": "collapse copies",
     "k_pack_rows": "pack_sources: 65536 sources -> 16384-slot packs; trainer_rectangle: "
                    "256 rows -> token-budget bins",
     "k_thd_tables_copy": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses "
@@ -607,6 +613,11 @@ GRID_LABEL = {
     ("k_pack_rows", "15360"): "trainer_rectangle: 256 rows -> 15 token-budget bins",
     ("k_doc_segments", "256"): "doc_map_small [4,64]",
     ("k_doc_segments", "2048"): "doc_map_medium [8,4096]",
+    ("k_doc_segments", "65536"): "stage_embedding step, launch 1: doc map [32,32768] -> "
+                                 "cu_seqlens, max_seqlen, mask",
+    ("k_copies", "537395200"): "stage_embedding step, launch 2: bf16 [32,32768,4096] + int64 "
+                               "positions collapse (8 GiB + 8 MiB)",
+    ("k_copies", "67108864"): "1 GiB calibration copy (counter runs only)",
 }
 
 
@@ -718,7 +729,9 @@ def main():
         "config": dict(info, **{"algorithmic_bytes_per_step": algo,
                                 "hbm_gbs_per_step": round(algo / (ms_per_step * 1e-3) / 1e9, 1)}),
         "roofline": dict(roofline(algo, k_mean, traffic),
-                         kernel="k_doc_segments_copy<int> (segmentation + mask + collapse, one launch)",
+                         kernel="k_doc_segments<int> + k_copies<u32x4,true>: one psq_process_thd "
+                                "call, the metadata launch then the collapse copy (HIP events "
+                                "bracket both)",
                          kernel_ms_mean=round(k_mean, 4), kernel_ms_min=round(k_min, 4)),
     }
 

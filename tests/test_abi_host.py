@@ -121,6 +121,11 @@ def test_process_thd_validation(lib):
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
     arr, n = _lib.make_copies([(FAKE, FAKE + 65536, 1, 64, 64, -8)])
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
+    # more units than one launch grid holds: 2^31 + 1 single-byte units
+    arr, n = _lib.make_copies([(FAKE + 1, FAKE + (1 << 40), 1, (1 << 31) + 1, (1 << 31) + 1)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_OVERFLOW
+    arr, n = _lib.make_copies([(FAKE, FAKE + (1 << 40), 1 << 40, 1 << 30, 1 << 30)])
+    assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_OVERFLOW  # 2^70 B
     # destination rows at a stride reaching back into the source
     arr, n = _lib.make_copies([(FAKE + 4096, FAKE, 4, 64, 64, 2048)])
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG

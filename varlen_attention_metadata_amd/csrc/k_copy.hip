@@ -9,7 +9,7 @@ namespace {
 
 template <typename U, bool kDense>
 __global__ __launch_bounds__(kCopyThreads) void k_copies(CopyBatch batch) {
-    copy_group<U, kDense>(batch, blockIdx.x);
+    copy_group<kCopyThreads, U, kDense>(batch, blockIdx.x);
 }
 
 __global__ __launch_bounds__(kCopyThreads) void k_zero_fill(uint8_t *__restrict__ p, uint64_t bytes) {
@@ -27,6 +27,7 @@ __global__ __launch_bounds__(kCopyThreads) void k_zero_fill(uint8_t *__restrict_
 hipError_t launch_copy_plan(const CopyPlan &plan, int first_variant, hipStream_t stream) {
     for (int v = first_variant; v < 8; ++v) {
         if (plan.groups[v] == 0) continue;
+        if (plan.threads[v] != kCopyThreads) return hipErrorInvalidValue;
         const dim3 grid((uint32_t)plan.groups[v]), block(kCopyThreads);
         const CopyBatch &b = plan.batch[v];
 #define PSQ_COPY_LAUNCH(U)                                                                   \
@@ -49,7 +50,7 @@ hipError_t launch_copy_plan(const CopyPlan &plan, int first_variant, hipStream_t
 
 hipError_t launch_copies(const psq_copy *copies, int n_copies, hipStream_t stream) {
     CopyPlan plan;
-    plan_copies(copies, n_copies, &plan);
+    plan_copies(copies, n_copies, &plan, kCopyThreads);
     return launch_copy_plan(plan, 0, stream);
 }
 

@@ -18,7 +18,6 @@
 // a decoupled look-back whose descriptors carry (boundary count, last
 // boundary + 1), so the compaction and the longest-segment reduction finish
 // in the same pass.
-#include "psq_copy.hpp"
 #include "psq_device.hpp"
 #include "psq_internal.hpp"
 
@@ -301,34 +300,22 @@ __global__ __launch_bounds__(kThreads) void k_doc_segments(DocSegArgs<T> a) {
     doc_segments_body<T>(PSQ_DOC_ARGS(a), gridDim.x);
 }
 
-// The same tiles followed, in one grid, by the 16-byte dense copies of the
-// THD collapse: one launch per call instead of two.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_doc_segments_copy(DocSegArgs<T> a, uint32_t n_meta,
-                                                                CopyBatch batch) {
-    if (blockIdx.x < n_meta)
-        doc_segments_body<T>(PSQ_DOC_ARGS(a), n_meta);
-    else
-        copy_group<u32x4, true>(batch, (int64_t)blockIdx.x - n_meta);
-}
 #undef PSQ_DOC_ARGS
 
+// The metadata launch, then the collapse copies in one-wave workgroups.  The
+// copies are not fused into the metadata grid: on MI355X the 8 GiB collapse
+// of the stage-embedding workload streamed 3 % faster in its own launch of
+// one-wave workgroups (1 KiB each) than as 256-thread workgroups appended to
+// the metadata grid, and a fused grid of one-wave workgroups was slower
+// again (the look-back chain over 4x as many tiles).
 template <typename T>
 hipError_t launch_typed(DocSegArgs<T> a, const psq_copy *copies, int n_copies,
                         hipStream_t stream) {
     const uint32_t n_meta = a.n_tiles > 0 ? a.n_tiles : 1u;
-    CopyPlan plan;
-    plan_copies(copies, n_copies, &plan);
-    if (plan.groups[0] > 0) {
-        const uint64_t grid = (uint64_t)n_meta + (uint64_t)plan.groups[0];
-        hipLaunchKernelGGL(k_doc_segments_copy<T>, dim3((uint32_t)grid), dim3(kThreads), 0,
-                           stream, a, n_meta, plan.batch[0]);
-    } else {
-        hipLaunchKernelGGL(k_doc_segments<T>, dim3(n_meta), dim3(kThreads), 0, stream, a);
-    }
+    hipLaunchKernelGGL(k_doc_segments<T>, dim3(n_meta), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_copy_plan(plan, 1, stream);
+    if (e != hipSuccess || n_copies == 0) return e;
+    return launch_copies(copies, n_copies, stream);
 }
 
 }  // namespace

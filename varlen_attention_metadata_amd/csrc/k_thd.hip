@@ -476,14 +476,14 @@ __global__ __launch_bounds__(kThreads) void k_thd_tables_copy(ThdArgs<TL> a, uin
     if (blockIdx.x < n_meta)
         thd_tables_body<TL>(a, n_meta);
     else
-        copy_group<u32x4, true>(batch, (int64_t)blockIdx.x - n_meta);
+        copy_group<kThreads, u32x4, true>(batch, (int64_t)blockIdx.x - n_meta);
 }
 
 template <typename TL>
 hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, int n_copies,
                         hipStream_t stream) {
     CopyPlan plan;
-    plan_copies(copies, n_copies, &plan);
+    plan_copies(copies, n_copies, &plan, kThreads);
     if (plan.groups[0] > 0) {
         const uint64_t grid = (uint64_t)n_meta + (uint64_t)plan.groups[0];
         hipLaunchKernelGGL(k_thd_tables_copy<TL>, dim3((uint32_t)grid), dim3(kThreads), 0,

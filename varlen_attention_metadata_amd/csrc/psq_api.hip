@@ -3,7 +3,10 @@
 // before the first HIP call, so a rejected call enqueues nothing.
 #include <string.h>
 
+#include <algorithm>
+
 #include "psq.h"
+#include "psq_copy.hpp"
 #include "psq_internal.hpp"
 
 namespace {
@@ -30,10 +33,13 @@ int check_copies(const psq_copy *copies, int n_copies) {
             (c.rows > 1 && c.dst_row_stride_bytes != 0 && c.dst_row_stride_bytes < c.row_bytes))
             return PSQ_ERR_ARG;
         const int64_t dst_stride = c.dst_row_stride_bytes ? c.dst_row_stride_bytes : c.row_bytes;
+        const int64_t widest = std::max(std::max(dst_stride, c.src_row_stride_bytes), c.row_bytes);
+        if (c.rows > (INT64_MAX - c.row_bytes) / widest) return PSQ_ERR_OVERFLOW;
         const int64_t dst_span = (c.rows - 1) * dst_stride + c.row_bytes;
         const int64_t src_span = (c.rows - 1) * c.src_row_stride_bytes + c.row_bytes;
         if (overlaps(c.src, src_span, c.dst, dst_span)) return PSQ_ERR_ARG;
     }
+    if (!psq::copies_fit(copies, n_copies)) return PSQ_ERR_OVERFLOW;
     return PSQ_OK;
 }
 

@@ -8,12 +8,14 @@
 // THD buffer.
 //
 // Each copy is cut into units of g bytes, g the largest of 16/8/4/1 dividing
-// both addresses, the row length and both row strides.  A workgroup moves
-// 256 threads x 1 unit (4 KiB at g = 16): on MI355X many short workgroups
-// streamed faster than fewer long ones with several loads in flight per
-// thread (8 GiB copies: 6.4 TB/s at 4 KiB per workgroup, 5.5 TB/s at 16 KiB,
-// 5.0 TB/s at 32 KiB).  Loads are non-temporal (the source is read once);
-// stores are plain, which measured faster than non-temporal stores.
+// both addresses, the row length and both row strides.  A standalone copy
+// workgroup is one wave moving one unit per lane (1 KiB at g = 16): on
+// MI355X many short workgroups streamed faster than fewer long ones with
+// several loads in flight per thread (8 GiB copies: 6.55 TB/s at 1 KiB per
+// one-wave workgroup, 6.4 TB/s at 4 KiB per 256-thread workgroup, 5.5 TB/s
+// at 16 KiB, 5.0 TB/s at 32 KiB).  Loads are non-temporal (the source is
+// read once); stores are plain, which measured faster than non-temporal
+// stores.
 #pragma once
 
 #include "psq.h"
@@ -21,9 +23,9 @@
 
 namespace psq {
 
-constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 1;
-constexpr int64_t kCopyUnitsPerGroup = (int64_t)kCopyThreads * kCopyUnroll;
+// Threads of a standalone copy workgroup.  A fused launch carries its copy
+// workgroups at its own block size (kT below): one unit per thread.
+constexpr int kCopyThreads = 64;
 
 struct CopyJob {
     const uint8_t *src;
@@ -42,55 +44,53 @@ struct CopyBatch {
     int32_t n;
 };
 
-template <typename U, bool kDense>
+// Units u0 .. u0+kT-1 of one copy, one per thread of a kT-thread workgroup.
+template <int kT, typename U, bool kDense>
 __device__ __forceinline__ void copy_units(const CopyJob &jb, int64_t u0) {
     const U *__restrict__ s = (const U *)jb.src;
     U *__restrict__ d = (U *)jb.dst;
-    if (kDense && u0 + kCopyUnitsPerGroup <= jb.units) {
-        U v[kCopyUnroll];
-#pragma unroll
-        for (int k = 0; k < kCopyUnroll; ++k)
-            v[k] = __builtin_nontemporal_load(s + u0 + (int64_t)k * kCopyThreads + threadIdx.x);
-#pragma unroll
-        for (int k = 0; k < kCopyUnroll; ++k)
-            d[u0 + (int64_t)k * kCopyThreads + threadIdx.x] = v[k];
+    const int64_t u = u0 + threadIdx.x;
+    if (kDense && u0 + kT <= jb.units) {
+        d[u] = __builtin_nontemporal_load(s + u);
         return;
     }
-    // ragged tail or strided rows: one unit at a time (kept register-light,
-    // since a kernel's register budget is the maximum over all its paths)
-    const int64_t stride_units = jb.src_stride >> jb.shift;
-    const int64_t dst_stride_units = jb.dst_stride >> jb.shift;
-    for (int k = 0; k < kCopyUnroll; ++k) {
-        const int64_t u = u0 + (int64_t)k * kCopyThreads + threadIdx.x;
-        if (u >= jb.units) break;
-        int64_t at = u, to = u;
-        if (!kDense) {
-            const int64_t row = u / jb.units_per_row;
-            const int64_t col = u - row * jb.units_per_row;
-            at = row * stride_units + col;
-            to = row * dst_stride_units + col;
-        }
-        d[to] = __builtin_nontemporal_load(s + at);
+    // ragged tail or strided rows (kept register-light, since a kernel's
+    // register budget is the maximum over all its paths)
+    if (u >= jb.units) return;
+    int64_t at = u, to = u;
+    if (!kDense) {
+        const int64_t row = u / jb.units_per_row;
+        const int64_t col = u - row * jb.units_per_row;
+        at = row * (jb.src_stride >> jb.shift) + col;
+        to = row * (jb.dst_stride >> jb.shift) + col;
     }
+    d[to] = __builtin_nontemporal_load(s + at);
 }
 
-// Workgroup g of a batch: the jobs sit back to back in the grid.
-template <typename U, bool kDense>
+// Workgroup g of a batch planned at kT units per workgroup: the jobs sit
+// back to back in the grid.
+template <int kT, typename U, bool kDense>
 __device__ __forceinline__ void copy_group(const CopyBatch &batch, int64_t g) {
     int i = 0;
     while (i + 1 < batch.n && g >= batch.job[i + 1].group_begin) ++i;
     const CopyJob &jb = batch.job[i];
-    copy_units<U, kDense>(jb, (g - jb.group_begin) * kCopyUnitsPerGroup);
+    copy_units<kT, U, kDense>(jb, (g - jb.group_begin) * kT);
 }
 
+// Largest unit count of one call per kernel variant: the grid of a launch is
+// counted in 32-bit work-items, one per unit.
+constexpr int64_t kMaxCopyUnits = (int64_t)1 << 31;
+
 // Host side: the copies of one call grouped by kernel variant (unit shift
-// 4/3/2/0 x dense/strided).  Variant 0 (16-byte, dense) is the one the
-// fused metadata+copy launches carry; any other variant is launched alone.
+// 4/3/2/0 x dense/strided).  Variant 0 (16-byte, dense) is planned at
+// `fused_threads` units per workgroup -- the block size of the launch that
+// carries it; every other variant is launched alone, at kCopyThreads.
 struct CopyPlan {
     CopyBatch batch[8];
     int64_t groups[8];
     int shift[8];
     int dense[8];
+    int threads[8];
 };
 
 // Destination row stride of a copy (0 in the struct means dense rows).
@@ -110,8 +110,27 @@ inline int copy_unit_shift(const psq_copy &c) {
     return 0;
 }
 
-inline void plan_copies(const psq_copy *copies, int n_copies, CopyPlan *plan) {
+// True when every variant of these copies fits one launch.
+inline bool copies_fit(const psq_copy *copies, int n_copies) {
+    int64_t units[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < n_copies; ++i) {
+        const psq_copy &c = copies[i];
+        if (c.rows <= 0 || c.row_bytes <= 0) continue;
+        if (c.rows > INT64_MAX / c.row_bytes) return false;
+        const int shift = copy_unit_shift(c);
+        const int v = (shift == 4 ? 0 : shift == 3 ? 1 : shift == 2 ? 2 : 3);
+        const int64_t u = (c.rows * c.row_bytes) >> shift;
+        if (u >= kMaxCopyUnits) return false;
+        units[v] += u;
+        if (units[v] >= kMaxCopyUnits) return false;
+    }
+    return true;
+}
+
+inline void plan_copies(const psq_copy *copies, int n_copies, CopyPlan *plan,
+                        int fused_threads) {
     for (int v = 0; v < 8; ++v) {
+        const int64_t per_group = v == 0 ? fused_threads : kCopyThreads;
         const int want_shift = (v >> 1) == 0 ? 4 : (v >> 1) == 1 ? 3 : (v >> 1) == 2 ? 2 : 0;
         const int want_dense = (v & 1) == 0;
         CopyBatch &batch = plan->batch[v];
@@ -138,16 +157,18 @@ inline void plan_copies(const psq_copy *copies, int n_copies, CopyPlan *plan) {
             jb.dst_stride = copy_dst_stride(c);
             jb.dense = dense;
             jb.group_begin = groups;
-            groups += (jb.units + kCopyUnitsPerGroup - 1) / kCopyUnitsPerGroup;
+            groups += (jb.units + per_group - 1) / per_group;
         }
         batch.n = n;
         plan->groups[v] = groups;
         plan->shift[v] = want_shift;
         plan->dense[v] = want_dense;
+        plan->threads[v] = (int)per_group;
     }
 }
 
-// Launch every variant of the plan from `first_variant` on, alone.
+// Launch every variant of the plan from `first_variant` on, alone (variant 0
+// only when it was planned at kCopyThreads).
 hipError_t launch_copy_plan(const CopyPlan &plan, int first_variant, hipStream_t stream);
 
 }  // namespace psq
