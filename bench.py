@@ -5,7 +5,8 @@ One step is one ``psq_process_thd`` call on the pipeline-stage embedding
 workload: a document map int32 [32, 32768] (docs of length U{1..24},
 trailing pad U{0..16} per row) with bf16 hidden states [32, 32768, 4096]
 and int64 position ids, collapsed to THD [1048576, 4096] with cu_seqlens,
-max_seqlen and the padding mask -- one fused kernel launch.  Inputs are
+max_seqlen and the padding mask -- the map kernel, then the collapse copy.
+Inputs are
 resident in HBM before timing starts.  The other four workloads are timed
 too and reported under ``per_config`` (the document maps [4, 64] and
 [8, 4096], the length tables with 3 collapsed int64 tensors, and the
@@ -44,7 +45,7 @@ STAGE_KERNEL_SOURCES = ("k_segments.hip", "k_copy.hip", "psq_copy.hpp", "psq_dev
 # launch grids (work-items) of the stage step's kernels: 256 metadata tiles of
 # 256 threads, and one 64-lane workgroup per KiB of the 8 GiB + 8 MiB collapse
 STAGE_GRIDS = {"psq::k_doc_segments<int>": "65536",
-               "psq::k_copies<unsigned int __attribute__((ext_vector_type(4))), true>": "537395200"}
+               "psq::k_copies<u32x4, true>": "537395200"}
 # the 1 GiB calibration copy: a one-token map, then 2^26 copy lanes
 CALIB_GRID = str((1 << 30) // 16)
 
@@ -60,6 +61,16 @@ def source_hash(names=STAGE_KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_short_name(name: str) -> str:
+    """psq kernel name without namespaces' noise and without its parameter list
+    (vector element types are spelled u32x4)."""
+    import re
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    name = re.sub(r"unsigned int __attribute__\(\(ext_vector_type\((\d+)\)\)\)", r"u32x\1", name)
+    name = name.replace("unsigned int __vector(4)", "u32x4")
+    return name.split("(")[0]
+
+
 def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     """Turn two rocprofv3 --pmc runs of ``--profile-launches`` (FETCH_SIZE,
     then WRITE_SIZE, KiB per dispatch) into per-kernel HBM bytes, scaled by
@@ -71,10 +82,9 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     def load(path):
         per = {}
         for r in csv.DictReader(open(path)):
-            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
-            if "psq::" not in name:
+            if "psq::" not in r["Kernel_Name"]:
                 continue
-            short = name.split("(")[0].replace("void ", "")
+            short = kernel_short_name(r["Kernel_Name"])
             # one kernel can serve several workloads: the grid tells them apart
             key = ("calibration_copy_1GiB" if r["Grid_Size"] == CALIB_GRID and "k_copies" in short
                    else f"{short} [grid {r['Grid_Size']}]")
@@ -636,8 +646,7 @@ def summarize_trace(stats_csv: str, out_md: str, command: str) -> None:
     for r in csv.DictReader(open(trace_csv)):
         if "psq::" not in r["Kernel_Name"]:
             continue
-        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "")
-        short = name.split("(")[0]
+        short = kernel_short_name(r["Kernel_Name"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         per.setdefault((short, r["Grid_Size_X"]), []).append(dur)
     for (short, grid), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
@@ -649,8 +658,7 @@ def summarize_trace(stats_csv: str, out_md: str, command: str) -> None:
               "| kernel | calls | avg us |", "|---|---|---|"]
     for r in csv.DictReader(open(stats_csv)):
         if "psq::" in r["Name"]:
-            short = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
-            lines.append(f"| `{short.split('(')[0]}` | {r['Calls']} | "
+            lines.append(f"| `{kernel_short_name(r['Name'])}` | {r['Calls']} | "
                          f"{float(r['AverageNs']) / 1e3:.1f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -1,6 +1,6 @@
 // k_copy.hip -- copy-only launches of the THD collapse, and the workspace
 // zero fill.  The copy device code lives in psq_copy.hpp, shared with the
-// fused metadata+copy launches.
+// fused metadata+copy launch of the length-table path.
 #include "psq_copy.hpp"
 #include "psq_internal.hpp"
 

@@ -1,5 +1,6 @@
 // psq_copy.hpp -- the BSHD -> THD collapse as batched byte copies: device
-// code shared by the copy-only launch and the fused metadata+copy launches.
+// code shared by the copy-only launch and the fused metadata+copy launch of
+// the length-table path.
 //
 // NeMo AutoModel 0.5 API, nemo_automodel.components.distributed.thd_utils:
 // process_input_for_thd collapses the batch axis of input_ids / labels /

@@ -10,7 +10,7 @@
 
 namespace psq {
 
-// k_segments.hip -- document map -> segment boundaries (+ fused collapse copies).
+// k_segments.hip -- document map -> segment boundaries (then the collapse copies).
 size_t doc_segments_workspace(int64_t B, int64_t S);
 hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_t S,
                                int32_t *cu, int32_t *cu2, int32_t *num_segments,
