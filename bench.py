@@ -6,17 +6,17 @@ workload: a document map int32 [32, 32768] (docs of length U{1..24},
 trailing pad U{0..16} per row) with bf16 hidden states [32, 32768, 4096]
 and int64 position ids, collapsed to THD [1048576, 4096] with cu_seqlens,
 max_seqlen and the padding mask -- the map kernel, then the collapse copy.
-Inputs are
-resident in HBM before timing starts.  The other four workloads are timed
-too and reported under ``per_config`` (the document maps [4, 64] and
-[8, 4096], the length tables with 3 collapsed int64 tensors, and the
+Inputs are resident in HBM before timing starts.  The other four workloads
+are timed too and reported under ``per_config`` (the document maps [4, 64]
+and [8, 4096], the length tables with 3 collapsed int64 tensors, and the
 squeeze of 65536 sources into 16384-slot packs), and so are the steps around
 them: the length tables split into 4 row groups, the metadata-free padding
 mask of a 131072-id stream, and the trainer's squeeze of a 256-row padded
-rectangle into token-budget bins.
+rectangle into token-budget bins.  Every workload's outputs are compared bit
+for bit with the CPU oracle after timing.
 
 Prints one JSON line.  ``roofline`` relates the algorithmic bytes of one
-launch (each input read once, each output written once) to the launch's
+call (each input read once, each output written once) to the call's
 average duration from HIP events on the launch stream; ``cpu_baseline`` is
 the CPU oracle on a bounded sample of the same workload, on one host core.
 """
