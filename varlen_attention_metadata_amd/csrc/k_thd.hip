@@ -21,7 +21,9 @@
 // Work layout: one 256-thread workgroup per (row, chunk of 4096 slots).
 // Every workgroup re-derives its row's layout from the row's table (a few
 // hundred bytes, read through L2) into LDS and writes its chunk of the mask
-// from there: no workgroup waits on another for the mask.  The chunk-0
+// from there: no workgroup waits on another for the mask.  Each slot finds
+// its sequence through a per-chunk owner map (one LDS read) built by one
+// block-wide max scan over the sequences' start slots.  The chunk-0
 // workgroup of each row also takes part in a decoupled look-back over rows
 // carrying (sequence count, real-token sum) and writes the row's entries of
 // cu_seqlens / cu_seqlens_padded.  The last workgroup to finish applies the
@@ -185,6 +187,60 @@ inline ThdWsLayout thd_ws_layout(int64_t B, int64_t G, int64_t ld) {
     return w;
 }
 
+// Owner map of one chunk [lo, hi) for one LDS batch of nb sequences:
+// s_own[u - lo] = 1 + the last sequence of the batch starting at or before
+// slot u (0 before the batch's first start).  Starts are non-decreasing, so
+// each sequence marks its start slot (the last of equal starts wins: the
+// others own no slot) and one block-wide max scan fills the gaps; every slot
+// then finds its sequence with one LDS read instead of a binary search.
+constexpr int kOwnWords = kSlots / kThreads / 2;   // owner-map words per thread
+static_assert(kSlots % (kThreads * 8) == 0, "owner map is zeroed 16 bytes per thread");
+
+__device__ __forceinline__ void fill_owner_map(RowLds &s, uint16_t *s_own, uint32_t &s_before,
+                                               uint32_t nb, uint32_t lo, uint32_t hi) {
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    for (uint32_t e = threadIdx.x * 8u; e < kSlots; e += kThreads * 8u)
+        *(u32x4 *)(s_own + e) = u32x4{0u, 0u, 0u, 0u};
+    if (threadIdx.x == 0) s_before = 0;
+    __syncthreads();
+    uint32_t before = 0;     // 1 + the last sequence starting at or before lo
+    for (uint32_t k = threadIdx.x; k < nb; k += kThreads) {
+        const uint32_t st = (uint32_t)s.start[k];
+        if (st <= lo)
+            before = k + 1u;
+        else if (st < hi && (k + 1u == nb || (uint32_t)s.start[k + 1u] != st))
+            s_own[st - lo] = (uint16_t)(k + 1u);
+    }
+    if (before) atomicMax(&s_before, before);
+    __syncthreads();
+    // thread t owns kOwnWords consecutive words (2 entries each)
+    uint32_t v[kOwnWords];
+    const uint32_t *own_w = (const uint32_t *)s_own + threadIdx.x * kOwnWords;
+#pragma unroll
+    for (int e = 0; e < kOwnWords; ++e) v[e] = own_w[e];
+    uint32_t run = 0;
+#pragma unroll
+    for (int e = 0; e < kOwnWords; ++e) {
+        const uint32_t a0 = max(run, v[e] & 0xffffu);
+        const uint32_t a1 = max(a0, v[e] >> 16);
+        run = a1;
+        v[e] = a0 | (a1 << 16);
+    }
+    const uint32_t incl = (uint32_t)wave_incl_max((int)run);
+    if (lane == kWave - 1) s.wsum[0][w] = incl;
+    __syncthreads();
+    uint32_t pre = s_before;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q)
+        if (q < w) pre = max(pre, s.wsum[0][q]);
+    pre = max(pre, (uint32_t)wave_shr1((int)incl, 0));
+    uint32_t *own_o = (uint32_t *)s_own + threadIdx.x * kOwnWords;
+#pragma unroll
+    for (int e = 0; e < kOwnWords; ++e)
+        own_o[e] = max(v[e] & 0xffffu, pre) | (max(v[e] >> 16, pre) << 16);
+    __syncthreads();
+}
+
 template <typename TL>
 struct ThdArgs {
     const TL *L, *Lp;
@@ -221,6 +277,8 @@ __device__ __forceinline__ void thd_tables_body(const ThdArgs<TL> &args, uint32_
     WsHeader *__restrict__ ws = args.ws;
     __shared__ RowLds s;
     __shared__ __attribute__((aligned(16))) uint8_t s_mask[kSlots];
+    __shared__ __attribute__((aligned(16))) uint16_t s_own[kSlots];
+    __shared__ uint32_t s_before;
     __shared__ uint32_t s_slot;
     __shared__ uint32_t s_ex_a, s_ex_b, s_wserr;
 
@@ -264,15 +322,13 @@ __device__ __forceinline__ void thd_tables_body(const ThdArgs<TL> &args, uint32_
             // slots whose owner is in this batch: [first, end of its last one)
             const uint32_t b_lo = max(lo, first);
             const uint32_t b_hi = min(hi, carry[1]);
-            for (uint32_t u = b_lo + threadIdx.x; u < b_hi; u += kThreads) {
-                // last sequence of the batch starting at or before u
-                uint32_t a = 0, b = nb;
-                while (b - a > 1) {
-                    const uint32_t m = (a + b) >> 1;
-                    if ((uint32_t)s.start[m] <= u) a = m; else b = m;
+            if (b_lo < b_hi) {   // uniform
+                fill_owner_map(s, s_own, s_before, nb, lo, hi);
+                for (uint32_t u = b_lo + threadIdx.x; u < b_hi; u += kThreads) {
+                    const uint32_t a = (uint32_t)s_own[u - lo] - 1u;   // >= 0 here
+                    const bool tok = (u - (uint32_t)s.start[a]) < (uint32_t)s.real[a];
+                    s_mask[u - lo] = tok ? 0 : 1;
                 }
-                const bool tok = (u - (uint32_t)s.start[a]) < (uint32_t)s.real[a];
-                s_mask[u - lo] = tok ? 0 : 1;
             }
             __syncthreads();
             if (j0 + kBatch >= P) break;
