@@ -1,0 +1,146 @@
+"""GPU checks at the size limits of the C ABI, through the C ABI.
+
+Boundary arrays are int32, so a document map or a THD batch may hold up to
+2^31 - 1 tokens and a pack up to 2^30 slots.  At those sizes the CPU oracle
+would need tens of GB, so the outputs are checked against properties that
+hold at any size and that the inputs fix in closed form: every row start is
+a boundary, a row of one document and one trailing pad run has exactly two
+segments, the padding mask counts exactly the pad slots, and a squeezed
+source sits at its padded offset.  The same closed forms are checked against
+the oracle at small sizes first, so they are pinned to it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import varlen_attention_metadata_amd as psq
+from varlen_attention_metadata_amd import _lib
+
+pytestmark = pytest.mark.gpu
+V = -1000
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def two_run_rows(B, S, pad):
+    """Closed form of a map whose rows are one document then `pad` zeros."""
+    starts = []
+    for r in range(B):
+        starts.append(r * S)
+        if 0 < pad < S:
+            starts.append(r * S + S - pad)
+    return np.array(starts + [B * S], dtype=np.int64)
+
+
+def test_closed_form_matches_oracle_small():
+    B, S, pad = 5, 12, 3
+    doc = np.ones((B, S), dtype=np.int64)
+    doc[:, S - pad:] = 0
+    ref = oracle.doc_segments(doc)
+    assert np.array_equal(ref["cu_seqlens"], two_run_rows(B, S, pad))
+    assert ref["max_seqlen"] == S - pad
+    ref = oracle.thd_tables(np.array([[S - pad, V]] * B), np.array([[S - pad, V]] * B), S)
+    assert ref["cu_seqlens_padded"].tolist() == [r * S for r in range(B + 1)]
+    assert ref["cu_seqlens"].tolist() == [r * (S - pad) for r in range(B + 1)]
+    assert ref["pad_between_seqs"] == 1 and ref["max_seqlen"] == S - pad
+
+
+def test_doc_map_at_int32_limit(dev):
+    B, S, pad = 2047, 1 << 20, 4099
+    T = B * S
+    assert T < 2 ** 31
+    say(f"doc map at the int32 limit: B={B} S={S} (T={T})")
+    doc = torch.ones((B, S), dtype=torch.int32, device=dev)
+    doc[:, S - pad:] = 0
+    want = two_run_rows(B, S, pad)
+    cu_full = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    scal = torch.full((4,), -7, dtype=torch.int32, device=dev)
+    mask = torch.empty(T, dtype=torch.uint8, device=dev)
+    ws = psq.workspace_for(dev, _lib.psq_params_from_doc_ids_workspace(B, S))
+    sp = scal.data_ptr()
+    _lib.psq_params_from_doc_ids(doc.data_ptr(), _lib.I32, B, S, cu_full.data_ptr(), sp, sp + 4,
+                                 mask.data_ptr(), sp + 8, ws.data_ptr(), ws.numel(),
+                                 _stream(dev))
+    n, mx, st, _ = scal.cpu().tolist()
+    assert st == 0
+    assert n == want.size - 1
+    assert np.array_equal(cu_full[: n + 1].cpu().numpy(), want)
+    assert mx == S - pad
+    assert int(mask.sum(dtype=torch.int64).item()) == B * pad
+    del doc, mask, cu_full
+
+
+def test_thd_tables_at_int32_limit(dev):
+    B, S, real = 2047, 1 << 20, (1 << 20) - 4099
+    T = B * S
+    say(f"thd tables at the int32 limit: B={B} S={S}")
+    L = torch.tensor([[real, V]] * B, dtype=torch.int64, device=dev)
+    cap = B * 2 + 1
+    cu = torch.empty(cap, dtype=torch.int32, device=dev)
+    cp = torch.empty(cap, dtype=torch.int32, device=dev)
+    mask = torch.empty(T, dtype=torch.uint8, device=dev)
+    scal = torch.full((4,), -7, dtype=torch.int32, device=dev)
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, L.data_ptr(), L.data_ptr(), _lib.I64, 2, V)
+    ws = psq.workspace_for(dev, _lib.psq_process_thd_workspace(lay, B, S))
+    arr, n_c = _lib.make_copies([])
+    sp = scal.data_ptr()
+    _lib.psq_process_thd(lay, B, S, cu.data_ptr(), cp.data_ptr(), sp, sp + 4, sp + 8,
+                         mask.data_ptr(), arr, n_c, sp + 12, ws.data_ptr(), ws.numel(),
+                         _stream(dev))
+    n, mx, pb, st = scal.cpu().tolist()
+    assert st == 0 and n == B
+    assert cp[: n + 1].cpu().tolist() == [r * S for r in range(B + 1)]
+    # every row folds its tail pad: no interior boundary agrees, no absorption
+    assert cu[: n + 1].cpu().tolist() == [r * real for r in range(B + 1)]
+    assert pb == 1 and mx == real
+    assert int(mask.sum(dtype=torch.int64).item()) == B * (S - real)
+    del mask
+
+
+def test_pack_at_capacity_limit(dev):
+    C = 1 << 30
+    q = 64
+    lens = [5, 1000, 70000]
+    N = len(lens)
+    say(f"squeeze into one pack of {C} slots")
+    rng = np.random.default_rng(3)
+    toks = [rng.integers(0, 1 << 40, size=n) for n in lens]
+    src = torch.from_numpy(np.concatenate(toks)).to(dev)
+    off = torch.tensor(np.concatenate([[0], np.cumsum(lens)[:-1]]), dtype=torch.int64, device=dev)
+    rl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ps = torch.tensor([0, N], dtype=torch.int64, device=dev)
+    packed = torch.empty((1, C), dtype=torch.int64, device=dev)
+    tm = torch.empty((1, C), dtype=torch.uint8, device=dev)
+    cu = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    cp = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    st = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, _lib.psq_pack_rows_workspace(N, 1, C))
+    _lib.psq_pack_rows(src.data_ptr(), src.numel(), off.data_ptr(), rl.data_ptr(), N, q, None,
+                       ps.data_ptr(), 1, C, 1, -1, packed.data_ptr(), tm.data_ptr(),
+                       cu.data_ptr(), cp.data_ptr(), st.data_ptr(), ws.data_ptr(), ws.numel(),
+                       _stream(dev))
+    assert int(st.item()) == 0
+    padded = [-(-n // q) * q for n in lens]
+    assert cu.cpu().tolist() == [0, 5, 1005, 71005]
+    assert cp.cpu().tolist() == [0, padded[0], padded[0] + padded[1], C]
+    at = 0
+    for n, p, t in zip(lens, padded, toks):
+        assert np.array_equal(packed[0, at:at + n].cpu().numpy(), t)
+        assert bool((packed[0, at + n:at + p] == -1).all())
+        at += p
+    assert int(tm.sum(dtype=torch.int64).item()) == sum(lens)
+    assert bool((packed[0, at:] == -1).all())
+    del packed, tm
