@@ -1,0 +1,241 @@
+"""The C-ABI calls inside HIP graphs and on concurrent streams.
+
+Every call enqueues only kernels (the workspace is cleared by the kernels
+themselves and by a fill kernel, never by a memset node), so a captured call
+can be replayed.  Each graph here is replayed several times with eager work
+and synchronizations between replays, and every replay is compared with the
+CPU oracle.  Calls on two streams with their own workspaces must not
+interfere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from varlen_attention_metadata_amd import _lib
+
+pytestmark = pytest.mark.gpu
+V = -1000
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def zeroed_workspace(dev, nbytes):
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _lib.psq_workspace_init(ws.data_ptr(), ws.numel(), torch.cuda.current_stream(dev).cuda_stream)
+    return ws
+
+
+def replay_and_check(dev, call, outputs, check, replays=4):
+    """Capture `call(stream)` in a graph, then replay it `replays` times with
+    the outputs overwritten eagerly before each replay."""
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream(dev).cuda_stream)
+    for rep in range(replays):
+        for t in outputs:
+            t.fill_(7 + rep)                     # eager work between replays
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        check(rep)
+
+
+def test_graph_thd_tables_with_copies(dev):
+    w = synth.thd_tables()
+    S = w["S"]
+    B, P = w["seq_lens"].shape
+    T = B * S
+    say("graph: thd tables + 3 collapses")
+    t = {k: torch.from_numpy(w[k]).to(dev) for k in
+         ("input_ids", "labels", "position_ids", "seq_lens", "seq_lens_padded")}
+    outs = {k: torch.empty(T, dtype=torch.int64, device=dev) for k in ("input_ids", "labels", "position_ids")}
+    cu = torch.empty(B * P + 1, dtype=torch.int32, device=dev)
+    cp = torch.empty_like(cu)
+    mask = torch.empty(T, dtype=torch.uint8, device=dev)
+    scal = torch.empty(4, dtype=torch.int32, device=dev)
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, t["seq_lens"].data_ptr(),
+                           t["seq_lens_padded"].data_ptr(), _lib.I64, P, V)
+    ws = zeroed_workspace(dev, _lib.psq_process_thd_workspace(lay, B, S))
+    arr, n_c = _lib.make_copies([(t[k].data_ptr(), outs[k].data_ptr(), 1, T * 8, T * 8)
+                                 for k in ("input_ids", "labels", "position_ids")])
+    sp = scal.data_ptr()
+    ref = oracle.thd_tables(w["seq_lens"], w["seq_lens_padded"], S)
+
+    def call(stream):
+        _lib.psq_process_thd(lay, B, S, cu.data_ptr(), cp.data_ptr(), sp, sp + 4, sp + 8,
+                             mask.data_ptr(), arr, n_c, sp + 12, ws.data_ptr(), ws.numel(),
+                             stream)
+
+    def check(rep):
+        n, mx, pb, st = scal.cpu().tolist()
+        assert st == 0 and n == ref["num_seqs"], rep
+        assert (mx, pb) == (ref["max_seqlen"], ref["pad_between_seqs"]), rep
+        assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"]), rep
+        assert np.array_equal(cp[: n + 1].cpu().numpy(), ref["cu_seqlens_padded"]), rep
+        assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"]), rep
+        for k in outs:
+            assert np.array_equal(outs[k].cpu().numpy(), w[k].reshape(-1)), (rep, k)
+
+    replay_and_check(dev, call, [cu, cp, mask, scal] + list(outs.values()), check)
+
+
+def test_graph_doc_map_with_copy(dev):
+    d = synth.doc_map_medium()
+    B, S = d.shape
+    T = B * S
+    say("graph: doc map + bf16 collapse")
+    doc = torch.from_numpy(d).to(dev)
+    hidden = torch.randn((B, S, 64), dtype=torch.bfloat16, device=dev)
+    out_h = torch.empty((T, 64), dtype=torch.bfloat16, device=dev)
+    cu = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    mask = torch.empty(T, dtype=torch.uint8, device=dev)
+    scal = torch.empty(4, dtype=torch.int32, device=dev)
+    lay = _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=doc.data_ptr(), doc_dtype=_lib.I32)
+    ws = zeroed_workspace(dev, _lib.psq_process_thd_workspace(lay, B, S))
+    arr, n_c = _lib.make_copies([(hidden.data_ptr(), out_h.data_ptr(), 1, hidden.numel() * 2,
+                                  hidden.numel() * 2)])
+    sp = scal.data_ptr()
+    ref = oracle.doc_segments(d)
+
+    def call(stream):
+        _lib.psq_process_thd(lay, B, S, cu.data_ptr(), None, sp, sp + 4, sp + 8, mask.data_ptr(),
+                             arr, n_c, sp + 12, ws.data_ptr(), ws.numel(), stream)
+
+    def check(rep):
+        n, mx, pb, st = scal.cpu().tolist()
+        assert (n, mx, pb, st) == (ref["num_segments"], ref["max_seqlen"], 0, 0), rep
+        assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"]), rep
+        assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"]), rep
+        assert torch.equal(out_h.view(torch.int16), hidden.reshape(T, 64).view(torch.int16)), rep
+
+    replay_and_check(dev, call, [cu, mask, scal, out_h], check)
+
+
+def test_graph_pack_split_and_padids(dev):
+    w = synth.pack_sources(N=2048)
+    C, q = w["capacity"], w["q"]
+    N = w["real_len"].size
+    P = w["pack_start"].size - 1
+    say(f"graph: squeeze of {N} sources into {P} packs, a 4-group split, a pad-id mask")
+    src = torch.from_numpy(w["src"]).to(dev)
+    off = torch.from_numpy(w["src_off"]).to(dev)
+    rl = torch.from_numpy(w["real_len"]).to(dev)
+    ps = torch.from_numpy(w["pack_start"]).to(dev)
+    packed = torch.empty((P, C), dtype=torch.int64, device=dev)
+    tm = torch.empty((P, C), dtype=torch.uint8, device=dev)
+    pcu = torch.empty(N + P, dtype=torch.int32, device=dev)
+    pcp = torch.empty(N + P, dtype=torch.int32, device=dev)
+    pst = torch.empty(1, dtype=torch.int32, device=dev)
+    ws_pack = zeroed_workspace(dev, _lib.psq_pack_rows_workspace(N, P, C))
+    ref_pack = oracle.pack(w["src"], w["src_off"], w["real_len"], q, w["pack_start"], C)
+
+    t3 = synth.thd_tables()
+    S3 = t3["S"]
+    B3, P3 = t3["seq_lens"].shape
+    G = 4
+    L = torch.from_numpy(t3["seq_lens"]).to(dev)
+    Lp = torch.from_numpy(t3["seq_lens_padded"]).to(dev)
+    cap = G * (B3 // G * P3 + 1)
+    scu = torch.empty(cap, dtype=torch.int32, device=dev)
+    scp = torch.empty(cap, dtype=torch.int32, device=dev)
+    smask = torch.empty(B3 * S3, dtype=torch.uint8, device=dev)
+    per = torch.empty((3, G), dtype=torch.int32, device=dev)
+    sscal = torch.empty(2, dtype=torch.int32, device=dev)
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, L.data_ptr(), Lp.data_ptr(), _lib.I64, P3, V)
+    ws_split = zeroed_workspace(dev, _lib.psq_split_thd_workspace(lay, B3, S3, G))
+    noc, _ = _lib.make_copies([])
+    ref_split = oracle.split_thd(t3["seq_lens"], t3["seq_lens_padded"], S3, G)
+
+    pt = synth.pad_tail_stream()
+    ids = torch.from_numpy(pt["input_ids"]).to(dev)
+    Ti = ids.numel()
+    imask = torch.empty(Ti, dtype=torch.uint8, device=dev)
+    iscal = torch.empty(2, dtype=torch.int32, device=dev)
+    ws_ids = zeroed_workspace(dev, _lib.psq_padding_mask_from_token_ids_workspace(Ti))
+    ref_ids = oracle.pad_mask_from_ids(pt["input_ids"], pt["pad_id"])
+
+    def call(stream):
+        _lib.psq_pack_rows(src.data_ptr(), src.numel(), off.data_ptr(), rl.data_ptr(), N, q,
+                           None, ps.data_ptr(), P, C, 1, 0, packed.data_ptr(), tm.data_ptr(),
+                           pcu.data_ptr(), pcp.data_ptr(), pst.data_ptr(), ws_pack.data_ptr(),
+                           ws_pack.numel(), stream)
+        pp, sp = per.data_ptr(), sscal.data_ptr()
+        _lib.psq_split_thd(lay, B3, S3, G, scu.data_ptr(), scp.data_ptr(), sp, pp, pp + 4 * G,
+                           pp + 8 * G, smask.data_ptr(), noc, 0, sp + 4, ws_split.data_ptr(),
+                           ws_split.numel(), stream)
+        ip = iscal.data_ptr()
+        _lib.psq_padding_mask_from_token_ids(ids.data_ptr(), _lib.I64, Ti, pt["pad_id"],
+                                             imask.data_ptr(), ip, ip + 4, ws_ids.data_ptr(),
+                                             ws_ids.numel(), stream)
+
+    def check(rep):
+        used = ref_pack["cu_seqlens"].size
+        assert int(pst.item()) == 0, rep
+        assert np.array_equal(packed.cpu().numpy(), ref_pack["packed"]), rep
+        assert np.array_equal(tm.cpu().numpy(), ref_pack["token_mask"]), rep
+        assert np.array_equal(pcu[:used].cpu().numpy(), ref_pack["cu_seqlens"]), rep
+        assert np.array_equal(pcp[:used].cpu().numpy(), ref_pack["cu_seqlens_padded"]), rep
+        width, st = sscal.cpu().tolist()
+        assert st == 0 and width == ref_split["cu_seqlens"].shape[1], rep
+        assert np.array_equal(scu[: G * width].view(G, width).cpu().numpy(), ref_split["cu_seqlens"]), rep
+        assert np.array_equal(scp[: G * width].view(G, width).cpu().numpy(),
+                              ref_split["cu_seqlens_padded"]), rep
+        assert np.array_equal(per[1].cpu().numpy(), ref_split["max_seqlen"]), rep
+        assert np.array_equal(smask.cpu().numpy().reshape(G, -1), ref_split["padding_mask"]), rep
+        nc, ist = iscal.cpu().tolist()
+        assert (nc, ist) == (ref_ids["num_content"], ref_ids["status"]), rep
+        assert np.array_equal(imask.cpu().numpy(), ref_ids["padding_mask"]), rep
+
+    replay_and_check(dev, call, [packed, tm, pcu, pcp, pst, scu, scp, smask, per, sscal, imask,
+                                 iscal], check)
+
+
+def test_two_streams_with_own_workspaces(dev):
+    """Two different tables on two streams at once, each with its workspace."""
+    rng = np.random.default_rng(21)
+    cases = []
+    for k in range(2):
+        B, P, S = 12 + 4 * k, 40, 3000
+        L = np.full((B, P), V, dtype=np.int64)
+        for r in range(B):
+            m = int(rng.integers(1, P))
+            L[r, :m] = rng.integers(0, S // (2 * m) + 1, size=m)
+        cases.append((L, S))
+    say("two streams, two workspaces")
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    bufs = []
+    for (L, S), s in zip(cases, streams):
+        B, P = L.shape
+        tL = torch.from_numpy(L).to(dev)
+        cu = torch.empty(B * P + 1, dtype=torch.int32, device=dev)
+        mask = torch.empty(B * S, dtype=torch.uint8, device=dev)
+        scal = torch.empty(4, dtype=torch.int32, device=dev)
+        lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, tL.data_ptr(), None, _lib.I64, P, V)
+        ws = zeroed_workspace(dev, _lib.psq_process_thd_workspace(lay, B, S))
+        bufs.append((tL, cu, mask, scal, lay, ws, B, S, P))
+    torch.cuda.synchronize(dev)
+    arr, _ = _lib.make_copies([])
+    for it in range(10):
+        for (tL, cu, mask, scal, lay, ws, B, S, P), s in zip(bufs, streams):
+            sp = scal.data_ptr()
+            _lib.psq_process_thd(lay, B, S, cu.data_ptr(), None, sp, sp + 4, sp + 8,
+                                 mask.data_ptr(), arr, 0, sp + 12, ws.data_ptr(), ws.numel(),
+                                 s.cuda_stream)
+    torch.cuda.synchronize(dev)
+    for (L, S), (tL, cu, mask, scal, lay, ws, B, _, P) in zip(cases, bufs):
+        ref = oracle.thd_tables(L, None, S)
+        n, mx, pb, st = scal.cpu().tolist()
+        assert st == 0 and n == ref["num_seqs"] and mx == ref["max_seqlen"]
+        assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
+        assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
