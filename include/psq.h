@@ -215,7 +215,8 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S,
  *   status            int32 scalar, required (OR over the groups).
  *   workspace         psq_split_thd_workspace(layout, B, S, num_chunks) bytes.
  * Host errors: as psq_process_thd, plus PSQ_ERR_ARG when num_chunks < 1,
- * num_chunks does not divide B, or the layout is not a table layout.
+ * num_chunks does not divide B, the layout is not a table layout, or
+ * pad_value does not fit int32 (it fills int32 rows).
  * ---------------------------------------------------------------------- */
 size_t psq_split_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S,
                                int64_t num_chunks);

@@ -149,6 +149,8 @@ def test_split_thd_validation(lib):
     assert _split(lib, lay, G=3) == _lib.ERR_ARG                   # does not divide B
     assert _split(lib, _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=FAKE)) == _lib.ERR_ARG
     assert _split(lib, lay, w=None) == _lib.ERR_ARG
+    wide = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, FAKE, _lib.I64, 1, -(1 << 40))
+    assert _split(lib, wide) == _lib.ERR_ARG                       # sentinel beyond int32
     assert _split(lib, lay, n=None) == _lib.ERR_ARG
     assert _split(lib, lay, st=None) == _lib.ERR_ARG
     assert _split(lib, lay, B=1 << 20, S=1 << 12, G=1 << 10) == _lib.ERR_OVERFLOW

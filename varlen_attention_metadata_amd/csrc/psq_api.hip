@@ -164,6 +164,8 @@ int psq_split_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int64_t nu
     if (layout == nullptr || B < 0 || S < 0) return PSQ_ERR_ARG;
     if (num_chunks < 1 || B % num_chunks != 0) return PSQ_ERR_ARG;
     if (layout->kind != PSQ_LAYOUT_SEQ_LENS) return PSQ_ERR_ARG;
+    // the sentinel also fills the stacked int32 boundary rows
+    if (layout->pad_value < INT32_MIN || layout->pad_value > INT32_MAX) return PSQ_ERR_ARG;
     if (S > 0 && B > (kI32Limit - 1) / S) return PSQ_ERR_OVERFLOW;
     if (cu_seqlens == nullptr || cu_width == nullptr || num_seqs == nullptr ||
         max_seqlen == nullptr || pad_between_seqs == nullptr || status == nullptr)
