@@ -21,8 +21,10 @@
 // for the loads they need.  On MI355X this shape beat 256-thread workgroups
 // over 4096 slots by 4 %: a one-wave workgroup synchronizes cheaply, and more
 // of them stay resident.  Token-mask bytes are staged in LDS and leave as
-// 16-byte stores.  Stores are plain (not non-temporal): on gfx950 the
-// non-temporal form measured slower here.  The chunk-0 workgroup of each
+// 16-byte stores.  Every global load and store of the data is non-temporal
+// (each byte is touched once): on MI355X that took the 65536-source workload
+// from 194 to 173 us; non-temporal stores alone were slower (212 us), the
+// loads alone 181 us.  The chunk-0 workgroup of each
 // pack also writes the pack's boundary arrays and reports data errors
 // through one relaxed 64-bit word (finished count | status bits); the last
 // of those to finish publishes *status.
@@ -240,14 +242,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                         idx = m_so[x] + (tok ? off : (rl ? rl - 1u : 0u));
                         if (!tok && !rl) idx = 0;
                     }
-                    const int64_t v = srcp[idx];
+                    const int64_t v = __builtin_nontemporal_load(srcp + idx);
                     val[t] = tok ? v : pad_token;
                     if (in[t]) s_mask[s - lo] = tok ? 1 : 0;
                 }
 #pragma unroll
                 for (int t = 0; t < kPerThread; ++t) {
                     const uint32_t s = ub + threadIdx.x + (uint32_t)kThreads * (uint32_t)t;
-                    if (in[t]) row[s] = val[t];
+                    if (in[t]) __builtin_nontemporal_store(val[t], row + s);
                 }
             }
         }
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const uint32_t len = hi - lo;
         if (vec_mask && ((p * (int64_t)C + lo) % 16) == 0 && (len % 16) == 0) {
             for (uint32_t u = threadIdx.x * 16u; u < len; u += kThreads * 16u)
-                *(u32x4 *)(mrow + lo + u) = *(const u32x4 *)(s_mask + u);
+                __builtin_nontemporal_store(*(const u32x4 *)(s_mask + u), (u32x4 *)(mrow + lo + u));
         } else {
             for (uint32_t u = threadIdx.x; u < len; u += kThreads) mrow[lo + u] = s_mask[u];
         }
