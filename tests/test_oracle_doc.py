@@ -144,3 +144,19 @@ def test_copy_rows_is_identity():
     # strided rows: the first 3 columns of every row
     got = oracle.copy_rows(a, rows=5, row_bytes=3 * 8, src_row_stride_bytes=7 * 8)
     assert got.tobytes() == np.ascontiguousarray(a[:, :3]).tobytes()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_maps_against_groupby(seed):
+    # medium random maps of every flavour (long runs, short runs, heavy pad)
+    rng = np.random.default_rng(100 + seed)
+    B, S = int(rng.integers(1, 9)), int(rng.integers(1, 700))
+    alphabet = int(rng.integers(1, 6))
+    doc = rng.integers(0, alphabet, size=(B, S))
+    if seed % 2:                       # long runs: repeat each value a few times
+        doc = np.repeat(doc, int(rng.integers(2, 9)), axis=1)[:, :S]
+    out = oracle.doc_segments(doc)
+    cu, mx = groupby_segments(doc)
+    assert out["cu_seqlens"].tolist() == cu
+    assert out["max_seqlen"] == mx
+    assert out["padding_mask"].tolist() == (doc.reshape(-1) == 0).astype(int).tolist()

@@ -267,3 +267,32 @@ def test_workload_tables():
     ref = grid_formulation(L, Lp, S)
     assert cu.tolist() == ref["cu_seqlens"] and cp.tolist() == ref["cu_seqlens_padded"]
     assert out["padding_mask"].tolist() == ref["padding_mask"]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_tables_against_grid(seed):
+    # medium random tables (holes, zero lengths, tight and padded rows)
+    rng = np.random.default_rng(200 + seed)
+    B, P, S = int(rng.integers(1, 6)), int(rng.integers(1, 9)), int(rng.integers(4, 120))
+    L = np.full((B, P), V, dtype=np.int64)
+    Lp = np.full((B, P), V, dtype=np.int64)
+    for r in range(B):
+        used = 0
+        slots = sorted(rng.choice(P, size=int(rng.integers(1, P + 1)), replace=False))
+        for j in slots:
+            real = int(rng.integers(0, S // 3 + 1))
+            padded = real + (0 if seed % 3 == 0 else int(rng.integers(0, 4)))
+            if used + padded > S:
+                break
+            L[r, j], Lp[r, j] = real, padded
+            used += padded
+        if not (L[r] != V).any():
+            L[r, slots[0]], Lp[r, slots[0]] = 0, 0
+    out = oracle.thd_tables(L, Lp, S)
+    assert out["status"] == 0
+    ref = grid_formulation(L, Lp, S)
+    assert out["cu_seqlens"].tolist() == ref["cu_seqlens"]
+    assert out["cu_seqlens_padded"].tolist() == ref["cu_seqlens_padded"]
+    assert out["max_seqlen"] == ref["max_seqlen"]
+    assert out["pad_between_seqs"] == ref["pad_between_seqs"]
+    assert out["padding_mask"].tolist() == ref["padding_mask"]
