@@ -116,7 +116,14 @@ __device__ __forceinline__ void doc_segments_body(
         s_ex_a = 0;
         s_ex_b = 0;
     }
-    const uint32_t tile = claim_tile(ws, &s_slot);
+    // A map of one tile is one workgroup: it needs no ticket, no look-back and
+    // no completion counter, and leaves the workspace untouched.
+    const bool solo = n_groups == 1 && n_tiles <= 1;
+    uint32_t tile = 0;
+    if (solo)
+        __syncthreads();
+    else
+        tile = claim_tile(ws, &s_slot);
     const int w = threadIdx.x / kWave;
     const int lane = lane_id();
 
@@ -206,7 +213,7 @@ __device__ __forceinline__ void doc_segments_body(
         // ---------------- decoupled look-back (wave 0) --------------------
         if (w == 0) {
             if (tile == 0) {
-                if (lane == 0) st_relaxed(desc, desc_pack(kDescIncl, agg_c, agg_l));
+                if (lane == 0 && !solo) st_relaxed(desc, desc_pack(kDescIncl, agg_c, agg_l));
             } else {
                 if (lane == 0) st_relaxed(desc + tile, desc_pack(kDescAgg, agg_c, agg_l));
                 uint32_t ex_a, ex_b;
@@ -270,6 +277,14 @@ __device__ __forceinline__ void doc_segments_body(
         if (lane == kWave - 1) atomicMax(&s_max, lmax);
     }
     __syncthreads();
+    if (solo) {
+        if (threadIdx.x == 0) {
+            *max_seqlen = s_max;
+            if (status) *status = (int32_t)s_err;
+            if (pad_between) *pad_between = 0;
+        }
+        return;
+    }
     if (threadIdx.x == 0) {
         if (s_max > 0) max_relaxed(&ws->max, s_max);
         if (s_err) or_relaxed(&ws->status, s_err);
