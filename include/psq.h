@@ -31,8 +31,12 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  No
  *    call synchronizes: outputs and *status are valid once the stream reaches
  *    the work.  Calls that overlap in time must use distinct workspaces.
- *  - Return value: PSQ_OK, or a PSQ_ERR_* code for errors found on the host
- *    from the arguments alone.  Nothing is enqueued when an error is returned.
+ *  - Return value: PSQ_OK, or a PSQ_ERR_* code.  PSQ_ERR_ARG, _OVERFLOW and
+ *    _WORKSPACE are found on the host from the arguments alone, before
+ *    anything is enqueued.  PSQ_ERR_HIP means the runtime refused a launch;
+ *    launches of the same call issued before it may already be enqueued.
+ *  - Calls enqueue kernels only (no memset, no allocation), so they may be
+ *    captured in a HIP graph and replayed.
  *  - Data-dependent errors (found by the kernels) are bits OR-ed into the
  *    device word *status (0 = success).  Output contents are unspecified
  *    when *status != 0, but every kernel stays inside the buffers described
@@ -62,7 +66,8 @@ extern "C" {
 /* host-side return codes */
 #define PSQ_OK            0
 #define PSQ_ERR_ARG       1   /* null required pointer, bad enum, bad size   */
-#define PSQ_ERR_OVERFLOW  2   /* a size does not fit int32 boundaries        */
+#define PSQ_ERR_OVERFLOW  2   /* a size does not fit int32 boundaries, or a
+                                 call's copies do not fit one launch grid    */
 #define PSQ_ERR_WORKSPACE 3   /* workspace missing or smaller than required  */
 #define PSQ_ERR_HIP       4   /* the HIP runtime refused a launch            */
 
@@ -179,8 +184,9 @@ typedef struct psq_thd_layout {
  *   status            int32 scalar, required (data errors above).
  *   workspace         psq_process_thd_workspace(layout, B, S) bytes.
  * Host errors: PSQ_ERR_ARG (null pointer, negative size, bad kind/dtype,
- * n_copies out of range, a copy with a null pointer or overlapping src/dst),
- * PSQ_ERR_OVERFLOW (B*S or B*P+1 >= 2^31), PSQ_ERR_WORKSPACE.
+ * n_copies out of range, a copy with a null pointer, a stride below its row
+ * or overlapping src/dst), PSQ_ERR_OVERFLOW (B*S or B*P+1 >= 2^31, or copies
+ * of 2^31 units of one size or more), PSQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
 size_t psq_process_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S);
 int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S,
