@@ -79,7 +79,8 @@ def test_doc_page_examples(dev):
 @pytest.mark.parametrize("B,S", [(0, 5), (3, 0), (1, 1), (5, 1), (1, 2), (2, 3), (3, 4),
                                  (1, 5), (2, 63), (3, 64), (2, 65), (1, 255), (4, 256),
                                  (3, 1000), (2, 4095), (1, 4096), (2, 4097), (3, 8191),
-                                 (1, 12289), (2, 50000), (7, 3333)])
+                                 (1, 12289), (2, 50000), (7, 3333), (4097, 1), (16384, 2),
+                                 (1, 32767), (1, 32768), (1, 32769), (8, 4096)])
 @pytest.mark.parametrize("kind", ["alphabet3", "runs", "const", "pad_heavy"])
 def test_doc_fuzz(dev, B, S, kind):
     rng = np.random.default_rng(hash((B, S, kind)) % 2**32)
