@@ -623,7 +623,7 @@ def summarize_trace(stats_csv: str, out_md: str, command: str) -> None:
     import statistics
     trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
     lines = ["# Kernel trace: " + os.path.basename(out_md)[:-3], "",
-             "Command (GPU box, repository root):", "", "```", command, "```", "",
+             "Command (on an MI355X, from the repository root):", "", "```", command, "```", "",
              "| kernel | grid (threads) | workload | calls | avg us | min us | max us |",
              "|---|---|---|---|---|---|---|"]
     per = {}
