@@ -49,6 +49,17 @@ STAGE_GRIDS = {"psq::k_doc_segments<int>": "65536",
 # the 1 GiB calibration copy: a one-token map, then 2^26 copy lanes
 CALIB_GRID = str((1 << 30) // 16)
 
+# per-config workloads whose launch has a grid no other launch of a counter run
+# shares, and the sources that kernel is built from (the doc_map_small map
+# shares its grid with the calibration copy's map, and thd_split_4 its grid
+# with thd_tables, so neither is listed)
+WORKLOAD_COUNTERS = {
+    "pack_sources": ("psq::k_pack_rows [grid 3590144]", ("k_pack.hip", "psq_device.hpp")),
+    "trainer_rectangle": ("psq::k_pack_rows [grid 15360]", ("k_pack.hip", "psq_device.hpp")),
+    "pad_tail_stream": ("psq::k_pad_ids<long> [grid 8192]", ("k_padids.hip", "psq_device.hpp")),
+    "doc_map_medium": ("psq::k_doc_segments<int> [grid 2048]", ("k_segments.hip", "psq_device.hpp")),
+}
+
 
 def source_hash(names=STAGE_KERNEL_SOURCES) -> str:
     """Hash of the kernel's sources: stored HBM counter figures are only used
@@ -102,10 +113,13 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
                        "read_bytes": round(rb), "write_bytes": round(wb),
                        "bytes_per_launch": round(rb + wb)}
     stage = [rows[f"{k} [grid {g}]"]["bytes_per_launch"] for k, g in STAGE_GRIDS.items()]
+    workloads = {name: {"kernel": key, "source_hash": source_hash(srcs),
+                        "bytes_per_launch": rows[key]["bytes_per_launch"]}
+                 for name, (key, srcs) in WORKLOAD_COUNTERS.items() if key in rows}
     out = {"source_hash": source_hash(), "kernel": " + ".join(STAGE_GRIDS),
            "workload": "stage_embedding", "bytes_per_launch": sum(stage),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
-           "kernels": rows}
+           "workloads": workloads, "kernels": rows}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
@@ -698,11 +712,20 @@ def main():
     print(f"[bench] stage_embedding parity: {parity}", file=sys.stderr, flush=True)
 
     traffic = None
+    tr = {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("source_hash") == source_hash():
             traffic = tr.get("bytes_per_launch")
+
+    def workload_traffic(name):
+        """Counter bytes per launch of a per-config workload, or None once its
+        kernel's sources differ from those the counters were taken on."""
+        w = tr.get("workloads", {}).get(name)
+        if w is None or name not in WORKLOAD_COUNTERS:
+            return None
+        return w["bytes_per_launch"] if w["source_hash"] == source_hash(WORKLOAD_COUNTERS[name][1]) else None
 
     result = {
         "metric": METRIC,
@@ -753,7 +776,8 @@ def main():
                 "us_mean": round(m * 1e3, 2), "us_median": round(med * 1e3, 2),
                 "us_min": round(mn * 1e3, 2),
                 "gtok_s": round(c_tok / (m * 1e-3) / 1e9, 4), "tokens_per_call": c_tok,
-                "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m), "parity": parity})
+                "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m, workload_traffic(name)),
+                "parity": parity})
             print(f"[bench] {name}: {m * 1e3:.2f} us, parity {parity}", file=sys.stderr, flush=True)
             del c_keep
         per["stage_embedding"] = {"us_mean": round(k_mean * 1e3, 2), "gtok_s": result["value"],
