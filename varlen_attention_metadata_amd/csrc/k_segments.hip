@@ -142,14 +142,42 @@ __device__ __forceinline__ void doc_segments_body(
         T carry = (T)0;
         if (wave_base > 0 && wave_base < total) carry = doc[wave_base - 1];
 
+        // All of the wave's loads are issued before any is used.  A wave whose
+        // whole span is in range takes straight-line vector loads (a uniform
+        // branch); per-chunk branches would make the compiler wait for each
+        // load before issuing the next.
+        T dall[kIters][kPerLane];
+        int pres[kIters];
+        if (vec_in && wave_base + kWaveSpan <= total) {
+#pragma unroll
+            for (int j = 0; j < kIters; ++j) {
+                const uint32_t pos0 = wave_base + (uint32_t)j * kChunk + (uint32_t)lane * kPerLane;
+                if constexpr (sizeof(T) == 4) {
+                    const i32x4 v = *(const i32x4 *)(doc + pos0);
+                    dall[j][0] = v.x; dall[j][1] = v.y; dall[j][2] = v.z; dall[j][3] = v.w;
+                } else {
+                    const i64x2 v0 = *(const i64x2 *)(doc + pos0);
+                    const i64x2 v1 = *(const i64x2 *)(doc + pos0 + 2);
+                    dall[j][0] = v0.x; dall[j][1] = v0.y; dall[j][2] = v1.x; dall[j][3] = v1.y;
+                }
+                pres[j] = kPerLane;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kIters; ++j) {
+                const uint32_t pos0 = wave_base + (uint32_t)j * kChunk + (uint32_t)lane * kPerLane;
+                pres[j] = load4(doc, pos0, total, vec_in != 0, dall[j]);
+            }
+        }
+
         uint32_t fm[kIters], off[kIters], prv[kIters];
         uint32_t run_c = 0, run_l = 0;
         const bool small_s = S < (uint32_t)kPerLane;
 #pragma unroll
         for (int j = 0; j < kIters; ++j) {
             const uint32_t pos0 = wave_base + (uint32_t)j * kChunk + (uint32_t)lane * kPerLane;
-            T d[kPerLane];
-            const int present = load4(doc, pos0, total, vec_in != 0, d);
+            const T *d = dall[j];
+            const int present = pres[j];
 
             if (mask != nullptr && present > 0) {
                 if (present == kPerLane && vec_mask) {
