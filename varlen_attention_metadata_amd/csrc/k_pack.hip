@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
                 for (int t = 0; t < kPerThread; ++t) {
                     const uint32_t s = ub + threadIdx.x + (uint32_t)kThreads * (uint32_t)t;
-                    if (in[t]) __builtin_nontemporal_store(val[t], row + s);
+                    if (in[t]) store_stream(row + s, val[t]);
                 }
             }
         }
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const uint32_t len = hi - lo;
         if (vec_mask && ((p * (int64_t)C + lo) % 16) == 0 && (len % 16) == 0) {
             for (uint32_t u = threadIdx.x * 16u; u < len; u += kThreads * 16u)
-                __builtin_nontemporal_store(*(const u32x4 *)(s_mask + u), (u32x4 *)(mrow + lo + u));
+                store_stream((u32x4 *)(mrow + lo + u), *(const u32x4 *)(s_mask + u));
         } else {
             for (uint32_t u = threadIdx.x; u < len; u += kThreads) mrow[lo + u] = s_mask[u];
         }

@@ -52,7 +52,10 @@ __device__ __forceinline__ void copy_units(const CopyJob &jb, int64_t u0) {
     U *__restrict__ d = (U *)jb.dst;
     const int64_t u = u0 + threadIdx.x;
     if (kDense && u0 + kT <= jb.units) {
-        __builtin_nontemporal_store(__builtin_nontemporal_load(s + u), d + u);
+        if constexpr (sizeof(U) == 16)
+            store_stream(d + u, __builtin_nontemporal_load(s + u));
+        else
+            __builtin_nontemporal_store(__builtin_nontemporal_load(s + u), d + u);
         return;
     }
     // ragged tail or strided rows (kept register-light, since a kernel's
