@@ -147,8 +147,23 @@ def test_split_hand_ragged(dev):
     ([[3, 2], [V, V]], [[4, 2], [V, V]], 8, 2),     # empty row in chunk 1
     ([[9], [2]], [[9], [2]], 8, 2),                 # row overflow in chunk 0
 ])
-def test_split_error_bits(dev, L, Lp, S, G):
-    check_split(dev, np.array(L), np.array(Lp), S, G)
+@pytest.mark.parametrize("wide", [False, True])
+def test_split_error_bits(dev, L, Lp, S, G, wide):
+    L, Lp = np.array(L), np.array(Lp)
+    if wide:
+        # sentinel columns: the same tables, past the single-workgroup size
+        extra = np.full((L.shape[0], 2100), V)
+        L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
+    check_split(dev, L, Lp, S, G)
+
+
+# on either side of the single-workgroup limits (2048 entries, 64 groups)
+@pytest.mark.parametrize("B,P,S,G", [(128, 2, 16, 64), (130, 2, 16, 65), (64, 32, 100, 64),
+                                     (64, 33, 100, 16)])
+def test_split_single_workgroup_limits(dev, B, P, S, G):
+    rng = np.random.default_rng(B * 7919 + P * 31 + G)
+    L, Lp = rand_tables(rng, B, P, S, 4)
+    check_split(dev, L, Lp, S, G)
 
 
 def test_split_matches_process_thd_at_one_chunk(dev):

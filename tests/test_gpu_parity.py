@@ -234,8 +234,25 @@ def test_thd_hand_cases(dev, L, Lp, S):
     ([[4]], [[2**62]], 8),
     ([[5], [V]], [[4], [V]], 8),
 ])
-def test_thd_error_bits(dev, L, Lp, S):
-    check_thd(dev, np.array(L), np.array(Lp), S)
+@pytest.mark.parametrize("wide", [False, True])
+def test_thd_error_bits(dev, L, Lp, S, wide):
+    L, Lp = np.array(L), np.array(Lp)
+    if wide:
+        # sentinel columns change nothing but take the table past the
+        # single-workgroup size, so the multi-workgroup kernel decides
+        extra = np.full((L.shape[0], 2100), V)
+        L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
+    check_thd(dev, L, Lp, S)
+
+
+# tables on either side of the single-workgroup limit (2048 entries)
+@pytest.mark.parametrize("B,P,S", [(32, 64, 300), (33, 64, 300), (1, 2048, 5000), (1, 2049, 5000),
+                                   (512, 1, 7), (513, 1, 7), (512, 4, 40)])
+def test_thd_single_workgroup_limits(dev, B, P, S):
+    rng = np.random.default_rng(B * 10007 + P)
+    L, Lp = rand_tables(rng, B, P, S, 4, maxlen=max(1, S // max(1, P // 4)))
+    check_thd(dev, L, Lp, S)
+    check_thd(dev, L, None, S)
 
 
 def rand_tables(rng, B, P, S, q, tight=False, holes=False, zero_frac=0.1, maxlen=None):

@@ -64,25 +64,27 @@ struct RowLds {
     int32_t last_real, last_pad;
 };
 
-// Exclusive block scan of three uint32 values (wrapping arithmetic).
-__device__ __forceinline__ void block_scan3(RowLds &s, uint32_t v0, uint32_t v1, uint32_t v2,
-                                            uint32_t (&ex)[3], uint32_t (&tot)[3]) {
+// Exclusive block scan of three uint32 values (wrapping arithmetic) over a
+// workgroup of kW waves.
+template <int kW = kWaves>
+__device__ __forceinline__ void block_scan3(uint32_t (&wsum)[3][kW], uint32_t v0, uint32_t v1,
+                                            uint32_t v2, uint32_t (&ex)[3], uint32_t (&tot)[3]) {
     const int w = threadIdx.x / kWave, lane = lane_id();
     const uint32_t in[3] = {v0, v1, v2};
     uint32_t inc[3];
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         inc[q] = (uint32_t)wave_incl_sum((int)in[q]);
-        if (lane == kWave - 1) s.wsum[q][w] = inc[q];
+        if (lane == kWave - 1) wsum[q][w] = inc[q];
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         uint32_t before = 0, all = 0;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
+        for (int v = 0; v < kW; ++v) {
             if (v == w) before = all;
-            all += s.wsum[q][v];
+            all += wsum[q][v];
         }
         ex[q] = before + inc[q] - in[q];
         tot[q] = all;
@@ -132,7 +134,7 @@ __device__ __forceinline__ uint32_t row_batch(RowLds &s, const TL *__restrict__ 
         }
     }
     uint32_t ex[3], tot[3];
-    block_scan3(s, cnt, pad, real, ex, tot);
+    block_scan3(s.wsum, cnt, pad, real, ex, tot);
     uint32_t ci = ex[0], st = carry[1] + ex[1], rp = carry[2] + ex[2];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -257,6 +259,63 @@ struct ThdArgs {
     WsHeader *ws;
 };
 
+// Row r's layout from its table (batch by batch into LDS) and chunk c of the
+// mask.  `s` must hold zeroed accumulators, published by a barrier.  On
+// return carry = (sequences, padded sum, real sum) of the row and `s` holds
+// the row's last batch and its per-row flags.
+template <typename TL>
+__device__ __forceinline__ void row_layout_and_mask(const ThdArgs<TL> &args, RowLds &s,
+                                                    uint8_t *s_mask, uint16_t *s_own,
+                                                    uint32_t &s_before, uint32_t r, uint32_t c,
+                                                    uint32_t (&carry)[3]) {
+    const TL *__restrict__ L = args.L;
+    const TL *__restrict__ Lp = args.Lp;
+    const uint32_t P = args.P, S = args.S;
+    const int64_t pad_value = args.pad_value;
+    uint8_t *__restrict__ mask = args.mask;
+    const int vec_mask = args.vec_mask;
+    const uint32_t lo = c * kSlots;
+    const uint32_t hi = min(S, lo + kSlots);
+    const uint64_t row_off = (uint64_t)r * P;
+
+    // chunk mask starts as all padding; token slots are cleared below
+    for (uint32_t u = threadIdx.x * 16u; u < kSlots; u += kThreads * 16u)
+        *(u32x4 *)(s_mask + u) = u32x4{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+
+    for (uint32_t j0 = 0; j0 < P || j0 == 0; j0 += kBatch) {
+        const uint32_t first = carry[1];
+        const uint32_t nb = row_batch(s, L, Lp, row_off, P, S, pad_value, j0, carry);
+        if (nb == 0 || hi <= lo) {
+            if (j0 + kBatch >= P) break;
+            continue;
+        }
+        // slots whose owner is in this batch: [first, end of its last one)
+        const uint32_t b_lo = max(lo, first);
+        const uint32_t b_hi = min(hi, carry[1]);
+        if (b_lo < b_hi) {   // uniform
+            fill_owner_map(s, s_own, s_before, nb, lo, hi);
+            for (uint32_t u = b_lo + threadIdx.x; u < b_hi; u += kThreads) {
+                const uint32_t a = (uint32_t)s_own[u - lo] - 1u;   // >= 0 here
+                const bool tok = (u - (uint32_t)s.start[a]) < (uint32_t)s.real[a];
+                s_mask[u - lo] = tok ? 0 : 1;
+            }
+        }
+        __syncthreads();
+        if (j0 + kBatch >= P) break;
+    }
+
+    if (mask != nullptr && hi > lo) {
+        const uint64_t g = (uint64_t)r * S + lo;
+        const uint32_t len = hi - lo;
+        if (vec_mask && (g % 16) == 0 && (len % 16) == 0) {
+            for (uint32_t u = threadIdx.x * 16u; u < len; u += kThreads * 16u)
+                *(u32x4 *)(mask + g + u) = *(const u32x4 *)(s_mask + u);
+        } else {
+            for (uint32_t u = threadIdx.x; u < len; u += kThreads) mask[g + u] = s_mask[u];
+        }
+    }
+}
+
 // One (row, chunk) per workgroup; `n_groups` is the number of workgroups
 // running this body (the launch may append copy workgroups after them).
 template <typename TL>
@@ -266,14 +325,12 @@ __device__ __forceinline__ void thd_tables_body(const ThdArgs<TL> &args, uint32_
     const uint32_t B = args.B, P = args.P, S = args.S;
     const int64_t pad_value = args.pad_value;
     const uint32_t n_chunks = args.n_chunks;
-    const int vec_mask = args.vec_mask;
     const uint32_t G = args.G, Bc = args.Bc, ld = args.ld;
     int32_t *__restrict__ cu = args.cu;
     int32_t *__restrict__ cp = args.cp;
     int32_t *__restrict__ cu_st = args.cu_st;
     int32_t *__restrict__ cp_st = args.cp_st;
     GroupRec *__restrict__ recs = args.recs;
-    uint8_t *__restrict__ mask = args.mask;
     WsHeader *__restrict__ ws = args.ws;
     __shared__ RowLds s;
     __shared__ __attribute__((aligned(16))) uint8_t s_mask[kSlots];
@@ -302,48 +359,11 @@ __device__ __forceinline__ void thd_tables_body(const ThdArgs<TL> &args, uint32_
         const bool leader = (c == 0);
         const uint32_t g = r / Bc;           // group of the row
         const uint32_t rg = r - g * Bc;      // row inside its group
-        const uint32_t lo = c * kSlots;
-        const uint32_t hi = min(S, lo + kSlots);
         const uint64_t row_off = (uint64_t)r * P;
 
-        // chunk mask starts as all padding; token slots are cleared below
-        for (uint32_t u = threadIdx.x * 16u; u < kSlots; u += kThreads * 16u)
-            *(u32x4 *)(s_mask + u) = u32x4{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
-
         uint32_t carry[3] = {0, 0, 0};
-        bool one_batch = P <= (uint32_t)kBatch;
-        for (uint32_t j0 = 0; j0 < P || j0 == 0; j0 += kBatch) {
-            const uint32_t first = carry[1];
-            const uint32_t nb = row_batch(s, L, Lp, row_off, P, S, pad_value, j0, carry);
-            if (nb == 0 || hi <= lo) {
-                if (j0 + kBatch >= P) break;
-                continue;
-            }
-            // slots whose owner is in this batch: [first, end of its last one)
-            const uint32_t b_lo = max(lo, first);
-            const uint32_t b_hi = min(hi, carry[1]);
-            if (b_lo < b_hi) {   // uniform
-                fill_owner_map(s, s_own, s_before, nb, lo, hi);
-                for (uint32_t u = b_lo + threadIdx.x; u < b_hi; u += kThreads) {
-                    const uint32_t a = (uint32_t)s_own[u - lo] - 1u;   // >= 0 here
-                    const bool tok = (u - (uint32_t)s.start[a]) < (uint32_t)s.real[a];
-                    s_mask[u - lo] = tok ? 0 : 1;
-                }
-            }
-            __syncthreads();
-            if (j0 + kBatch >= P) break;
-        }
-
-        if (mask != nullptr && hi > lo) {
-            const uint64_t g = (uint64_t)r * S + lo;
-            const uint32_t len = hi - lo;
-            if (vec_mask && (g % 16) == 0 && (len % 16) == 0) {
-                for (uint32_t u = threadIdx.x * 16u; u < len; u += kThreads * 16u)
-                    *(u32x4 *)(mask + g + u) = *(const u32x4 *)(s_mask + u);
-            } else {
-                for (uint32_t u = threadIdx.x; u < len; u += kThreads) mask[g + u] = s_mask[u];
-            }
-        }
+        const bool one_batch = P <= (uint32_t)kBatch;
+        row_layout_and_mask(args, s, s_mask, s_own, s_before, r, c, carry);
 
         if (leader) {
             const uint32_t count = carry[0];
@@ -535,10 +555,404 @@ __global__ __launch_bounds__(kThreads) void k_thd_tables_copy(ThdArgs<TL> a, uin
         copy_group<kThreads, u32x4, true>(batch, (int64_t)blockIdx.x - n_meta);
 }
 
+// ---------------------------------------------------------------------------
+// Small tables (B*P <= kSmallEntries, G <= kSmallGroups).
+// Workgroup 0 holds the whole table in registers and LDS and derives every
+// group's boundaries and scalars from it with block-wide scans; each of the
+// next workgroups writes one (row, chunk) of the mask from its own row's
+// table.  No workgroup waits on another, so there is no ticket, look-back or
+// completion count, and the workspace is left untouched.  The status bits
+// are the same predicates as above, evaluated over the whole table at once.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSmallEntries = 2048;
+constexpr uint32_t kSmallGroups = 64;
+constexpr int kSmallThreads = 1024;      // workgroup size of the small-table launch
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr int kSmallPer = (int)(kSmallEntries / kSmallThreads);   // table entries per thread
+constexpr uint32_t kSmallSlots = 16384;   // mask slots per workgroup (1024 per wave)
+constexpr uint32_t kNoSeq = 0xffffffffu;   // real[] of an entry holding no sequence
+
+struct SmallMeta {
+    uint32_t real[kSmallEntries];             // clamped real length, or kNoSeq
+    uint32_t phys[kSmallEntries];             // clamped padded length; a row's last folded
+    uint32_t g_last[kSmallGroups];            // 1 + the group's last valid entry
+    uint32_t g_flag[kSmallGroups];            // an interior boundary departs from its physical one
+    int32_t g_max[kSmallGroups];              // largest real length of the group
+    uint32_t g_base[3][kSmallGroups + 1];     // (count, real, physical) before each group
+    uint32_t wsum[3][kSmallWaves];
+    uint32_t err;
+};
+
+// a + b saturated at `sat` (sat <= 2^31; a, b <= sat, so a wrap is caught)
+__device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat) {
+    const uint32_t s = a + b;
+    return (s < a || s > sat) ? sat : s;
+}
+
+template <typename TL>
+__device__ __forceinline__ void thd_small_meta(const ThdArgs<TL> &args, SmallMeta &m) {
+    const uint32_t B = args.B, P = args.P, S = args.S, G = args.G, Bc = args.Bc;
+    const uint32_t E = B * P;       // table entries, 1 .. kSmallEntries
+    const uint32_t Eg = Bc * P;     // entries of one group
+    const uint32_t Tc = Bc * S;     // tokens of one group (< 2^31)
+    const uint32_t sat = S + 1u;    // clamp of a length, and of a row's padded sum
+    const int64_t pv = args.pad_value;
+    const TL *__restrict__ L = args.L;
+    const TL *__restrict__ Lq = args.Lp ? args.Lp : args.L;
+    int32_t *__restrict__ cu = args.cu;
+    int32_t *__restrict__ cp = args.cp;
+    const int w = threadIdx.x / kWave, lane = lane_id();
+
+    for (uint32_t g = threadIdx.x; g < G; g += kSmallThreads) {
+        m.g_last[g] = 0;
+        m.g_flag[g] = 0;
+        m.g_max[g] = 0;
+    }
+    if (threadIdx.x == 0) m.err = 0;
+
+    // thread t owns the kSmallPer consecutive entries from e0; every load is
+    // issued before any is used (indices clamped into the table)
+    const uint32_t e0 = threadIdx.x * (uint32_t)kSmallPer;
+    int64_t l[kSmallPer], lp[kSmallPer];
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        const uint32_t e = min(e0 + (uint32_t)k, E - 1u);
+        l[k] = (int64_t)L[e];
+        lp[k] = (int64_t)Lq[e];
+    }
+
+    // validity, the length checks, clamped lengths (kept in registers, and
+    // in LDS for the row pass)
+    uint32_t rc[kSmallPer], pc[kSmallPer];
+    uint32_t err = 0;
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        const uint32_t e = e0 + (uint32_t)k;
+        rc[k] = kNoSeq;
+        pc[k] = 0;
+        if (e < E) {
+            const bool valid = l[k] != pv;
+            if (args.Lp && ((lp[k] != pv) != valid)) err |= PSQ_DATA_TABLE_MISMATCH;
+            if (valid) {
+                if (l[k] < 0 || lp[k] < l[k]) err |= PSQ_DATA_BAD_LENGTH;
+                const int64_t lim = (int64_t)sat;
+                pc[k] = (uint32_t)(lp[k] < 0 ? 0 : (lp[k] > lim ? lim : lp[k]));
+                rc[k] = (uint32_t)(l[k] < 0 ? 0 : (l[k] > lim ? lim : l[k]));
+            }
+        }
+        m.real[e] = rc[k];
+        m.phys[e] = pc[k];
+    }
+    if (err) atomicOr(&m.err, err);
+    __syncthreads();
+
+    // rows: a row needs a sequence and must fit S (its padded sum, saturated
+    // at S+1, says so exactly); its tail pad is folded into its last
+    // sequence.  Short rows take one thread each, longer rows one wave each
+    // (kRowsAtOnce rows side by side per wave, so that their LDS reads and DPP
+    // chains would overlap; one is fastest with 16 waves).
+    if (P <= 32u) {
+        for (uint32_t r = threadIdx.x; r < B; r += kSmallThreads) {
+            uint32_t sum = 0, last = 0, last_pd = 0;
+            int32_t mx = 0;
+            for (uint32_t e = r * P; e < r * P + P; ++e) {
+                const uint32_t rl = m.real[e];
+                if (rl != kNoSeq) {
+                    last_pd = m.phys[e];
+                    sum = sat_add(sum, last_pd, sat);
+                    last = e + 1u;
+                    mx = max(mx, (int32_t)rl);
+                }
+            }
+            uint32_t e2 = 0;
+            if (last == 0) e2 |= PSQ_DATA_EMPTY_ROW;
+            if (sum > S) e2 |= PSQ_DATA_ROW_OVERFLOW;
+            if (e2) atomicOr(&m.err, e2);
+            if (last) {
+                m.phys[last - 1u] = last_pd + (S - sum);
+                atomicMax(&m.g_last[r / Bc], last);
+            }
+            if (mx) atomicMax(&m.g_max[r / Bc], mx);
+        }
+    } else {
+        constexpr int kRowsAtOnce = 1;
+        uint32_t e2 = 0;
+        for (uint32_t r0 = (uint32_t)w * kRowsAtOnce; r0 < B; r0 += kSmallWaves * kRowsAtOnce) {
+            uint32_t sum[kRowsAtOnce], last[kRowsAtOnce], my_e[kRowsAtOnce], my_pd[kRowsAtOnce];
+            int32_t mx[kRowsAtOnce];
+#pragma unroll
+            for (int q = 0; q < kRowsAtOnce; ++q) {
+                const uint32_t r = r0 + (uint32_t)q;
+                sum[q] = 0;
+                last[q] = 0;
+                my_e[q] = kNoSeq;   // + 1 wraps to 0: never a row's last
+                my_pd[q] = 0;
+                mx[q] = 0;
+                if (r < B) {
+                    for (uint32_t j = (uint32_t)lane; j < P; j += kWave) {
+                        const uint32_t e = r * P + j;
+                        const uint32_t rl = m.real[e];
+                        if (rl != kNoSeq) {
+                            const uint32_t pd = m.phys[e];
+                            sum[q] = sat_add(sum[q], pd, sat);
+                            last[q] = e + 1u;
+                            my_e[q] = e;
+                            my_pd[q] = pd;
+                            mx[q] = max(mx[q], (int32_t)rl);
+                        }
+                    }
+                }
+            }
+            // saturating wave sums and wave maxima over DPP (lane 63 holds them)
+#pragma unroll
+            for (int q = 0; q < kRowsAtOnce; ++q) {
+                uint32_t x = sum[q];
+                x = sat_add(x, (uint32_t)dpp0<0x111>((int)x), sat);
+                x = sat_add(x, (uint32_t)dpp0<0x112>((int)x), sat);
+                x = sat_add(x, (uint32_t)dpp0<0x114>((int)x), sat);
+                x = sat_add(x, (uint32_t)dpp0<0x118>((int)x), sat);
+                x = sat_add(x, (uint32_t)dpp0<0x142, 0xa>((int)x), sat);
+                x = sat_add(x, (uint32_t)dpp0<0x143, 0xc>((int)x), sat);
+                sum[q] = (uint32_t)read_lane((int)x, kWave - 1);
+                last[q] = (uint32_t)read_lane(wave_incl_max((int)last[q]), kWave - 1);
+                mx[q] = read_lane(wave_incl_max(mx[q]), kWave - 1);
+            }
+#pragma unroll
+            for (int q = 0; q < kRowsAtOnce; ++q) {
+                const uint32_t r = r0 + (uint32_t)q;
+                if (r < B) {   // uniform
+                    if (last[q] == 0) e2 |= PSQ_DATA_EMPTY_ROW;
+                    if (sum[q] > S) e2 |= PSQ_DATA_ROW_OVERFLOW;
+                    // the lane holding the row's last sequence folds it
+                    if (last[q] && my_e[q] + 1u == last[q])
+                        m.phys[my_e[q]] = my_pd[q] + (S - sum[q]);
+                    if (lane == 0) {
+                        if (last[q]) atomicMax(&m.g_last[r / Bc], last[q]);
+                        if (mx[q]) atomicMax(&m.g_max[r / Bc], mx[q]);
+                    }
+                }
+            }
+        }
+        if (lane == 0 && e2) atomicOr(&m.err, e2);
+    }
+    __syncthreads();
+
+    // the fold changed some physical lengths: take them back from LDS
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) pc[k] = m.phys[e0 + (uint32_t)k];
+
+    // one block-wide exclusive scan of (count, real, physical) over the
+    // flattened table (wrapping sums: exact whenever no status bit is set)
+    uint32_t cnt = 0, rsum = 0, psum = 0;
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        if (rc[k] != kNoSeq) {
+            cnt += 1;
+            rsum += rc[k];
+            psum += pc[k];
+        }
+    }
+    uint32_t ex[3], tot[3];
+    block_scan3<kSmallWaves>(m.wsum, cnt, rsum, psum, ex, tot);
+    // group of entry e0, and the first entry of the next group
+    const uint32_t g0 = min(e0, E - 1u) / Eg;
+    {
+        uint32_t c = ex[0], rr = ex[1], pp = ex[2];
+        uint32_t g = g0, g_end = (g0 + 1u) * Eg;
+#pragma unroll
+        for (int k = 0; k < kSmallPer; ++k) {
+            const uint32_t e = e0 + (uint32_t)k;
+            if (e < E) {
+                while (e >= g_end) {
+                    ++g;
+                    g_end += Eg;
+                }
+                if (e == g_end - Eg) {
+                    m.g_base[0][g] = c;
+                    m.g_base[1][g] = rr;
+                    m.g_base[2][g] = pp;
+                }
+                if (rc[k] != kNoSeq) {
+                    // every sequence but its group's last must be tight
+                    if (e + 1u != m.g_last[g] && rc[k] != pc[k]) m.g_flag[g] = 1u;
+                    c += 1;
+                    rr += rc[k];
+                    pp += pc[k];
+                }
+            }
+        }
+        if (threadIdx.x == 0) {
+            m.g_base[0][G] = tot[0];
+            m.g_base[1][G] = tot[1];
+            m.g_base[2][G] = tot[2];
+        }
+    }
+    __syncthreads();
+
+    const uint32_t st = m.err;
+    uint32_t width = 0;   // longest group's boundary count, n + 1
+    if (st == 0)
+        for (uint32_t g = 0; g < G; ++g) width = max(width, m.g_base[0][g + 1] - m.g_base[0][g] + 1u);
+    const uint32_t stride = G > 1 ? width : 0u;   // output row of group g starts at g * stride
+
+    // boundaries of every sequence (group-relative), then each group's close
+    if (st == 0) {
+        uint32_t c = ex[0], rr = ex[1], pp = ex[2];
+        uint32_t g = g0, g_end = (g0 + 1u) * Eg;
+#pragma unroll
+        for (int k = 0; k < kSmallPer; ++k) {
+            const uint32_t e = e0 + (uint32_t)k;
+            if (rc[k] != kNoSeq) {
+                while (e >= g_end) {
+                    ++g;
+                    g_end += Eg;
+                }
+                const uint32_t at = g * stride + (c - m.g_base[0][g]);
+                cu[at] = (int32_t)(rr - m.g_base[1][g]);
+                if (cp) cp[at] = (int32_t)(pp - m.g_base[2][g]);
+                c += 1;
+                rr += rc[k];
+                pp += pc[k];
+            }
+        }
+    }
+    for (uint32_t g = threadIdx.x; g < G; g += kSmallThreads) {
+        if (st == 0) {
+            const uint32_t n = m.g_base[0][g + 1] - m.g_base[0][g];
+            const uint32_t total = m.g_base[1][g + 1] - m.g_base[1][g];
+            const bool disagree = m.g_flag[g] != 0;
+            const bool absorbed = !disagree && total < Tc;
+            int32_t mx = m.g_max[g];
+            // without a status bit every row, hence every group, holds a sequence
+            const uint32_t last = m.g_last[g];
+            if (absorbed && last) mx = max(mx, (int32_t)(Tc - (total - m.real[last - 1u])));
+            const uint32_t base = g * stride;
+            cu[base + n] = (int32_t)(absorbed ? Tc : total);
+            if (cp) cp[base + n] = (int32_t)Tc;
+            for (uint32_t j = n + 1u; j < stride; ++j) {
+                cu[base + j] = (int32_t)pv;
+                if (cp) cp[base + j] = (int32_t)pv;
+            }
+            args.num_seqs[g] = (int32_t)n;
+            args.max_seqlen[g] = mx;
+            args.pad_between[g] = disagree ? 1 : 0;
+        } else {
+            args.num_seqs[g] = 0;
+            args.max_seqlen[g] = 0;
+            args.pad_between[g] = 0;
+        }
+    }
+    if (threadIdx.x == 0) {
+        *args.status = (int32_t)st;
+        if (args.cu_width) *args.cu_width = (int32_t)(st == 0 ? width : 0u);
+    }
+}
+
+// 4 mask bits (1 = padding) -> 4 bytes of 0/1
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+    return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+}
+
+// One (row, chunk of kSmallSlots) of the mask.  Each wave owns 1024 slots of
+// the chunk and each lane 16 consecutive slots of it.  The wave reads its row's table 64
+// entries at a time (one per lane), turns the padded lengths into physical
+// starts with a saturating DPP scan, and visits, through a ballot, only the
+// sequences whose tokens meet the wave's slots; a lane marks its slots that
+// fall in [start, start + real) and stores its 16 mask bytes at once.  No
+// LDS and no barrier.
+template <typename TL>
+__device__ __forceinline__ void thd_small_mask(const ThdArgs<TL> &args, uint32_t wg,
+                                               uint32_t n_mchunks) {
+    const uint32_t P = args.P, S = args.S;
+    const uint32_t r = wg / n_mchunks, c = wg % n_mchunks;
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    constexpr uint32_t kWaveSlots = kSmallSlots / kSmallWaves;
+    const uint32_t lo = c * kSmallSlots + (uint32_t)w * kWaveSlots;
+    const uint32_t hi = min(S, lo + kWaveSlots);
+    if (lo >= hi) return;   // wave-uniform
+    const uint32_t sat = S + 1u;
+    const int64_t pv = args.pad_value;
+    const TL *__restrict__ L = args.L + (uint64_t)r * P;
+    const TL *__restrict__ Lq = (args.Lp ? args.Lp : args.L) + (uint64_t)r * P;
+    const uint32_t a = lo + 16u * (uint32_t)lane;   // this lane's first slot
+    uint32_t tok = 0;                               // bit i: slot a + i holds a token
+    uint32_t run = 0;                               // padded sum of earlier batches (saturated)
+    for (uint32_t j0 = 0; j0 < P && run < hi; j0 += kWave) {   // uniform
+        const uint32_t j = j0 + (uint32_t)lane;
+        uint32_t rl = 0, pd = 0;
+        if (j < P) {
+            const int64_t x = (int64_t)L[j];
+            const int64_t y = (int64_t)Lq[j];
+            if (x != pv) {
+                const int64_t lim = (int64_t)sat;
+                pd = (uint32_t)(y < 0 ? 0 : (y > lim ? lim : y));
+                rl = (uint32_t)(x < 0 ? 0 : (x > lim ? lim : x));
+            }
+        }
+        uint32_t incl = pd;
+        incl = sat_add(incl, (uint32_t)dpp0<0x111>((int)incl), sat);
+        incl = sat_add(incl, (uint32_t)dpp0<0x112>((int)incl), sat);
+        incl = sat_add(incl, (uint32_t)dpp0<0x114>((int)incl), sat);
+        incl = sat_add(incl, (uint32_t)dpp0<0x118>((int)incl), sat);
+        incl = sat_add(incl, (uint32_t)dpp0<0x142, 0xa>((int)incl), sat);
+        incl = sat_add(incl, (uint32_t)dpp0<0x143, 0xc>((int)incl), sat);
+        const uint32_t st = sat_add(run, (uint32_t)wave_shr1((int)incl, 0), sat);
+        const uint32_t en = sat_add(st, rl, sat);   // tokens of entry j: [st, en)
+        run = sat_add(run, (uint32_t)read_lane((int)incl, kWave - 1), sat);
+        uint64_t meet = __ballot(en > st && st < hi && en > lo);
+        while (meet) {   // uniform
+            const int q = __builtin_ctzll(meet);
+            meet &= meet - 1ull;
+            const uint32_t s0 = (uint32_t)read_lane((int)st, q);
+            const uint32_t s1 = (uint32_t)read_lane((int)en, q);
+            const uint32_t b0 = max(s0, a), b1 = min(s1, a + 16u);
+            if (b0 < b1) tok |= ((1u << (b1 - a)) - 1u) & ~((1u << (b0 - a)) - 1u);
+        }
+    }
+    uint8_t *__restrict__ out = args.mask + (uint64_t)r * S;
+    const uint32_t pad = ~tok & 0xffffu;   // 1 = padding
+    if (args.vec_mask && ((uint64_t)r * S) % 16 == 0 && a + 16u <= hi) {
+        *(u32x4 *)(out + a) = u32x4{spread4(pad), spread4(pad >> 4), spread4(pad >> 8),
+                                    spread4(pad >> 12)};
+    } else {
+        for (uint32_t i = 0; i < 16u && a + i < hi; ++i) out[a + i] = (uint8_t)((pad >> i) & 1u);
+    }
+}
+
+template <typename TL>
+__global__ __launch_bounds__(kSmallThreads) void k_thd_small(ThdArgs<TL> a, uint32_t n_mask,
+                                                             uint32_t n_mchunks,
+                                                             CopyBatch batch) {
+    __shared__ SmallMeta meta;
+    if (blockIdx.x == 0)
+        thd_small_meta<TL>(a, meta);
+    else if (blockIdx.x <= n_mask)
+        thd_small_mask<TL>(a, blockIdx.x - 1u, n_mchunks);
+    else
+        copy_group<kSmallThreads, u32x4, true>(batch, (int64_t)blockIdx.x - 1 - n_mask);
+}
+
+template <typename TL>
+bool small_tables(const ThdArgs<TL> &a) {
+    return a.B >= 1 && a.P >= 1 && a.S >= 1 && (uint64_t)a.B * a.P <= kSmallEntries &&
+           a.G <= kSmallGroups;
+}
+
 template <typename TL>
 hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, int n_copies,
                         hipStream_t stream) {
     CopyPlan plan;
+    if (small_tables(a)) {
+        plan_copies(copies, n_copies, &plan, kSmallThreads);
+        const uint32_t n_mchunks = (a.S + kSmallSlots - 1u) / kSmallSlots;
+        const uint32_t n_mask = a.mask ? a.B * n_mchunks : 0u;
+        const uint64_t grid = 1ull + n_mask + (uint64_t)plan.groups[0];
+        hipLaunchKernelGGL(k_thd_small<TL>, dim3((uint32_t)grid), dim3(kSmallThreads), 0, stream,
+                           a, n_mask, n_mchunks, plan.batch[0]);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_copy_plan(plan, 1, stream);
+    }
     plan_copies(copies, n_copies, &plan, kThreads);
     if (plan.groups[0] > 0) {
         const uint64_t grid = (uint64_t)n_meta + (uint64_t)plan.groups[0];
