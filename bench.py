@@ -19,6 +19,11 @@ Prints one JSON line.  ``roofline`` relates the algorithmic bytes of one
 call (each input read once, each output written once) to the call's
 average duration from HIP events on the launch stream; ``cpu_baseline`` is
 the CPU oracle on a bounded sample of the same workload, on one host core.
+Each per-config line gives the time of an isolated call (HIP events around
+it; for the latency-bound workloads this includes the launch) and, for the
+workloads timed without a cache flush, ``us_back_to_back``: the time per
+call of a stream of calls enqueued without waiting, so that each launch
+overlaps the previous call.
 """
 from __future__ import annotations
 
@@ -402,6 +407,21 @@ def setup_rect(torch, psq, lib, synth, dev):
     return call, P * C, algo, info, (rows, rl, order, starts, packed, tm, cu, cp, st, ws)
 
 
+def back_to_back_ms(torch, call, iters):
+    """ms per call of `iters` calls enqueued back to back between one pair of
+    HIP events: the rate of a stream of calls, where each launch overlaps the
+    previous call's execution instead of waiting for the host."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(torch.cuda.current_stream())
+    for _ in range(iters):
+        call()
+    b.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
 def measure(torch, call, iters, flush=None):
     """(mean, min, median) ms of `iters` launches, HIP events on the launch stream."""
     timer = Timer(torch)
@@ -607,8 +627,9 @@ WORKLOAD_OF = {
     "k_copies": "collapse copies",
     "k_pack_rows": "pack_sources: 65536 sources -> 16384-slot packs; trainer_rectangle: "
                    "256 rows -> token-budget bins",
-    "k_thd_tables_copy": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses "
-                         "(whole batch, and split into 4 row groups)",
+    "k_thd_small": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses "
+                   "(whole batch, and split into 4 row groups)",
+    "k_thd_tables_copy": "length tables above 2048 entries, with collapses",
     "k_doc_segments": "doc_map_small [4,64] and doc_map_medium [8,4096]",
     "k_pad_ids": "pad_tail_stream: 131072 int64 ids with a pad tail",
     "k_zero_fill": "workspace zero fill (once per workspace)",
@@ -771,10 +792,12 @@ def main():
                 c_call()
             m, mn, med = measure(torch, c_call, args.per_config_iters,
                                  flush if do_flush else None)
+            b2b = None if do_flush else back_to_back_ms(torch, c_call, args.per_config_iters)
             parity = check_outputs(torch, name, c_keep) if not args.no_check else "not checked"
             per[name] = dict(c_info, **{
                 "us_mean": round(m * 1e3, 2), "us_median": round(med * 1e3, 2),
                 "us_min": round(mn * 1e3, 2),
+                "us_back_to_back": None if b2b is None else round(b2b * 1e3, 2),
                 "gtok_s": round(c_tok / (m * 1e-3) / 1e9, 4), "tokens_per_call": c_tok,
                 "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m, workload_traffic(name)),
                 "parity": parity})
