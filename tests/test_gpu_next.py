@@ -138,6 +138,24 @@ def test_split_fuzz(dev, B, P, S, G, mode):
         check_split(dev, L, Lp, S, G, torch.int32 if mode == "int32" else torch.int64)
 
 
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("wide", [False, True])
+def test_split_fault_fuzz(dev, seed, wide):
+    # the faults of the table fuzz, on row groups: status words and (when
+    # clean) the stacked outputs must match the oracle on both kernels
+    from test_gpu_parity import corrupt_tables
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.integers(1, 5))
+    B, P, S = G * int(rng.integers(1, 4)), int(rng.integers(1, 7)), int(rng.integers(4, 48))
+    L, Lp = rand_tables(rng, B, P, S, 4)
+    if seed % 2:
+        L, Lp = corrupt_tables(rng, L, Lp, S, int(rng.integers(1, 3)))
+    if wide:
+        extra = np.full((B, 2100), V)
+        L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
+    check_split(dev, L, Lp, S, G)
+
+
 def test_split_hand_ragged(dev):
     check_split(dev, np.array([[2, 3, 1], [1, V, V]]), np.array([[2, 3, 1], [1, V, V]]), 8, 2)
 

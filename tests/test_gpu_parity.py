@@ -290,6 +290,47 @@ def test_thd_fuzz(dev, B, P, S, mode):
         check_thd(dev, L, Lp, S, torch.int32 if mode == "int32" else torch.int64)
 
 
+def corrupt_tables(rng, L, Lp, S, n_bad):
+    """Plant n_bad random faults in copies of valid tables: a sentinel in one
+    table only, a negative length, real > padded, a row overflow, an emptied
+    row, or a length far above S."""
+    L, Lp = L.copy(), Lp.copy()
+    B, P = L.shape
+    for _ in range(n_bad):
+        r, j = int(rng.integers(B)), int(rng.integers(P))
+        kind = int(rng.integers(6))
+        if kind == 0:
+            (L if rng.random() < 0.5 else Lp)[r, j] = V
+        elif kind == 1:
+            L[r, j], Lp[r, j] = -int(rng.integers(1, 5)), max(int(Lp[r, j]), 0)
+        elif kind == 2:
+            L[r, j] = max(int(Lp[r, j]), 0) + int(rng.integers(1, 5))
+            Lp[r, j] = max(int(Lp[r, j]), 0)
+        elif kind == 3:
+            L[r, j], Lp[r, j] = 1, S
+        elif kind == 4:
+            L[r, :], Lp[r, :] = V, V
+        else:
+            L[r, j], Lp[r, j] = 1, 2**40
+    return L, Lp
+
+
+# every fault, alone or combined, must give the oracle's status word exactly,
+# on the single-workgroup kernel and (with sentinel columns) the multi-workgroup one
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("wide", [False, True])
+def test_thd_fault_fuzz(dev, seed, wide):
+    rng = np.random.default_rng(1000 + seed)
+    B, P, S = int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.integers(4, 64))
+    L, Lp = rand_tables(rng, B, P, S, 4)
+    L, Lp = corrupt_tables(rng, L, Lp, S, int(rng.integers(1, 4)))
+    if wide:
+        extra = np.full((B, 2100), V)
+        L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
+    check_thd(dev, L, Lp, S)
+    check_thd(dev, L, Lp, S, torch.int32 if np.abs(np.concatenate([L, Lp])).max() < 2**31 else torch.int64)
+
+
 def test_thd_full_rows_absorb(dev):
     # every row fully tight except the very last sequence: absorption fires
     L = np.array([[100, 28], [64, 50]])
