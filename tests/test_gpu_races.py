@@ -1,0 +1,199 @@
+"""Race tests: the kernels with cross-workgroup protocols, run on the
+race-test build of the library (``libpsq_jitter.so``, built with PSQ_JITTER).
+
+In that build every wave sleeps a pseudo-random time, drawn afresh on each
+call, before each protocol step: claiming a tile ticket, publishing a
+look-back descriptor, looking back, and counting itself finished.  The
+orders in which workgroups reach those steps are therefore shuffled from
+call to call.  Each case runs repeatedly on the same inputs and every run
+must equal the CPU oracle exactly and leave the workspace zero-filled.
+
+The kernels covered: the document-map tiles (ticket, look-back, completion
+count), the multi-workgroup length-table kernel with and without row groups
+(ticket, look-back over rows, completion count), the squeeze (completion
+word) and the pad-id mask (completion count).  The single-workgroup table
+kernel has no cross-workgroup step.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from varlen_attention_metadata_amd import _build, _lib
+
+pytestmark = pytest.mark.gpu
+V = -1000
+REPEATS = 6
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def jl():
+    return _lib.open_library(_build.JITTER_LIB)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _workspace(dev, nbytes):
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+def _assert_zero(ws):
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0, "workspace not left zero-filled"
+
+
+@pytest.mark.parametrize("shape", [(8, 4096), (32, 32768), (3, 100003)])
+def test_doc_map_tiles_under_jitter(jl, dev, shape):
+    B, S = shape
+    doc_np = synth.stage_embedding(5, B, S)["doc_ids"] if S == 32768 else \
+        synth.doc_map_medium(2, B, S)
+    ref = oracle.doc_segments(doc_np)
+    d = torch.from_numpy(doc_np).to(dev)
+    ws = _workspace(dev, jl.psq_params_from_doc_ids_workspace(B, S))
+    for rep in range(REPEATS):
+        say(f"jitter doc map {shape} run {rep}")
+        cu = torch.full((B * S + 1,), -7, dtype=torch.int32, device=dev)
+        mask = torch.full((B * S,), 7, dtype=torch.uint8, device=dev)
+        scal = torch.full((3,), -7, dtype=torch.int32, device=dev)
+        sp = scal.data_ptr()
+        assert jl.psq_params_from_doc_ids(d.data_ptr(), _lib.I32, B, S, cu.data_ptr(), sp,
+                                          sp + 4, mask.data_ptr(), sp + 8, ws.data_ptr(),
+                                          ws.numel(), _stream(dev)) == 0
+        n, mx, st = scal.cpu().tolist()
+        assert st == 0
+        assert n == ref["num_segments"] and mx == ref["max_seqlen"]
+        assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
+        assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
+        _assert_zero(ws)
+
+
+def _tables(seed, B, P, S):
+    rng = np.random.default_rng(seed)
+    L = np.full((B, P), V, dtype=np.int64)
+    Lp = np.full((B, P), V, dtype=np.int64)
+    for r in range(B):
+        used = 0
+        for j in range(int(rng.integers(1, P + 1))):
+            real = int(rng.integers(0, 12))
+            padded = -(-real // 4) * 4 + 4 * int(rng.integers(0, 2))
+            if used + padded > S:
+                break
+            L[r, j], Lp[r, j] = real, padded
+            used += padded
+        if not (L[r] != V).any():
+            L[r, 0], Lp[r, 0] = 0, 0
+    return L, Lp
+
+
+# all above the single-workgroup table size, so the multi-workgroup kernel runs
+@pytest.mark.parametrize("B,P,S,G", [(600, 4, 64, 1), (40, 64, 5000, 1), (600, 4, 64, 300),
+                                     (96, 32, 300, 8)])
+def test_tables_under_jitter(jl, dev, B, P, S, G):
+    L, Lp = _tables(B * 31 + P, B, P, S)
+    ref = oracle.split_thd(L, Lp, S, G) if G > 1 else oracle.thd_tables(L, Lp, S)
+    assert ref["status"] == 0
+    tL, tLp = torch.from_numpy(L).to(dev), torch.from_numpy(Lp).to(dev)
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, tL.data_ptr(), tLp.data_ptr(), _lib.I64, P, V)
+    Bc = B // G
+    cap = G * (Bc * P + 1)
+    ws = _workspace(dev, jl.psq_split_thd_workspace(ctypes.byref(lay), B, S, G))
+    arr, n_c = _lib.make_copies([])
+    for rep in range(REPEATS):
+        say(f"jitter tables B={B} P={P} S={S} G={G} run {rep}")
+        cu = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+        cp = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+        mask = torch.full((B * S,), 7, dtype=torch.uint8, device=dev)
+        per = torch.full((3, G), -7, dtype=torch.int32, device=dev)
+        scal = torch.full((2,), -7, dtype=torch.int32, device=dev)
+        pp, sp = per.data_ptr(), scal.data_ptr()
+        assert jl.psq_split_thd(ctypes.byref(lay), B, S, G, cu.data_ptr(), cp.data_ptr(), sp,
+                                pp, pp + 4 * G, pp + 8 * G, mask.data_ptr(), arr, n_c, sp + 4,
+                                ws.data_ptr(), ws.numel(), _stream(dev)) == 0
+        width, st = scal.cpu().tolist()
+        assert st == 0
+        got_mask = mask.cpu().numpy()
+        if G == 1:
+            n = int(per[0, 0].item())
+            assert n == ref["num_seqs"]
+            assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
+            assert np.array_equal(cp[: n + 1].cpu().numpy(), ref["cu_seqlens_padded"])
+            assert int(per[1, 0].item()) == ref["max_seqlen"]
+            assert int(per[2, 0].item()) == ref["pad_between_seqs"]
+            assert np.array_equal(got_mask, ref["padding_mask"])
+        else:
+            assert width == ref["cu_seqlens"].shape[1]
+            assert np.array_equal(cu[: G * width].view(G, width).cpu().numpy(), ref["cu_seqlens"])
+            assert np.array_equal(cp[: G * width].view(G, width).cpu().numpy(),
+                                  ref["cu_seqlens_padded"])
+            for i, key in enumerate(("num_seqs", "max_seqlen", "pad_between_seqs")):
+                assert np.array_equal(per[i].cpu().numpy(), ref[key]), key
+            assert np.array_equal(got_mask.reshape(G, Bc * S), ref["padding_mask"])
+        _assert_zero(ws)
+
+
+def test_pack_under_jitter(jl, dev):
+    w = synth.pack_sources(4, N=4096)
+    C, q = w["capacity"], w["q"]
+    src, off, rl, ps = w["src"], w["src_off"], w["real_len"], w["pack_start"]
+    N, P = rl.size, ps.size - 1
+    ref = oracle.pack(src, off, rl, q, ps, C, fold=True)
+    assert ref["status"] == 0
+    t = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (src, off, rl, ps)]
+    ws = _workspace(dev, jl.psq_pack_rows_workspace(N, P, C))
+    for rep in range(REPEATS):
+        say(f"jitter pack N={N} P={P} run {rep}")
+        packed = torch.full((P, C), -5, dtype=torch.int64, device=dev)
+        tm = torch.full((P, C), 9, dtype=torch.uint8, device=dev)
+        cu = torch.full((N + P,), -7, dtype=torch.int32, device=dev)
+        cp = torch.full((N + P,), -7, dtype=torch.int32, device=dev)
+        st = torch.full((1,), -7, dtype=torch.int32, device=dev)
+        assert jl.psq_pack_rows(t[0].data_ptr(), src.size, t[1].data_ptr(), t[2].data_ptr(), N,
+                                q, None, t[3].data_ptr(), P, C, 1, 0, packed.data_ptr(),
+                                tm.data_ptr(), cu.data_ptr(), cp.data_ptr(), st.data_ptr(),
+                                ws.data_ptr(), ws.numel(), _stream(dev)) == 0
+        assert int(st.item()) == 0
+        assert np.array_equal(packed.cpu().numpy(), ref["packed"])
+        assert np.array_equal(tm.cpu().numpy(), ref["token_mask"])
+        assert np.array_equal(cu.cpu().numpy(), ref["cu_seqlens"])
+        assert np.array_equal(cp.cpu().numpy(), ref["cu_seqlens_padded"])
+        _assert_zero(ws)
+
+
+@pytest.mark.parametrize("kind", ["tail", "collide"])
+def test_pad_ids_under_jitter(jl, dev, kind):
+    w = synth.pad_tail_stream(7, T=1 << 20)
+    ids = w["input_ids"].copy()
+    pad = w["pad_id"]
+    if kind == "collide":
+        ids[1000] = pad
+    ref = oracle.pad_mask_from_ids(ids, pad)
+    t = torch.from_numpy(ids).to(dev)
+    T = ids.size
+    ws = _workspace(dev, jl.psq_padding_mask_from_token_ids_workspace(T))
+    for rep in range(REPEATS):
+        say(f"jitter pad ids {kind} run {rep}")
+        mask = torch.full((T,), 7, dtype=torch.uint8, device=dev)
+        scal = torch.full((2,), -7, dtype=torch.int32, device=dev)
+        sp = scal.data_ptr()
+        assert jl.psq_padding_mask_from_token_ids(t.data_ptr(), _lib.I64, T, pad,
+                                                  mask.data_ptr(), sp, sp + 4, ws.data_ptr(),
+                                                  ws.numel(), _stream(dev)) == 0
+        nc, st = scal.cpu().tolist()
+        assert st == ref["status"]
+        assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
+        assert nc == ref["num_content"]
+        _assert_zero(ws)

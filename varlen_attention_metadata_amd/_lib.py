@@ -67,13 +67,19 @@ def header_functions() -> list:
 def load():
     """Load ``libpsq.so``; raises if it is missing (build it first)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+    if _lib is None:
+        _lib = open_library(LIB_PATH)
+    return _lib
+
+
+def open_library(path: str):
+    """A ctypes handle on a build of the library at ``path`` (``libpsq.so``,
+    or the race-test build ``libpsq_jitter.so``) with every prototype set."""
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build the HIP library first "
+            f"{path} is missing: build the HIP library first "
             "(python -c 'import __graft_entry__ as g; g.build()')")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     ci = ctypes.c_int
     lib.psq_status_string.restype = ctypes.c_char_p
@@ -106,7 +112,6 @@ def load():
     lib.psq_pack_rows.restype = ci
     lib.psq_pack_rows.argtypes = [vp, i64, vp, vp, i64, i32, vp, vp, i64, i32, ci, i64,
                                   vp, vp, vp, vp, vp, vp, sz, vp]
-    _lib = lib
     return lib
 
 

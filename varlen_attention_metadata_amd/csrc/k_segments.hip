@@ -243,6 +243,7 @@ __device__ __forceinline__ void doc_segments_body(
             if (tile == 0) {
                 if (lane == 0 && !solo) st_relaxed(desc, desc_pack(kDescIncl, agg_c, agg_l));
             } else {
+                jitter(5);
                 if (lane == 0) st_relaxed(desc + tile, desc_pack(kDescAgg, agg_c, agg_l));
                 uint32_t ex_a, ex_b;
                 bool timed_out;

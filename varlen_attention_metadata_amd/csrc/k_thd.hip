@@ -388,6 +388,7 @@ __device__ __forceinline__ void thd_tables_body(const ThdArgs<TL> &args, uint32_
                 if (rg == 0) {
                     if (lane == 0) st_relaxed(desc + r, desc_pack(kDescIncl, count, realsum));
                 } else {
+                    jitter(6);
                     if (lane == 0) st_relaxed(desc + r, desc_pack(kDescAgg, count, realsum));
                     bool timed_out;
                     lookback<true>(desc, r, &ex_a, &ex_b, &timed_out);

@@ -36,6 +36,28 @@ __device__ __forceinline__ void store_stream(int64_t *p, int64_t v) {
 }
 
 // ---------------------------------------------------------------------------
+// Progress jitter for the race tests.  In the PSQ_JITTER build of the library
+// (libpsq_jitter.so) a wave sleeps a pseudo-random time, up to about 15 us, at
+// each marked step of a cross-workgroup protocol: claiming a tile, publishing
+// a look-back descriptor, looking back, counting itself finished.  The orders
+// in which workgroups take those steps then change from call to call, and
+// the tests check that the results do not.  In the normal build it is empty.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void jitter(uint32_t site) {
+#ifdef PSQ_JITTER
+    uint32_t h = (uint32_t)wall_clock64() ^ (blockIdx.x * 0x9e3779b1u) ^ (site * 0x85ebca77u);
+    h ^= h >> 16;
+    h *= 0x7feb352du;
+    h ^= h >> 15;
+    h *= 0x846ca68bu;
+    h ^= h >> 16;
+    for (uint32_t i = 0, n = h & 63u; i < n; ++i) __builtin_amdgcn_s_sleep(8);
+#else
+    (void)site;
+#endif
+}
+
+// ---------------------------------------------------------------------------
 // Workspace.  The first 256 bytes hold the header; per-tile descriptors
 // follow.  Every kernel that uses it leaves it zero-filled on completion (the
 // last workgroup to finish clears what the call used), so a workspace needs
@@ -79,8 +101,10 @@ __device__ __forceinline__ void max_relaxed(int32_t *p, int32_t v) {
 // Claim a tile id: workgroups that got a smaller ticket were dispatched
 // earlier, so waiting on them always makes progress.
 __device__ __forceinline__ uint32_t claim_tile(WsHeader *ws, uint32_t *lds_slot) {
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
+        jitter(1);
         *lds_slot = fetch_add_relaxed(&ws->ticket, 1u);
+    }
     __syncthreads();
     return *lds_slot;
 }
@@ -92,6 +116,7 @@ __device__ __forceinline__ bool finish_is_last(WsHeader *ws, uint32_t n_groups,
                                                uint32_t *lds_slot) {
     __syncthreads();
     if (threadIdx.x == 0) {
+        jitter(2);
         uint32_t prev = __hip_atomic_fetch_add(&ws->done, 1u, __ATOMIC_RELEASE,
                                                __HIP_MEMORY_SCOPE_AGENT);
         uint32_t last = (prev == n_groups - 1u);
@@ -113,6 +138,7 @@ __device__ __forceinline__ bool finish_is_last(WsHeader *ws, uint32_t n_groups,
 // the word.  Called by one thread.
 __device__ __forceinline__ bool finish_status(WsHeader *ws, uint32_t bits, uint32_t n_groups,
                                               uint32_t *final_bits) {
+    jitter(3);
     if (bits)
         __hip_atomic_fetch_or(&ws->fin, (uint64_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t old = __hip_atomic_fetch_add(&ws->fin, 1ull << 32, __ATOMIC_RELAXED,
@@ -192,6 +218,7 @@ __device__ __forceinline__ uint32_t desc_b(uint64_t d) { return (uint32_t)d & 0x
 template <bool kSumB>
 __device__ inline void lookback(const uint64_t *desc, uint32_t tile, uint32_t *out_a,
                                 uint32_t *out_b, bool *timed_out) {
+    jitter(4);
     const int lane = lane_id();
     uint32_t acc_a = 0, acc_b = 0;
     int64_t base = (int64_t)tile - 1;
