@@ -23,7 +23,8 @@ Each per-config line gives the time of an isolated call (HIP events around
 it; for the latency-bound workloads this includes the launch) and, for the
 workloads timed without a cache flush, ``us_back_to_back``: the time per
 call of a stream of calls enqueued without waiting, so that each launch
-overlaps the previous call.
+overlaps the previous call.  ``launch_floor`` times the library's smallest
+launch the same two ways: the floor under the latency-bound workloads.
 """
 from __future__ import annotations
 
@@ -405,6 +406,24 @@ def setup_rect(torch, psq, lib, synth, dev):
     info = {"workload": "trainer_rectangle", "N": N, "W": W, "bins": P, "width": C,
             "pad_to": q, "real_tokens": real}
     return call, P * C, algo, info, (rows, rl, order, starts, packed, tm, cu, cp, st, ws)
+
+
+def launch_floor(torch, lib, dev, iters):
+    """The library's smallest launch (psq_workspace_init of 256 bytes: one
+    one-wave fill workgroup) timed like the latency-bound workloads: the floor
+    under their per-call times."""
+    buf = torch.empty(256, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        lib.psq_workspace_init(buf.data_ptr(), buf.numel(), stream)
+
+    for _ in range(5):
+        call()
+    m, _, med = measure(torch, call, iters)
+    return {"what": "psq_workspace_init of 256 bytes (one fill workgroup) through the ctypes "
+                    "binding", "us_median": round(med * 1e3, 2), "us_mean": round(m * 1e3, 2),
+            "us_back_to_back": round(back_to_back_ms(torch, call, iters) * 1e3, 2)}
 
 
 def back_to_back_ms(torch, call, iters):
@@ -809,6 +828,7 @@ def main():
         result["per_config"] = per
         del flush_buf
         result["copy_ceiling"] = copy_ceiling(torch, dev)
+        result["launch_floor"] = launch_floor(torch, lib, dev, args.per_config_iters)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(torch, keep)
