@@ -23,8 +23,10 @@ Each per-config line gives the time of an isolated call (HIP events around
 it; for the latency-bound workloads this includes the launch) and, for the
 workloads timed without a cache flush, ``us_back_to_back``: the time per
 call of a stream of calls enqueued without waiting, so that each launch
-overlaps the previous call.  ``launch_floor`` times the library's smallest
-launch the same two ways: the floor under the latency-bound workloads.
+overlaps the previous call, and ``us_in_graph``: the time per call of 20
+calls captured in one HIP graph and replayed.  ``launch_floor`` times the
+library's smallest launch the same three ways: the floor under the
+latency-bound workloads.
 """
 from __future__ import annotations
 
@@ -207,7 +209,7 @@ def setup_stage_embedding(torch, psq, lib, synth, dev):
     stream = torch.cuda.current_stream(dev).cuda_stream
     sp = scal.data_ptr()
 
-    def call():
+    def call(stream=stream):
         lib.psq_process_thd(layout, B, S, cu.data_ptr(), cp.data_ptr(), sp, sp + 4, sp + 8,
                             mask.data_ptr(), copies, n_c, sp + 12, ws.data_ptr(), ws.numel(),
                             stream)
@@ -233,7 +235,7 @@ def setup_doc_map(torch, psq, lib, synth, dev, which):
     stream = torch.cuda.current_stream(dev).cuda_stream
     sp = scal.data_ptr()
 
-    def call():
+    def call(stream=stream):
         lib.psq_params_from_doc_ids(doc.data_ptr(), lib.I32, B, S, cu.data_ptr(), sp, sp + 4,
                                     None, sp + 8, ws.data_ptr(), ws.numel(), stream)
 
@@ -264,7 +266,7 @@ def setup_thd(torch, psq, lib, synth, dev):
     stream = torch.cuda.current_stream(dev).cuda_stream
     sp = scal.data_ptr()
 
-    def call():
+    def call(stream=stream):
         lib.psq_process_thd(layout, B, S, cu.data_ptr(), cp.data_ptr(), sp, sp + 4, sp + 8,
                             mask.data_ptr(), copies, n_c, sp + 12, ws.data_ptr(), ws.numel(),
                             stream)
@@ -294,7 +296,7 @@ def setup_pack(torch, psq, lib, synth, dev):
     ws = psq.workspace_for(dev, lib.psq_pack_rows_workspace(N, P, C))
     stream = torch.cuda.current_stream(dev).cuda_stream
 
-    def call():
+    def call(stream=stream):
         lib.psq_pack_rows(src.data_ptr(), src.numel(), off.data_ptr(), rl.data_ptr(), N, q,
                           None, ps.data_ptr(), P, C, 1, 0, packed.data_ptr(), tm.data_ptr(),
                           cu.data_ptr(), cp.data_ptr(), st.data_ptr(), ws.data_ptr(),
@@ -332,7 +334,7 @@ def setup_split(torch, psq, lib, synth, dev, G=4):
     stream = torch.cuda.current_stream(dev).cuda_stream
     pp, sp = per.data_ptr(), scal.data_ptr()
 
-    def call():
+    def call(stream=stream):
         lib.psq_split_thd(layout, B, S, G, cu.data_ptr(), cp.data_ptr(), sp, pp, pp + 4 * G,
                           pp + 8 * G, mask.data_ptr(), copies, n_c, sp + 4, ws.data_ptr(),
                           ws.numel(), stream)
@@ -357,7 +359,7 @@ def setup_padids(torch, psq, lib, synth, dev):
     stream = torch.cuda.current_stream(dev).cuda_stream
     sp = scal.data_ptr()
 
-    def call():
+    def call(stream=stream):
         lib.psq_padding_mask_from_token_ids(ids.data_ptr(), lib.I64, T, w["pad_id"],
                                             mask.data_ptr(), sp, sp + 4, ws.data_ptr(),
                                             ws.numel(), stream)
@@ -393,7 +395,7 @@ def setup_rect(torch, psq, lib, synth, dev):
     ws = psq.workspace_for(dev, lib.psq_pack_rows_workspace(N, P, C))
     stream = torch.cuda.current_stream(dev).cuda_stream
 
-    def call():
+    def call(stream=stream):
         lib.psq_pack_padded_rows(rows.data_ptr(), W, rl.data_ptr(), N, q, order.data_ptr(),
                                  starts.data_ptr(), P, C, 0, 0, packed.data_ptr(), tm.data_ptr(),
                                  cu.data_ptr(), cp.data_ptr(), st.data_ptr(), ws.data_ptr(),
@@ -415,7 +417,7 @@ def launch_floor(torch, lib, dev, iters):
     buf = torch.empty(256, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
 
-    def call():
+    def call(stream=stream):
         lib.psq_workspace_init(buf.data_ptr(), buf.numel(), stream)
 
     for _ in range(5):
@@ -423,7 +425,34 @@ def launch_floor(torch, lib, dev, iters):
     m, _, med = measure(torch, call, iters)
     return {"what": "psq_workspace_init of 256 bytes (one fill workgroup) through the ctypes "
                     "binding", "us_median": round(med * 1e3, 2), "us_mean": round(m * 1e3, 2),
-            "us_back_to_back": round(back_to_back_ms(torch, call, iters) * 1e3, 2)}
+            "us_back_to_back": round(back_to_back_ms(torch, call, iters) * 1e3, 2),
+            "us_in_graph": round(graph_ms(torch, call, 20, 5) * 1e3, 2)}
+
+
+def graph_ms(torch, call, calls_per_graph, replays):
+    """ms per call when `calls_per_graph` calls are captured in one HIP graph
+    and the graph is replayed: the launches are submitted as one graph, so
+    the per-call launch cost of the isolated and back-to-back timings mostly
+    goes away.  The outputs of the last replay are the ones checked against
+    the oracle afterwards."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(calls_per_graph):
+            call(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(torch.cuda.current_stream())
+    for _ in range(replays):
+        g.replay()
+    b.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (replays * calls_per_graph)
+    del g
+    return ms
 
 
 def back_to_back_ms(torch, call, iters):
@@ -577,7 +606,7 @@ def setup_calibration_copy(torch, psq, lib, dev, nbytes=1 << 30):
     stream = torch.cuda.current_stream(dev).cuda_stream
     sp = scal.data_ptr()
 
-    def call():
+    def call(stream=stream):
         lib.psq_process_thd(layout, 1, 1, cu.data_ptr(), None, sp, sp + 4, sp + 8, None, copies,
                             n_c, sp + 12, ws.data_ptr(), ws.numel(), stream)
 
@@ -812,11 +841,13 @@ def main():
             m, mn, med = measure(torch, c_call, args.per_config_iters,
                                  flush if do_flush else None)
             b2b = None if do_flush else back_to_back_ms(torch, c_call, args.per_config_iters)
+            in_graph = None if do_flush else graph_ms(torch, c_call, 20, 5)
             parity = check_outputs(torch, name, c_keep) if not args.no_check else "not checked"
             per[name] = dict(c_info, **{
                 "us_mean": round(m * 1e3, 2), "us_median": round(med * 1e3, 2),
                 "us_min": round(mn * 1e3, 2),
                 "us_back_to_back": None if b2b is None else round(b2b * 1e3, 2),
+                "us_in_graph": None if in_graph is None else round(in_graph * 1e3, 2),
                 "gtok_s": round(c_tok / (m * 1e-3) / 1e9, 4), "tokens_per_call": c_tok,
                 "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m, workload_traffic(name)),
                 "parity": parity})
