@@ -18,6 +18,11 @@
 //   * max_seqlen is the widest step of cu_seqlens after absorption, i.e. the
 //     largest real length, or B*S - cu_seqlens[n-1] when absorption fired.
 //
+// Two kernels.  Tables of at most 2048 entries (and at most 64 row groups)
+// take k_thd_small, further down: one 1024-thread workgroup derives every
+// boundary from the whole table while the others write the mask, with no
+// workgroup waiting on another.  Larger tables take k_thd_tables:
+//
 // Work layout: one 256-thread workgroup per (row, chunk of 4096 slots).
 // Every workgroup re-derives its row's layout from the row's table (a few
 // hundred bytes, read through L2) into LDS and writes its chunk of the mask
