@@ -110,6 +110,11 @@ int64_t orc_doc_segments(const int64_t *doc, int64_t B, int64_t S,
 /*    sequence i owns [cp[i], cp[i]+real_i) as tokens, everything else pads. */
 /*  - without Lp, each sequence reserves exactly its real length.            */
 /*                                                                          */
+/* The page prints no case where a row's padded lengths fall short of S, or  */
+/* where absorption fires: those two readings are parity unpinned by any     */
+/* printed value.  The tests pin them by invariants, hand cases and an       */
+/* independent slot-grid formulation of the same readings.                   */
+/*                                                                          */
 /* cu, cp: room for B*P+1 entries.  mask: B*S bytes.                         */
 /* Returns the status bits; *nseq, *max_seqlen, *pad_between on success.     */
 /* ------------------------------------------------------------------------ */
