@@ -151,7 +151,7 @@ def test_split_fault_fuzz(dev, seed, wide):
     if seed % 2:
         L, Lp = corrupt_tables(rng, L, Lp, S, int(rng.integers(1, 3)))
     if wide:
-        extra = np.full((B, 2100), V)
+        extra = np.full((B, 4200), V)
         L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
     check_split(dev, L, Lp, S, G)
 
@@ -170,14 +170,14 @@ def test_split_error_bits(dev, L, Lp, S, G, wide):
     L, Lp = np.array(L), np.array(Lp)
     if wide:
         # sentinel columns: the same tables, past the single-workgroup size
-        extra = np.full((L.shape[0], 2100), V)
+        extra = np.full((L.shape[0], 4200), V)
         L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
     check_split(dev, L, Lp, S, G)
 
 
-# on either side of the single-workgroup limits (2048 entries, 64 groups)
-@pytest.mark.parametrize("B,P,S,G", [(128, 2, 16, 64), (130, 2, 16, 65), (64, 32, 100, 64),
-                                     (64, 33, 100, 16)])
+# on either side of the single-workgroup limits (4096 entries, 64 groups)
+@pytest.mark.parametrize("B,P,S,G", [(128, 2, 16, 64), (130, 2, 16, 65), (64, 64, 100, 64),
+                                     (64, 65, 100, 16)])
 def test_split_single_workgroup_limits(dev, B, P, S, G):
     rng = np.random.default_rng(B * 7919 + P * 31 + G)
     L, Lp = rand_tables(rng, B, P, S, 4)

@@ -240,14 +240,14 @@ def test_thd_error_bits(dev, L, Lp, S, wide):
     if wide:
         # sentinel columns change nothing but take the table past the
         # single-workgroup size, so the multi-workgroup kernel decides
-        extra = np.full((L.shape[0], 2100), V)
+        extra = np.full((L.shape[0], 4200), V)
         L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
     check_thd(dev, L, Lp, S)
 
 
-# tables on either side of the single-workgroup limit (2048 entries)
-@pytest.mark.parametrize("B,P,S", [(32, 64, 300), (33, 64, 300), (1, 2048, 5000), (1, 2049, 5000),
-                                   (512, 1, 7), (513, 1, 7), (512, 4, 40)])
+# tables on either side of the single-workgroup limit (4096 entries)
+@pytest.mark.parametrize("B,P,S", [(64, 64, 300), (65, 64, 300), (1, 4096, 5000), (1, 4097, 5000),
+                                   (512, 1, 7), (1024, 4, 40), (1025, 4, 40)])
 def test_thd_single_workgroup_limits(dev, B, P, S):
     rng = np.random.default_rng(B * 10007 + P)
     L, Lp = rand_tables(rng, B, P, S, 4, maxlen=max(1, S // max(1, P // 4)))
@@ -325,7 +325,7 @@ def test_thd_fault_fuzz(dev, seed, wide):
     L, Lp = rand_tables(rng, B, P, S, 4)
     L, Lp = corrupt_tables(rng, L, Lp, S, int(rng.integers(1, 4)))
     if wide:
-        extra = np.full((B, 2100), V)
+        extra = np.full((B, 4200), V)
         L, Lp = np.hstack([L, extra]), np.hstack([Lp, extra])
     check_thd(dev, L, Lp, S)
     check_thd(dev, L, Lp, S, torch.int32 if np.abs(np.concatenate([L, Lp])).max() < 2**31 else torch.int64)

@@ -100,8 +100,8 @@ def _tables(seed, B, P, S):
 
 
 # all above the single-workgroup table size, so the multi-workgroup kernel runs
-@pytest.mark.parametrize("B,P,S,G", [(600, 4, 64, 1), (40, 64, 5000, 1), (600, 4, 64, 300),
-                                     (96, 32, 300, 8)])
+@pytest.mark.parametrize("B,P,S,G", [(1100, 4, 64, 1), (80, 64, 5000, 1), (600, 4, 64, 300),
+                                     (160, 32, 300, 8)])
 def test_tables_under_jitter(jl, dev, B, P, S, G):
     L, Lp = _tables(B * 31 + P, B, P, S)
     ref = oracle.split_thd(L, Lp, S, G) if G > 1 else oracle.thd_tables(L, Lp, S)

@@ -18,7 +18,7 @@
 //   * max_seqlen is the widest step of cu_seqlens after absorption, i.e. the
 //     largest real length, or B*S - cu_seqlens[n-1] when absorption fired.
 //
-// Two kernels.  Tables of at most 2048 entries (and at most 64 row groups)
+// Two kernels.  Tables of at most 4096 entries (and at most 64 row groups)
 // take k_thd_small, further down: one 1024-thread workgroup derives every
 // boundary from the whole table while the others write the mask, with no
 // workgroup waiting on another.  Larger tables take k_thd_tables:
@@ -570,17 +570,20 @@ __global__ __launch_bounds__(kThreads) void k_thd_tables_copy(ThdArgs<TL> a, uin
 // completion count, and the workspace is left untouched.  The status bits
 // are the same predicates as above, evaluated over the whole table at once.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kSmallEntries = 2048;
+constexpr uint32_t kSmallEntries = 4096;
 constexpr uint32_t kSmallGroups = 64;
 constexpr int kSmallThreads = 1024;      // workgroup size of the small-table launch
 constexpr int kSmallWaves = kSmallThreads / kWave;
-constexpr int kSmallPer = (int)(kSmallEntries / kSmallThreads);   // table entries per thread
+// table entries per thread: 4 for tables above 2048 entries, else 2 (with
+// 4, workload-3 tables of 1024 entries took 6.1 instead of 5.1 us per call)
+constexpr int kSmallPerMax = (int)(kSmallEntries / kSmallThreads);
 constexpr uint32_t kSmallSlots = 16384;   // mask slots per workgroup (1024 per wave)
 constexpr uint32_t kNoSeq = 0xffffffffu;   // real[] of an entry holding no sequence
 
+template <int kPer>
 struct SmallMeta {
-    uint32_t real[kSmallEntries];             // clamped real length, or kNoSeq
-    uint32_t phys[kSmallEntries];             // clamped padded length; a row's last folded
+    uint32_t real[kPer * kSmallThreads];      // clamped real length, or kNoSeq
+    uint32_t phys[kPer * kSmallThreads];      // clamped padded length; a row's last folded
     uint32_t g_last[kSmallGroups];            // 1 + the group's last valid entry
     uint32_t g_flag[kSmallGroups];            // an interior boundary departs from its physical one
     int32_t g_max[kSmallGroups];              // largest real length of the group
@@ -595,10 +598,10 @@ __device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat
     return (s < a || s > sat) ? sat : s;
 }
 
-template <typename TL>
-__device__ __forceinline__ void thd_small_meta(const ThdArgs<TL> &args, SmallMeta &m) {
+template <typename TL, int kSmallPer>
+__device__ __forceinline__ void thd_small_meta(const ThdArgs<TL> &args, SmallMeta<kSmallPer> &m) {
     const uint32_t B = args.B, P = args.P, S = args.S, G = args.G, Bc = args.Bc;
-    const uint32_t E = B * P;       // table entries, 1 .. kSmallEntries
+    const uint32_t E = B * P;       // table entries, 1 .. kSmallPer * kSmallThreads
     const uint32_t Eg = Bc * P;     // entries of one group
     const uint32_t Tc = Bc * S;     // tokens of one group (< 2^31)
     const uint32_t sat = S + 1u;    // clamp of a length, and of a row's padded sum
@@ -925,13 +928,13 @@ __device__ __forceinline__ void thd_small_mask(const ThdArgs<TL> &args, uint32_t
     }
 }
 
-template <typename TL>
+template <typename TL, int kPer>
 __global__ __launch_bounds__(kSmallThreads) void k_thd_small(ThdArgs<TL> a, uint32_t n_mask,
                                                              uint32_t n_mchunks,
                                                              CopyBatch batch) {
-    __shared__ SmallMeta meta;
+    __shared__ SmallMeta<kPer> meta;
     if (blockIdx.x == 0)
-        thd_small_meta<TL>(a, meta);
+        thd_small_meta<TL, kPer>(a, meta);
     else if (blockIdx.x <= n_mask)
         thd_small_mask<TL>(a, blockIdx.x - 1u, n_mchunks);
     else
@@ -953,8 +956,10 @@ hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, 
         const uint32_t n_mchunks = (a.S + kSmallSlots - 1u) / kSmallSlots;
         const uint32_t n_mask = a.mask ? a.B * n_mchunks : 0u;
         const uint64_t grid = 1ull + n_mask + (uint64_t)plan.groups[0];
-        hipLaunchKernelGGL(k_thd_small<TL>, dim3((uint32_t)grid), dim3(kSmallThreads), 0, stream,
-                           a, n_mask, n_mchunks, plan.batch[0]);
+        const bool two = (uint64_t)a.B * a.P <= (uint64_t)2 * kSmallThreads;
+        hipLaunchKernelGGL((two ? k_thd_small<TL, 2> : k_thd_small<TL, kSmallPerMax>),
+                           dim3((uint32_t)grid), dim3(kSmallThreads), 0, stream, a, n_mask,
+                           n_mchunks, plan.batch[0]);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_copy_plan(plan, 1, stream);
