@@ -695,6 +695,8 @@ GRID_LABEL = {
     ("k_copies", "537395200"): "stage_embedding step, launch 2: bf16 [32,32768,4096] + int64 "
                                "positions collapse (8 GiB + 8 MiB)",
     ("k_copies", "67108864"): "1 GiB calibration copy (counter runs only)",
+    ("k_zero_fill", "64"): "launch floor: psq_workspace_init of 256 bytes (isolated, back to "
+                           "back and in a HIP graph)",
 }
 
 
