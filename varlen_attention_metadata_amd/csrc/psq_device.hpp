@@ -24,12 +24,15 @@ typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
 // one-wave 1 KiB workgroups streamed at 6.73 TB/s with these stores, against
 // 6.67 TB/s with plain non-temporal stores (nt) and 6.58 TB/s with default
 // stores; the loads stay non-temporal either way.
-// The compiler's hazard tracking does not see inside inline assembly: a store
-// of more than 8 bytes needs one wait state before a VALU write of its data
-// registers, so the 16-byte form carries its own s_nop.
+// The compiler's hazard tracking does not see inside inline assembly: on
+// gfx940 and later a store of more than 8 bytes needs two wait states before
+// a VALU instruction may write its data registers, so the 16-byte form
+// carries its own s_nop 1 (two wait states).  With one wait state a squeeze
+// build whose scheduler placed a register move right after the mask store
+// wrote wrong mask bytes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void store_stream(u32x4 *p, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 0" : : "v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void store_stream(int64_t *p, int64_t v) {
     asm volatile("global_store_dwordx2 %0, %1, off sc1 nt" : : "v"(p), "v"(v) : "memory");
