@@ -9,7 +9,7 @@
 // (cu_seqlens_padded [0,8,36]).
 //
 // Work layout: one single-wave workgroup (64 threads) per (pack, chunk of
-// 1024 slots; 256 when 1024-slot chunks would give fewer than 1024
+// 896 slots; 256 when 896-slot chunks would give fewer than 1024
 // workgroups: a trainer batch of 15 bins then takes 9.5 instead of 11.6 us).  The wave scans its pack's member lengths into LDS (64
 // members per batch; a saturating scan so an overfull pack is detected
 // exactly), marks each member's start slot in a per-chunk owner map and
@@ -44,9 +44,12 @@ namespace {
 constexpr int kThreads = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMembers = kThreads;       // members per LDS batch
-// Slots per workgroup: 1024, or 256 when 1024-slot chunks would leave most of
-// the chip idle (fewer than kFillGroups workgroups).
-constexpr uint32_t kBigSlots = 1024;
+// Slots per workgroup: 896, or 256 when 896-slot chunks would leave most of
+// the chip idle (fewer than kFillGroups workgroups).  896 slots (14 per lane)
+// hold 85 VGPRs, so 6 waves per SIMD stay resident; on MI355X the 65536-source
+// workload took 160 us this way, against 168.5 us at 1024 (93 VGPRs, 5
+// waves), 162-164 us at 640 or 768 and 168 us at 512.
+constexpr uint32_t kBigSlots = 896;
 constexpr uint32_t kSmallSlots = 256;
 constexpr uint64_t kFillGroups = 1024;
 
