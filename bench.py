@@ -62,7 +62,7 @@ CALIB_GRID = str((1 << 30) // 16)
 # shares its grid with the calibration copy's map, and thd_split_4 its grid
 # with thd_tables, so neither is listed)
 WORKLOAD_COUNTERS = {
-    "pack_sources": ("psq::k_pack_rows<1024u> [grid 3590144]", ("k_pack.hip", "psq_device.hpp")),
+    "pack_sources": ("psq::k_pack_rows<896u> [grid 4263296]", ("k_pack.hip", "psq_device.hpp")),
     "trainer_rectangle": ("psq::k_pack_rows<256u> [grid 61440]", ("k_pack.hip", "psq_device.hpp")),
     "pad_tail_stream": ("psq::k_pad_ids<long> [grid 16384]", ("k_padids.hip", "psq_device.hpp")),
     "doc_map_medium": ("psq::k_doc_segments<int> [grid 2048]", ("k_segments.hip", "psq_device.hpp")),
@@ -686,7 +686,7 @@ WORKLOAD_OF = {
 
 # (kernel, grid size in threads) -> workload, for kernels that serve several
 GRID_LABEL = {
-    ("k_pack_rows", "3590144"): "pack_sources: 65536 sources -> 3506 packs of 16384 slots",
+    ("k_pack_rows", "4263296"): "pack_sources: 65536 sources -> 3506 packs of 16384 slots",
     ("k_pack_rows", "61440"): "trainer_rectangle: 256 rows -> 15 token-budget bins",
     ("k_doc_segments", "256"): "doc_map_small [4,64]",
     ("k_doc_segments", "2048"): "doc_map_medium [8,4096]",
