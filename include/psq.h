@@ -44,7 +44,14 @@
  *  - Workspace: query its size with the matching *_workspace() call, then
  *    zero-fill it once (psq_workspace_init, or any zero fill) before its
  *    first use.  Every call leaves the workspace zero-filled again when it
- *    completes, so the zero fill is needed only once per allocation.
+ *    completes, so the zero fill is needed only once per allocation.  A
+ *    query returns 0 for sizes its call would reject (PSQ_ERR_ARG or
+ *    PSQ_ERR_OVERFLOW).
+ *  - Grids: one HIP launch runs fewer than 2^32 threads.  Sizes that would
+ *    need more in a call's metadata launch are PSQ_ERR_OVERFLOW; the limits
+ *    are given with each call and lie far beyond the memory one GPU holds
+ *    for any but degenerate shapes (millions of one-token rows, tens of
+ *    millions of tiny packs).
  *  - Boundary arrays (cu_seqlens*) are int32; entries past the valid count
  *    are left unspecified.  Masks are uint8 0/1 (byte-identical to a torch
  *    bool tensor).
@@ -185,8 +192,10 @@ typedef struct psq_thd_layout {
  *   workspace         psq_process_thd_workspace(layout, B, S) bytes.
  * Host errors: PSQ_ERR_ARG (null pointer, negative size, bad kind/dtype,
  * n_copies out of range, a copy with a null pointer, a stride below its row
- * or overlapping src/dst), PSQ_ERR_OVERFLOW (B*S or B*P+1 >= 2^31, or copies
- * of 2^31 units of one size or more), PSQ_ERR_WORKSPACE.
+ * or overlapping src/dst), PSQ_ERR_OVERFLOW (B*S or B*P+1 >= 2^31, copies
+ * of 2^31 units of one size or more, or, for the table layout above 4096
+ * table entries, 256 * B * ceil(S / 4096) threads plus the copy units of
+ * 16 bytes reaching 2^32), PSQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
 size_t psq_process_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S);
 int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S,
@@ -286,7 +295,8 @@ int psq_padding_mask_from_token_ids(const void *input_ids, int ids_dtype, int64_
  * src_tokens), BAD_LENGTH (real_len < 0).  With pack_order, the members
  * are pack_start[P] entries of it and the CSR holds pack_start[P] + P.
  * Host errors: PSQ_ERR_ARG (null pointer, negative size, pad_to < 1,
- * capacity < 1 or > 2^30), PSQ_ERR_OVERFLOW (N+P >= 2^31),
+ * capacity < 1 or > 2^30), PSQ_ERR_OVERFLOW (N+P >= 2^31, or
+ * P * ceil(capacity / 896) >= 2^26 workgroups of 64 threads),
  * PSQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
 size_t psq_pack_rows_workspace(int64_t N, int64_t P, int32_t capacity);

@@ -54,6 +54,18 @@ def test_workspace_sizes(lib):
     assert four >= one + 2 * 4 * 4 * (4 * 64 + 1)
     assert _lib.psq_split_thd_workspace(lay, 16, 8192, 3) == 0     # 3 does not divide 16
     assert _lib.psq_split_thd_workspace(lay, 16, 8192, 0) == 0
+    # sizes the calls reject as overflowing: the queries return 0 and form no product
+    assert lib.psq_params_from_doc_ids_workspace(1 << 40, 1 << 40) == 0
+    assert lib.psq_params_from_doc_ids_workspace(1 << 16, 1 << 15) == 0   # B*S = 2^31
+    assert lib.psq_params_from_doc_ids_workspace((1 << 16) - 1, 1 << 15) > 0
+    assert _lib.psq_process_thd_workspace(lay, 1 << 40, 1 << 40) == 0
+    huge = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, _lib.I64, 1 << 40)
+    assert _lib.psq_process_thd_workspace(huge, 1 << 40, 0) == 0
+    assert _lib.psq_split_thd_workspace(huge, 1 << 40, 0, 1) == 0
+    assert _lib.psq_split_thd_workspace(lay, 1 << 32, 0, 1 << 32) == 0
+    assert _lib.psq_process_thd_workspace(_lib.make_layout(7), 4, 4) == 0
+    doc = _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=FAKE)
+    assert _lib.psq_process_thd_workspace(doc, 4, 64) == a
 
 
 def _doc(lib, **kw):
@@ -103,6 +115,9 @@ def test_process_thd_validation(lib):
     big = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, _lib.I64, 1 << 20)
     assert _thd(lib, big, B=1 << 11, S=4) == _lib.ERR_OVERFLOW
     assert _thd(lib, lay, B=1 << 20, S=1 << 12) == _lib.ERR_OVERFLOW
+    # S = 0 leaves B free of the row-length bound; B*P must still be bounded first
+    huge = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, None, _lib.I64, 1 << 40)
+    assert _thd(lib, huge, B=1 << 40, S=0) == _lib.ERR_OVERFLOW
     assert _thd(lib, lay) == _lib.ERR_WORKSPACE           # wsb = 0
     assert _thd(lib, lay, ws=None, wsb=1 << 20) == _lib.ERR_WORKSPACE
     # copies: too many, null pointers, overlap, bad stride
@@ -126,6 +141,13 @@ def test_process_thd_validation(lib):
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_OVERFLOW
     arr, n = _lib.make_copies([(FAKE, FAKE + (1 << 40), 1 << 40, 1 << 30, 1 << 30)])
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_OVERFLOW  # 2^70 B
+    # one 256-thread workgroup per row chunk of 4096 slots: 2^24 rows need 2^32 threads
+    assert _thd(lib, lay, B=1 << 24, S=64) == _lib.ERR_OVERFLOW
+    assert _thd(lib, lay, B=(1 << 24) - 1, S=64) == _lib.ERR_WORKSPACE
+    # ... and the fused 16-byte copy units (one thread each) count toward the same grid
+    arr, n = _lib.make_copies([(FAKE, FAKE + (1 << 40), 1, 1 << 34, 1 << 34)])
+    assert _thd(lib, lay, B=3 << 22, S=64, copies=arr, n_copies=n) == _lib.ERR_OVERFLOW
+    assert _thd(lib, lay, B=(3 << 22) - 1, S=64, copies=arr, n_copies=n) == _lib.ERR_WORKSPACE
     # destination rows at a stride reaching back into the source
     arr, n = _lib.make_copies([(FAKE + 4096, FAKE, 4, 64, 64, 2048)])
     assert _thd(lib, lay, copies=arr, n_copies=n, wsb=1 << 20) == _lib.ERR_ARG
@@ -154,6 +176,12 @@ def test_split_thd_validation(lib):
     assert _split(lib, lay, n=None) == _lib.ERR_ARG
     assert _split(lib, lay, st=None) == _lib.ERR_ARG
     assert _split(lib, lay, B=1 << 20, S=1 << 12, G=1 << 10) == _lib.ERR_OVERFLOW
+    huge = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, FAKE, _lib.I64, 1 << 40)
+    assert _split(lib, huge, B=1 << 40, S=0, G=1) == _lib.ERR_OVERFLOW
+    assert _split(lib, lay, B=1 << 40, S=0, G=1 << 40) == _lib.ERR_OVERFLOW
+    assert _split(lib, lay, B=1 << 32, S=0, G=1 << 32) == _lib.ERR_OVERFLOW
+    assert _split(lib, lay, B=1 << 24, S=64, G=1 << 10) == _lib.ERR_OVERFLOW
+    assert _split(lib, lay, B=(1 << 24) - 1024, S=64, G=1 << 10, ws=None) == _lib.ERR_WORKSPACE
     assert _split(lib, lay, ws=None) == _lib.ERR_WORKSPACE
     assert _split(lib, lay, wsb=256) == _lib.ERR_WORKSPACE
 
@@ -225,6 +253,13 @@ def test_pack_rows_validation(lib):
     assert _pack(lib, src=None) == _lib.ERR_ARG
     assert _pack(lib, ws=None) == _lib.ERR_WORKSPACE
     assert _pack(lib, wsb=16) == _lib.ERR_WORKSPACE
+    # one workgroup of 64 threads per chunk of a pack: 2^26 of them would need 2^32 threads
+    assert _pack(lib, P=1 << 26, C=64, ws=None) == _lib.ERR_OVERFLOW
+    assert _pack(lib, P=(1 << 26) - 1, C=64, ws=None) == _lib.ERR_WORKSPACE
+    assert _pack(lib, P=1 << 22, C=16384, ws=None) == _lib.ERR_OVERFLOW     # 19 chunks each
+    assert _pack(lib, P=1 << 21, C=16384, ws=None) == _lib.ERR_WORKSPACE
+    assert _rect(lib, P=1 << 26, C=64, ws=None) == _lib.ERR_OVERFLOW
+    assert _rect(lib, P=(1 << 26) - 1, C=64, ws=None) == _lib.ERR_WORKSPACE
 
 
 def test_python_api_refuses_cpu_tensors():

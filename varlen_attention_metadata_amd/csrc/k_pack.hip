@@ -288,19 +288,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
 size_t pack_rows_workspace() { return 256; }
 
+namespace {
+uint64_t pack_groups(int64_t P, int32_t C, uint32_t *slots_out) {
+    const bool small = (uint64_t)P * (uint64_t)(((int64_t)C + kBigSlots - 1) / kBigSlots) <
+                       kFillGroups;
+    const uint32_t slots = small ? kSmallSlots : kBigSlots;
+    *slots_out = slots;
+    const uint64_t n_chunks = ((uint64_t)C + slots - 1) / slots;
+    return P > 0 ? (uint64_t)P * n_chunks : 1ull;
+}
+}  // namespace
+
+bool pack_rows_grid_fits(int64_t P, int32_t C) {
+    uint32_t slots;
+    return pack_groups(P, C, &slots) * (uint64_t)kThreads <= kMaxGridThreads;
+}
+
 hipError_t launch_pack_rows(const int64_t *src, int64_t src_len, const int64_t *src_off,
                             int64_t src_stride, const int32_t *real_len, int64_t N, int32_t q,
                             const int32_t *order, const int64_t *pack_start, int64_t P,
                             int32_t C, int fold, int64_t pad_token, int64_t *packed,
                             uint8_t *tmask, int32_t *cu, int32_t *cp, int32_t *status,
                             void *workspace, hipStream_t stream) {
-    const bool small = (uint64_t)P * (uint64_t)(((int64_t)C + kBigSlots - 1) / kBigSlots) <
-                       kFillGroups;
-    const uint32_t slots = small ? kSmallSlots : kBigSlots;
+    uint32_t slots;
+    const uint64_t groups = pack_groups(P, C, &slots);
+    if (groups * (uint64_t)kThreads > kMaxGridThreads) return hipErrorInvalidConfiguration;
     const uint32_t n_chunks = (uint32_t)(((int64_t)C + slots - 1) / slots);
-    const uint64_t groups = P > 0 ? (uint64_t)P * n_chunks : 1ull;
     const int vec_mask = ((uintptr_t)tmask % 16) == 0;
-    hipLaunchKernelGGL(small ? k_pack_rows<kSmallSlots> : k_pack_rows<kBigSlots>,
+    hipLaunchKernelGGL(slots == kSmallSlots ? k_pack_rows<kSmallSlots> : k_pack_rows<kBigSlots>,
                        dim3((uint32_t)groups), dim3(kThreads), 0, stream, src,
                        src_len, src_off, src_stride, real_len, N, q, order, pack_start, P, C, fold,
                        pad_token, packed, tmask, cu, cp, status, (WsHeader *)workspace,

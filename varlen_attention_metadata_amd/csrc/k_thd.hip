@@ -941,18 +941,38 @@ __global__ __launch_bounds__(kSmallThreads) void k_thd_small(ThdArgs<TL> a, uint
         copy_group<kSmallThreads, u32x4, true>(batch, (int64_t)blockIdx.x - 1 - n_mask);
 }
 
+bool small_tables(int64_t B, int64_t P, int64_t S, int64_t G) {
+    return B >= 1 && P >= 1 && S >= 1 && (uint64_t)B * (uint64_t)P <= kSmallEntries &&
+           G <= (int64_t)kSmallGroups;
+}
+
 template <typename TL>
 bool small_tables(const ThdArgs<TL> &a) {
-    return a.B >= 1 && a.P >= 1 && a.S >= 1 && (uint64_t)a.B * a.P <= kSmallEntries &&
-           a.G <= kSmallGroups;
+    return small_tables(a.B, a.P, a.S, a.G);
+}
+
+// Threads of the launch carrying the metadata (and the fused 16-byte copies):
+// the single-workgroup kernel for small tables, else one workgroup per row
+// chunk.  The copies launched alone are bounded by their unit count.
+uint64_t thd_meta_threads(int64_t B, int64_t P, int64_t S, int64_t G, const CopyPlan &plan) {
+    if (small_tables(B, P, S, G)) {
+        const uint64_t n_mask = (uint64_t)B * (((uint64_t)S + kSmallSlots - 1) / kSmallSlots);
+        return (1ull + n_mask + (uint64_t)plan.groups[0]) * (uint64_t)kSmallThreads;
+    }
+    const uint64_t n_chunks = S > 0 ? ((uint64_t)S + kSlots - 1) / kSlots : 1ull;
+    const uint64_t n_meta = B > 0 ? (uint64_t)B * n_chunks : 1ull;
+    return (n_meta + (uint64_t)plan.groups[0]) * (uint64_t)kThreads;
 }
 
 template <typename TL>
 hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, int n_copies,
                         hipStream_t stream) {
     CopyPlan plan;
-    if (small_tables(a)) {
-        plan_copies(copies, n_copies, &plan, kSmallThreads);
+    const bool small = small_tables(a);
+    plan_copies(copies, n_copies, &plan, small ? kSmallThreads : kThreads);
+    if (thd_meta_threads(a.B, a.P, a.S, a.G, plan) > kMaxGridThreads)
+        return hipErrorInvalidConfiguration;
+    if (small) {
         const uint32_t n_mchunks = (a.S + kSmallSlots - 1u) / kSmallSlots;
         const uint32_t n_mask = a.mask ? a.B * n_mchunks : 0u;
         const uint64_t grid = 1ull + n_mask + (uint64_t)plan.groups[0];
@@ -964,7 +984,6 @@ hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, 
         if (e != hipSuccess) return e;
         return launch_copy_plan(plan, 1, stream);
     }
-    plan_copies(copies, n_copies, &plan, kThreads);
     if (plan.groups[0] > 0) {
         const uint64_t grid = (uint64_t)n_meta + (uint64_t)plan.groups[0];
         hipLaunchKernelGGL(k_thd_tables_copy<TL>, dim3((uint32_t)grid), dim3(kThreads), 0,
@@ -978,6 +997,13 @@ hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, 
 }
 
 }  // namespace
+
+bool thd_tables_grid_fits(int64_t B, int64_t P, int64_t S, int64_t G, const psq_copy *copies,
+                          int n_copies) {
+    CopyPlan plan;
+    plan_copies(copies, n_copies, &plan, small_tables(B, P, S, G) ? kSmallThreads : kThreads);
+    return thd_meta_threads(B, P, S, G, plan) <= kMaxGridThreads;
+}
 
 size_t thd_tables_workspace(int64_t B, int64_t P, int64_t G) {
     const int64_t Bc = G > 0 ? B / G : 0;

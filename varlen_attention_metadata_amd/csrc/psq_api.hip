@@ -82,6 +82,7 @@ int psq_workspace_init(void *workspace, size_t bytes, void *stream) {
 
 size_t psq_params_from_doc_ids_workspace(int64_t B, int64_t S) {
     if (B < 0 || S < 0) return 0;
+    if (S > 0 && B > (kI32Limit - 1) / S) return 0;
     return psq::doc_segments_workspace(B, S);
 }
 
@@ -104,8 +105,11 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
 
 size_t psq_process_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t S) {
     if (layout == nullptr || B < 0 || S < 0) return 0;
+    if (S > 0 && B > (kI32Limit - 1) / S) return 0;
     if (layout->kind == PSQ_LAYOUT_DOC_IDS) return psq::doc_segments_workspace(B, S);
-    return psq::thd_tables_workspace(B, layout->P > 0 ? layout->P : 0, 1);
+    if (layout->kind != PSQ_LAYOUT_SEQ_LENS || layout->P < 0) return 0;
+    if (layout->P > 0 && B > (kI32Limit - 2) / layout->P) return 0;
+    return psq::thd_tables_workspace(B, layout->P, 1);
 }
 
 int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t *cu_seqlens,
@@ -135,8 +139,11 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t 
     }
     if (layout->kind != PSQ_LAYOUT_SEQ_LENS) return PSQ_ERR_ARG;
     if (!valid_dtype(layout->lens_dtype) || layout->P < 0) return PSQ_ERR_ARG;
-    if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
+    // bound B*P before forming it: with S = 0 the row-length check leaves B unbounded
     if (layout->P > 0 && B > (kI32Limit - 2) / layout->P) return PSQ_ERR_OVERFLOW;
+    if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
+    if (!psq::thd_tables_grid_fits(B, layout->P, S, 1, copies, n_copies))
+        return PSQ_ERR_OVERFLOW;
     if (workspace == nullptr || workspace_bytes < psq::thd_tables_workspace(B, layout->P, 1))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
@@ -152,7 +159,9 @@ size_t psq_split_thd_workspace(const psq_thd_layout *layout, int64_t B, int64_t 
     if (layout == nullptr || B < 0 || S < 0 || num_chunks < 1 || B % num_chunks != 0 ||
         layout->kind != PSQ_LAYOUT_SEQ_LENS || layout->P < 0)
         return 0;
-    if (layout->P > 0 && B > (kI32Limit - 2) / layout->P) return 0;
+    if (S > 0 && B > (kI32Limit - 1) / S) return 0;
+    if (num_chunks > kI32Limit) return 0;
+    if (layout->P > 0 && B > (kI32Limit - 2 - num_chunks) / layout->P) return 0;
     return psq::thd_tables_workspace(B, layout->P, num_chunks);
 }
 
@@ -173,9 +182,13 @@ int psq_split_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int64_t nu
     const int cc = check_copies(copies, n_copies);
     if (cc != PSQ_OK) return cc;
     if (!valid_dtype(layout->lens_dtype) || layout->P < 0) return PSQ_ERR_ARG;
-    if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
     // every staged / stacked boundary array holds at most B*P + num_chunks entries
+    // (checked before B*P is formed, which S = 0 would leave unbounded)
+    if (num_chunks > kI32Limit) return PSQ_ERR_OVERFLOW;
     if (layout->P > 0 && B > (kI32Limit - 2 - num_chunks) / layout->P) return PSQ_ERR_OVERFLOW;
+    if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
+    if (!psq::thd_tables_grid_fits(B, layout->P, S, num_chunks, copies, n_copies))
+        return PSQ_ERR_OVERFLOW;
     if (workspace == nullptr ||
         workspace_bytes < psq::thd_tables_workspace(B, layout->P, num_chunks))
         return PSQ_ERR_WORKSPACE;
@@ -226,6 +239,7 @@ int psq_pack_rows(const int64_t *src_tokens, int64_t src_len, const int64_t *src
     if (P > 0 && (packed == nullptr || token_mask == nullptr || cu_seqlens == nullptr ||
                   cu_seqlens_padded == nullptr))
         return PSQ_ERR_ARG;
+    if (!psq::pack_rows_grid_fits(P, capacity)) return PSQ_ERR_OVERFLOW;
     if (N > 0 && (src_offsets == nullptr || real_len == nullptr)) return PSQ_ERR_ARG;
     if (src_len > 0 && src_tokens == nullptr) return PSQ_ERR_ARG;
     if (workspace == nullptr || workspace_bytes < psq::pack_rows_workspace())
@@ -251,6 +265,7 @@ int psq_pack_padded_rows(const int64_t *rows, int64_t W, const int32_t *real_len
     if (P > 0 && (packed == nullptr || token_mask == nullptr || cu_seqlens == nullptr ||
                   cu_seqlens_padded == nullptr))
         return PSQ_ERR_ARG;
+    if (!psq::pack_rows_grid_fits(P, capacity)) return PSQ_ERR_OVERFLOW;
     if (N > 0 && real_len == nullptr) return PSQ_ERR_ARG;
     if (N * W > 0 && rows == nullptr) return PSQ_ERR_ARG;
     if (workspace == nullptr || workspace_bytes < psq::pack_rows_workspace())

@@ -10,6 +10,9 @@
 
 namespace psq {
 
+// One HIP launch runs at most 2^32 - 1 threads along x.
+constexpr uint64_t kMaxGridThreads = 0xffffffffull;
+
 // k_segments.hip -- document map -> segment boundaries (then the collapse copies).
 size_t doc_segments_workspace(int64_t B, int64_t S);
 hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_t S,
@@ -21,6 +24,10 @@ hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_
 // k_thd.hip -- length tables -> THD metadata and layout mask (+ fused copies),
 // for G equal row groups (G == 1: one process_input_for_thd call).
 size_t thd_tables_workspace(int64_t B, int64_t P, int64_t G);
+// Whether every grid of the call fits kMaxGridThreads (sizes already bounded
+// by the int32 checks of the API).
+bool thd_tables_grid_fits(int64_t B, int64_t P, int64_t S, int64_t G, const psq_copy *copies,
+                          int n_copies);
 hipError_t launch_thd_tables(const void *L, const void *Lp, int lens_dtype, int64_t B,
                              int64_t P, int64_t S, int64_t G, int64_t pad_value, int32_t *cu,
                              int32_t *cp, int32_t *num_seqs, int32_t *max_seqlen,
@@ -34,6 +41,7 @@ hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 
 // k_pack.hip -- the squeeze into fixed-capacity packs.
 size_t pack_rows_workspace();
+bool pack_rows_grid_fits(int64_t P, int32_t C);
 hipError_t launch_pack_rows(const int64_t *src, int64_t src_len, const int64_t *src_off,
                             int64_t src_stride, const int32_t *real_len, int64_t N, int32_t q,
                             const int32_t *order, const int64_t *pack_start, int64_t P,
