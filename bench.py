@@ -69,14 +69,24 @@ WORKLOAD_COUNTERS = {
 }
 
 
+def code_text(text: str) -> str:
+    """C++ source without its comments, trailing blanks and empty lines: an
+    edit of a comment leaves the kernel, and so its counter figures, as they
+    were.  (The sources hold no string literal containing a comment opener.)"""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash(names=STAGE_KERNEL_SOURCES) -> str:
-    """Hash of the kernel's sources: stored HBM counter figures are only used
+    """Hash of the kernel's code: stored HBM counter figures are only used
     while the kernel they were taken on is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "varlen_attention_metadata_amd", "csrc")
     for name in names:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update(name.encode() + b"\0" + code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

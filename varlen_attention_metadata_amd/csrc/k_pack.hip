@@ -46,9 +46,11 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMembers = kThreads;       // members per LDS batch
 // Slots per workgroup: 896, or 256 when 896-slot chunks would leave most of
 // the chip idle (fewer than kFillGroups workgroups).  896 slots (14 per lane)
-// hold 85 VGPRs, so 6 waves per SIMD stay resident; on MI355X the 65536-source
-// workload took 160 us this way, against 168.5 us at 1024 (93 VGPRs, 5
-// waves), 162-164 us at 640 or 768 and 168 us at 512.
+// hold 85 VGPRs (88 allocated), so 5 waves per SIMD stay resident, as at 1024
+// slots; on MI355X the 65536-source workload took 160 us this way, against
+// 168.5 us at 1024 (16 loads per lane), 162-164 us at 640 or 768 and 168 us at
+// 512.  Built for 6, 7 or 8 waves per SIMD the compiler spills, and the
+// workload took 166, 225 and 278 us.
 constexpr uint32_t kBigSlots = 896;
 constexpr uint32_t kSmallSlots = 256;
 constexpr uint64_t kFillGroups = 1024;
