@@ -279,3 +279,62 @@ def test_python_api_refuses_cpu_tensors():
         psq.thd_padding_mask_from_token_ids(torch.zeros(4, dtype=torch.int64), 0)
     with pytest.raises(ValueError, match="GPU"):
         psq.pack_padded_rows(torch.zeros((2, 4), dtype=torch.int64), [1, 2], [[0, 1]], 4)
+
+
+def test_header_is_c_and_matches_the_binding(tmp_path):
+    """``include/psq.h`` compiles as C99 and as C++, every function it declares
+    links against ``libpsq.so``, and its structs and constants have the
+    layout and values the ctypes binding assumes."""
+    import os
+    names = _lib.header_functions()
+    src = tmp_path / "abi.c"
+    src.write_text(
+        "#include <stddef.h>\n#include <stdio.h>\n#include \"psq.h\"\n"
+        "int main(void) {\n"
+        "    const void *fns[] = {" + ", ".join(f"(const void *)&{n}" for n in names) + "};\n"
+        "    size_t i, n = 0;\n"
+        "    for (i = 0; i < sizeof fns / sizeof fns[0]; ++i) n += fns[i] != NULL;\n"
+        "    printf(\"%zu\\n\", n);\n"
+        "    printf(\"%zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(psq_copy),\n"
+        "           offsetof(psq_copy, src), offsetof(psq_copy, dst), offsetof(psq_copy, rows),\n"
+        "           offsetof(psq_copy, row_bytes), offsetof(psq_copy, src_row_stride_bytes),\n"
+        "           offsetof(psq_copy, dst_row_stride_bytes));\n"
+        "    printf(\"%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(psq_thd_layout),\n"
+        "           offsetof(psq_thd_layout, kind), offsetof(psq_thd_layout, seq_lens),\n"
+        "           offsetof(psq_thd_layout, seq_lens_padded), offsetof(psq_thd_layout, lens_dtype),\n"
+        "           offsetof(psq_thd_layout, P), offsetof(psq_thd_layout, pad_value),\n"
+        "           offsetof(psq_thd_layout, doc_ids), offsetof(psq_thd_layout, doc_dtype));\n"
+        "    printf(\"%d %d %d %d %d %d %d %d %d %d\\n\", PSQ_I32, PSQ_I64, PSQ_OK, PSQ_ERR_ARG,\n"
+        "           PSQ_ERR_OVERFLOW, PSQ_ERR_WORKSPACE, PSQ_ERR_HIP, PSQ_LAYOUT_SEQ_LENS,\n"
+        "           PSQ_LAYOUT_DOC_IDS, PSQ_MAX_COPIES);\n"
+        "    printf(\"%d %d %d %d %d %d %d %d %d\\n\", PSQ_DATA_BAD_LENGTH,\n"
+        "           PSQ_DATA_TABLE_MISMATCH, PSQ_DATA_ROW_OVERFLOW, PSQ_DATA_EMPTY_ROW,\n"
+        "           PSQ_DATA_PACK_OVERFLOW, PSQ_DATA_EMPTY_PACK, PSQ_DATA_BAD_INDEX,\n"
+        "           PSQ_DATA_WORKSPACE, PSQ_DATA_PAD_IS_CONTENT);\n"
+        "    printf(\"%s\\n\", psq_status_string(PSQ_DATA_PACK_OVERFLOW, 1));\n"
+        "    return 0;\n}\n")
+    inc = os.path.dirname(_lib.HEADER)
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", inc, str(src),
+                    "-L", libdir, "-l:libpsq.so", f"-Wl,-rpath,{libdir}",
+                    "-Wl,--allow-shlib-undefined", "-o", str(exe)], check=True)
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++",
+                    "-I", inc, str(src)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    assert int(out[0]) == len(names)
+    C, L = _lib.PsqCopy, _lib.PsqThdLayout
+    assert [int(x) for x in out[1].split()] == [ctypes.sizeof(C)] + [
+        getattr(C, f).offset for f in ("src", "dst", "rows", "row_bytes",
+                                       "src_row_stride_bytes", "dst_row_stride_bytes")]
+    assert [int(x) for x in out[2].split()] == [ctypes.sizeof(L)] + [
+        getattr(L, f).offset for f in ("kind", "seq_lens", "seq_lens_padded", "lens_dtype", "P",
+                                       "pad_value", "doc_ids", "doc_dtype")]
+    assert [int(x) for x in out[3].split()] == [
+        _lib.I32, _lib.I64, _lib.OK, _lib.ERR_ARG, _lib.ERR_OVERFLOW, _lib.ERR_WORKSPACE,
+        _lib.ERR_HIP, _lib.LAYOUT_SEQ_LENS, _lib.LAYOUT_DOC_IDS, _lib.MAX_COPIES]
+    assert [int(x) for x in out[4].split()] == [
+        _lib.DATA_BAD_LENGTH, _lib.DATA_TABLE_MISMATCH, _lib.DATA_ROW_OVERFLOW,
+        _lib.DATA_EMPTY_ROW, _lib.DATA_PACK_OVERFLOW, _lib.DATA_EMPTY_PACK, _lib.DATA_BAD_INDEX,
+        _lib.DATA_WORKSPACE, _lib.DATA_PAD_IS_CONTENT]
+    assert out[5] == _lib.status_string(_lib.DATA_PACK_OVERFLOW, True)
