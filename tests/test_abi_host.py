@@ -338,3 +338,24 @@ def test_header_is_c_and_matches_the_binding(tmp_path):
         _lib.DATA_EMPTY_ROW, _lib.DATA_PACK_OVERFLOW, _lib.DATA_EMPTY_PACK, _lib.DATA_BAD_INDEX,
         _lib.DATA_WORKSPACE, _lib.DATA_PAD_IS_CONTENT]
     assert out[5] == _lib.status_string(_lib.DATA_PACK_OVERFLOW, True)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built HIP library there is no path at all: loading raises,
+    and so does the first call of the torch-facing API in a fresh process
+    whose library path points at nothing."""
+    with pytest.raises(RuntimeError, match="build the HIP library"):
+        _lib.open_library(str(tmp_path / "libpsq.so"))
+    import os
+    import sys
+    code = ("import torch, varlen_attention_metadata_amd as psq\n"
+            "from varlen_attention_metadata_amd import _lib\n"
+            f"_lib.LIB_PATH = {str(tmp_path / 'libpsq.so')!r}\n"
+            "try:\n"
+            "    _lib.psq_params_from_doc_ids_workspace(1, 1)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         check=True).stdout
+    assert out.startswith("raised:") and "is missing" in out
