@@ -460,3 +460,31 @@ def test_rect_trainer_workload(dev):
     assert out["width"] == ref["width"]
     assert np.array_equal(out["input_ids"].cpu().numpy(), ref["packed"])
     assert np.array_equal(out["cu_seqlens_flat"].cpu().numpy(), ref["cu_seqlens"])
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_rows_path_fuzz(dev, seed):
+    """Tables of at most 64 rows of at most 64 entries take the rows-in-wave
+    path of the single-workgroup kernel; the same tables widened past 64
+    entries per row with unused slots (identical outputs) take its general
+    path.  Random shapes at and around those limits, any row-group count,
+    half of them with planted faults, both paths against the oracle."""
+    from test_gpu_parity import corrupt_tables, rand_tables as rand_tables_holes
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.choice([1, 2, 3, 16, 33, 63, 64, int(rng.integers(1, 65))]))
+    P = int(rng.choice([1, 2, 5, 31, 32, 33, 63, 64, int(rng.integers(1, 65))]))
+    divisors = [g for g in range(1, B + 1) if B % g == 0]
+    G = int(rng.choice(divisors))
+    S = int(rng.choice([1, 4, 37, 512, 8192, int(rng.integers(1, 3000))]))
+    q = int(rng.choice([1, 4, 8]))
+    L, Lp = rand_tables_holes(rng, B, P, S, q, holes=bool(seed % 3 == 0))
+    if seed % 2:
+        L, Lp = corrupt_tables(rng, L, Lp, S, int(rng.integers(1, 3)))
+    extra = np.full((B, 65), V)
+    for lt, lpt in ((L, Lp), (np.hstack([L, extra]), np.hstack([Lp, extra]))):
+        check_split(dev, lt, lpt, S, G)
+        check_split(dev, lt, None, S, G)
+        if G == 1:
+            from test_gpu_parity import check_thd
+            fits = np.abs(np.concatenate([lt, lpt])).max() < 2**31
+            check_thd(dev, lt, lpt, S, torch.int32 if fits else torch.int64)

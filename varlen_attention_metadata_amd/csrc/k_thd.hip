@@ -564,7 +564,8 @@ __global__ __launch_bounds__(kThreads) void k_thd_tables_copy(ThdArgs<TL> a, uin
 // ---------------------------------------------------------------------------
 // Small tables (B*P <= kSmallEntries, G <= kSmallGroups).
 // Workgroup 0 holds the whole table in registers and LDS and derives every
-// group's boundaries and scalars from it with block-wide scans; each of the
+// group's boundaries and scalars from it with block-wide scans (tables of at
+// most 64 rows of at most 64 entries: one wave per row, thd_rows_meta); each of the
 // next workgroups writes one (row, chunk) of the mask from its own row's
 // table.  No workgroup waits on another, so there is no ticket, look-back or
 // completion count, and the workspace is left untouched.  The status bits
@@ -857,6 +858,217 @@ __device__ __forceinline__ void thd_small_meta(const ThdArgs<TL> &args, SmallMet
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tables of at most kRowsMax rows of at most one wave of entries (B <= 64,
+// P <= 64): each wave owns whole rows, lane j holding entry j of rows w,
+// w + 16, w + 32 and w + 48.  Validation, the row's saturating padded sum,
+// its fold, its longest sequence, the in-row scans and the tightness test
+// all run in registers (ballots and DPP scans), and one LDS exchange of the
+// per-row totals, behind one barrier, places every row.  The predicates and
+// outputs are those of thd_small_meta; on MI355X the 16 x 64 tables of the
+// length-table workload finish workgroup 0 in about half the time, because
+// the general path's five barrier-separated phases each wait about 1 us on
+// chains of dependent LDS accesses.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kRowsPerWave = 4;
+constexpr uint32_t kRowsMax = kRowsPerWave * (uint32_t)kSmallWaves;   // 64 rows
+
+struct RowsMeta {
+    uint32_t rt[3][kRowsMax];               // per row: sequences, real sum, folded padded sum
+    uint32_t g_flag[kSmallGroups];          // an interior boundary departs from its physical one
+    int32_t g_max[kSmallGroups];            // largest real length of the group
+    uint32_t g_last_real[kSmallGroups];     // real length of the group's last sequence
+    uint32_t err;
+};
+
+// wrapping inclusive sum over the wave
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t x) {
+    x += (uint32_t)dpp0<0x111>((int)x);
+    x += (uint32_t)dpp0<0x112>((int)x);
+    x += (uint32_t)dpp0<0x114>((int)x);
+    x += (uint32_t)dpp0<0x118>((int)x);
+    x += (uint32_t)dpp0<0x142, 0xa>((int)x);
+    x += (uint32_t)dpp0<0x143, 0xc>((int)x);
+    return x;
+}
+
+// inclusive sum over the wave, saturated at `sat` (sat <= 2^31)
+__device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
+    x = sat_add(x, (uint32_t)dpp0<0x111>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x112>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x114>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x118>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x142, 0xa>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x143, 0xc>((int)x), sat);
+    return x;
+}
+
+bool rows_tables(uint32_t B, uint32_t P) { return B <= kRowsMax && P <= (uint32_t)kWave; }
+
+template <typename TL>
+__device__ __forceinline__ void thd_rows_meta(const ThdArgs<TL> &args, RowsMeta &m) {
+    const uint32_t B = args.B, P = args.P, S = args.S, G = args.G, Bc = args.Bc;
+    const uint32_t Tc = Bc * S;     // tokens of one group (< 2^31)
+    const uint32_t sat = S + 1u;    // clamp of a length, and of a row's padded sum
+    const int64_t pv = args.pad_value;
+    const TL *__restrict__ L = args.L;
+    const TL *__restrict__ Lq = args.Lp ? args.Lp : args.L;
+    const bool has_lp = args.Lp != nullptr;
+    int32_t *__restrict__ cu = args.cu;
+    int32_t *__restrict__ cp = args.cp;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x / (uint32_t)kWave);
+    const uint32_t j = (uint32_t)lane_id();
+
+    if (threadIdx.x < kSmallGroups) {
+        m.g_flag[threadIdx.x] = 0;
+        m.g_max[threadIdx.x] = 0;
+    }
+    if (threadIdx.x == 0) m.err = 0;
+
+    // every load is issued before any is used; lanes outside the table read
+    // as unused slots
+    int64_t l[kRowsPerWave], lp[kRowsPerWave];
+#pragma unroll
+    for (uint32_t i = 0; i < kRowsPerWave; ++i) {
+        const uint32_t r = w + i * (uint32_t)kSmallWaves;
+        l[i] = pv;
+        lp[i] = pv;
+        if (r < B && j < P) {
+            l[i] = (int64_t)L[r * P + j];
+            lp[i] = (int64_t)Lq[r * P + j];
+        }
+    }
+    __syncthreads();   // the zeroed accumulators before any update
+
+    // each row: validity, the length checks, clamped lengths, the padded sum
+    // (saturated at S+1, so ROW_OVERFLOW is exact), the fold of the tail pad
+    // into the row's last sequence, and exclusive in-row scans
+    uint32_t exc[kRowsPerWave], exr[kRowsPerWave], exq[kRowsPerWave];
+    bool val[kRowsPerWave];
+    uint32_t err = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kRowsPerWave; ++i) {
+        const uint32_t r = w + i * (uint32_t)kSmallWaves;
+        const bool valid = l[i] != pv;
+        if (has_lp && ((lp[i] != pv) != valid)) err |= PSQ_DATA_TABLE_MISMATCH;
+        uint32_t r_c = 0, p_c = 0;
+        if (valid) {
+            if (l[i] < 0 || lp[i] < l[i]) err |= PSQ_DATA_BAD_LENGTH;
+            const int64_t lim = (int64_t)sat;
+            p_c = (uint32_t)(lp[i] < 0 ? 0 : (lp[i] > lim ? lim : lp[i]));
+            r_c = (uint32_t)(l[i] < 0 ? 0 : (l[i] > lim ? lim : l[i]));
+        }
+        val[i] = valid;
+        exc[i] = exr[i] = exq[i] = 0;
+        if (r < B) {   // uniform
+            const uint64_t vm = __ballot(valid);
+            const uint32_t sum = (uint32_t)read_lane((int)wave_incl_sat(p_c, sat), kWave - 1);
+            const int32_t mx = read_lane(wave_incl_max((int)r_c), kWave - 1);
+            const uint32_t last_j = vm ? 63u - (uint32_t)__clzll(vm) : 0u;
+            const bool is_last = vm != 0 && j == last_j;
+            if (is_last) p_c += S - sum;   // the fold (its value matters only if sum <= S)
+            const uint32_t ir = wave_incl_add(r_c);
+            const uint32_t ip = wave_incl_add(p_c);
+            exc[i] = (uint32_t)__popcll(vm & ((1ull << j) - 1ull));
+            exr[i] = ir - r_c;
+            exq[i] = ip - p_c;
+            const uint32_t g = r / Bc;
+            const bool group_last_row = r + 1u == (g + 1u) * Bc;
+            // every sequence but its group's last must be tight
+            const bool loose = valid && r_c != p_c && !(group_last_row && is_last);
+            const bool any_loose = __ballot(loose) != 0;
+            const uint32_t tot_r = (uint32_t)read_lane((int)ir, kWave - 1);
+            const uint32_t tot_p = (uint32_t)read_lane((int)ip, kWave - 1);
+            if (j == 0) {
+                uint32_t e2 = 0;
+                if (vm == 0) e2 |= PSQ_DATA_EMPTY_ROW;
+                if (sum > S) e2 |= PSQ_DATA_ROW_OVERFLOW;
+                if (e2) atomicOr(&m.err, e2);
+                m.rt[0][r] = (uint32_t)__popcll(vm);
+                m.rt[1][r] = tot_r;
+                m.rt[2][r] = tot_p;
+                if (any_loose) atomicOr(&m.g_flag[g], 1u);
+                if (mx > 0) atomicMax(&m.g_max[g], mx);
+            }
+            if (group_last_row && is_last) m.g_last_real[g] = r_c;
+        }
+    }
+    if (err) atomicOr(&m.err, err);
+    __syncthreads();
+
+    const uint32_t st = m.err;
+    // inclusive scans of the row totals: lane x holds rows 0 .. x
+    const uint32_t ic = wave_incl_add(j < B ? m.rt[0][j] : 0u);
+    const uint32_t ir = wave_incl_add(j < B ? m.rt[1][j] : 0u);
+    const uint32_t ip = wave_incl_add(j < B ? m.rt[2][j] : 0u);
+    // sum over rows 0 .. x-1 (x uniform, <= B)
+    auto pre = [](uint32_t v, uint32_t x) -> uint32_t {
+        return x ? (uint32_t)read_lane((int)v, (int)x - 1) : 0u;
+    };
+    // longest group's boundary count, n + 1: lane g holds group g's.  The
+    // shuffles run on every lane (a source lane outside the exec mask would
+    // read as 0); lanes past the groups read lane 0 and are discarded.
+    const uint32_t g_hi = j < G ? (j + 1u) * Bc - 1u : 0u;
+    const uint32_t g_lo = (j < G && j) ? j * Bc - 1u : 0u;
+    const uint32_t c_hi = (uint32_t)__shfl((int)ic, (int)g_hi);
+    const uint32_t c_lo = (uint32_t)__shfl((int)ic, (int)g_lo);
+    const uint32_t n_lane = j < G ? c_hi - (j ? c_lo : 0u) + 1u : 0u;
+    const uint32_t width = (uint32_t)read_lane(wave_incl_max((int)n_lane), kWave - 1);
+    const uint32_t stride = G > 1 ? width : 0u;   // output row of group g starts at g * stride
+
+    // boundaries of every sequence (group-relative)
+    if (st == 0) {
+#pragma unroll
+        for (uint32_t i = 0; i < kRowsPerWave; ++i) {
+            const uint32_t r = w + i * (uint32_t)kSmallWaves;
+            if (r < B) {   // uniform
+                const uint32_t g = r / Bc, r0 = g * Bc;
+                const uint32_t bc = pre(ic, r) - pre(ic, r0);
+                const uint32_t br = pre(ir, r) - pre(ir, r0);
+                const uint32_t bp = pre(ip, r) - pre(ip, r0);
+                if (val[i]) {
+                    const uint32_t at = g * stride + bc + exc[i];
+                    cu[at] = (int32_t)(br + exr[i]);
+                    if (cp) cp[at] = (int32_t)(bp + exq[i]);
+                }
+            }
+        }
+    }
+    // each group's close, the sentinel fill of its stacked row, its scalars
+    for (uint32_t g = w; g < G; g += (uint32_t)kSmallWaves) {   // uniform
+        const uint32_t r0 = g * Bc, r1 = r0 + Bc;
+        if (st == 0) {
+            const uint32_t n = pre(ic, r1) - pre(ic, r0);
+            const uint32_t total = pre(ir, r1) - pre(ir, r0);
+            const bool disagree = m.g_flag[g] != 0;
+            const bool absorbed = !disagree && total < Tc;
+            int32_t mx = m.g_max[g];
+            // without a status bit every row, hence every group, holds a sequence
+            if (absorbed && n) mx = max(mx, (int32_t)(Tc - (total - m.g_last_real[g])));
+            const uint32_t base = g * stride;
+            if (j == 0) {
+                cu[base + n] = (int32_t)(absorbed ? Tc : total);
+                if (cp) cp[base + n] = (int32_t)Tc;
+                args.num_seqs[g] = (int32_t)n;
+                args.max_seqlen[g] = mx;
+                args.pad_between[g] = disagree ? 1 : 0;
+            }
+            for (uint32_t x = n + 1u + j; x < stride; x += (uint32_t)kWave) {
+                cu[base + x] = (int32_t)pv;
+                if (cp) cp[base + x] = (int32_t)pv;
+            }
+        } else if (j == 0) {
+            args.num_seqs[g] = 0;
+            args.max_seqlen[g] = 0;
+            args.pad_between[g] = 0;
+        }
+    }
+    if (threadIdx.x == 0) {
+        *args.status = (int32_t)st;
+        if (args.cu_width) *args.cu_width = (int32_t)(st == 0 ? width : 0u);
+    }
+}
+
 // 4 mask bits (1 = padding) -> 4 bytes of 0/1
 __device__ __forceinline__ uint32_t spread4(uint32_t x) {
     return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
@@ -932,10 +1144,15 @@ template <typename TL, int kPer>
 __global__ __launch_bounds__(kSmallThreads) void k_thd_small(ThdArgs<TL> a, uint32_t n_mask,
                                                              uint32_t n_mchunks,
                                                              CopyBatch batch) {
-    __shared__ SmallMeta<kPer> meta;
-    if (blockIdx.x == 0)
-        thd_small_meta<TL, kPer>(a, meta);
-    else if (blockIdx.x <= n_mask)
+    if (blockIdx.x == 0) {
+        if constexpr (kPer == 0) {
+            __shared__ RowsMeta meta;
+            thd_rows_meta<TL>(a, meta);
+        } else {
+            __shared__ SmallMeta<kPer> meta;
+            thd_small_meta<TL, kPer>(a, meta);
+        }
+    } else if (blockIdx.x <= n_mask)
         thd_small_mask<TL>(a, blockIdx.x - 1u, n_mchunks);
     else
         copy_group<kSmallThreads, u32x4, true>(batch, (int64_t)blockIdx.x - 1 - n_mask);
@@ -977,7 +1194,9 @@ hipError_t launch_typed(ThdArgs<TL> a, uint32_t n_meta, const psq_copy *copies, 
         const uint32_t n_mask = a.mask ? a.B * n_mchunks : 0u;
         const uint64_t grid = 1ull + n_mask + (uint64_t)plan.groups[0];
         const bool two = (uint64_t)a.B * a.P <= (uint64_t)2 * kSmallThreads;
-        hipLaunchKernelGGL((two ? k_thd_small<TL, 2> : k_thd_small<TL, kSmallPerMax>),
+        hipLaunchKernelGGL((rows_tables(a.B, a.P) ? k_thd_small<TL, 0>
+                            : two               ? k_thd_small<TL, 2>
+                                                : k_thd_small<TL, kSmallPerMax>),
                            dim3((uint32_t)grid), dim3(kSmallThreads), 0, stream, a, n_mask,
                            n_mchunks, plan.batch[0]);
         const hipError_t e = hipGetLastError();
