@@ -27,6 +27,7 @@
  * condition that holds; outputs are unspecified when the result is non-zero.
  */
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -38,6 +39,18 @@
 #define ORC_EMPTY_PACK     32u   /* a pack has no member                       */
 #define ORC_BAD_INDEX      64u   /* member / pack / source range out of bounds */
 #define ORC_PAD_IS_CONTENT 256u   /* the pad id also occurs before the pad tail */
+
+/* malloc that never returns NULL: an oracle that cannot hold its scratch */
+/* arrays stops the test run instead of returning a wrong answer.        */
+static void *orc_alloc(size_t bytes)
+{
+    void *p = malloc(bytes > 0 ? bytes : 1);
+    if (p == NULL) {
+        fprintf(stderr, "psq oracle: out of memory (%zu bytes)\n", bytes);
+        abort();
+    }
+    return p;
+}
 
 /* ------------------------------------------------------------------------ */
 /* [P1] packed_seq_params_from_doc_ids.                                      */
@@ -161,8 +174,8 @@ uint32_t orc_thd_tables(const int64_t *L, const int64_t *Lp,
         return status;
 
     /* Step 1: keep the valid entries in row-major order (sentinel filter). */
-    real = (int64_t *)malloc(sizeof(int64_t) * (size_t)(B * P + 1));
-    phys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(B * P + 1));
+    real = (int64_t *)orc_alloc(sizeof(int64_t) * (size_t)(B * P + 1));
+    phys = (int64_t *)orc_alloc(sizeof(int64_t) * (size_t)(B * P + 1));
     n = 0;
     for (r = 0; r < B; r++) {
         int64_t row_used = 0;
@@ -371,7 +384,7 @@ uint32_t orc_pack_rect(const int64_t *rows, int64_t W, const int32_t *real_len,
     int64_t i;
     int64_t *off;
 
-    off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+    off = (int64_t *)orc_alloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
     for (i = 0; i < N; i++)
         off[i] = i * W;
     status = pack_impl(rows, N * W, off, real_len, N, q, order, pack_start, P, C,
