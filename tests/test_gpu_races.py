@@ -15,6 +15,7 @@ word) and the pad-id mask (completion count).  The single-workgroup table
 kernel has no cross-workgroup step.
 """
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -26,7 +27,8 @@ from varlen_attention_metadata_amd import _build, _lib
 
 pytestmark = pytest.mark.gpu
 V = -1000
-REPEATS = 6
+# runs per case; PSQ_RACE_REPEATS raises it for a longer stress run
+REPEATS = int(os.environ.get("PSQ_RACE_REPEATS", "6"))
 
 
 def say(msg):
