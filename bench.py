@@ -69,6 +69,90 @@ WORKLOAD_COUNTERS = {
 }
 
 
+# rows of profiles/hbm_traffic_counters.md: (label, counter key, workload whose
+# algorithmic bytes the row is measured against; the stage step's two launches
+# are split into the collapse copy and the map)
+COUNTER_TABLE = [
+    ("k_copies<u32x4, true> (stage_embedding, launch 2: the collapse)",
+     "psq::k_copies<u32x4, true> [grid 537395200]", "stage_copy"),
+    ("k_doc_segments<int> (stage_embedding, launch 1: the map)",
+     "psq::k_doc_segments<int> [grid 65536]", "stage_map"),
+    ("stage_embedding step (both launches)", None, "stage_embedding"),
+    ("k_pack_rows<896> (pack_sources)", WORKLOAD_COUNTERS["pack_sources"][0], "pack_sources"),
+    ("k_pack_rows<256> (trainer_rectangle)", WORKLOAD_COUNTERS["trainer_rectangle"][0],
+     "trainer_rectangle"),
+    ("k_thd_small<long, 0> (thd_tables and thd_split_4: same grid, medians merged)",
+     "psq::k_thd_small<long, 0> [grid 214016]", "thd_tables"),
+    ("k_pad_ids<long> (pad_tail_stream)", WORKLOAD_COUNTERS["pad_tail_stream"][0],
+     "pad_tail_stream"),
+    ("k_doc_segments<int> (doc_map_medium)", WORKLOAD_COUNTERS["doc_map_medium"][0],
+     "doc_map_medium"),
+]
+
+COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+COUNTER_COMMANDS = """rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- python3 bench.py --profile-launches 3 --launch-info gpurun_out/launch_info.json
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- python3 bench.py --profile-launches 3
+python bench.py --summarize-counters gpurun_out/pmc_fetch/fetch_counter_collection.csv gpurun_out/pmc_write/write_counter_collection.csv --launch-info gpurun_out/launch_info.json"""
+
+COUNTERS_NOTES = """Per-kernel values are medians over the launches. `profiles/traffic_stage_embedding.json`
+holds the full output, tagged with the hash of the stage kernels' code. bench.py uses
+it for the headline `roofline.traffic` only while that code is unchanged.
+
+Its `workloads` entries carry the same figure for per-config lines whose launch grid no
+other launch of the run shares: pack_sources, trainer_rectangle, pad_tail_stream and
+doc_map_medium. Each is tagged with a hash of its own kernel's code, and bench.py
+reports it as that line's `roofline.traffic` under the same rule. doc_map_small's map
+shares its grid with the calibration copy's one-token map, and thd_split_4 shares its
+grid with thd_tables, so their traffic stays null.
+
+The calibration factor holds for launches that spread over every memory channel. Below
+about 1 MB, the scaled FETCH_SIZE is dominated by fixed per-launch reads: kernel code,
+arguments, the workspace header and the look-back descriptors. doc_map_medium's ratio is
+that overhead on a 128 KiB map, not re-reads. For the two large kernels the counters
+match the algorithmic bytes to within 2 %.
+
+The squeeze moves about 1.5 % more than its algorithmic bytes, all of it on the read
+side. Pad slots re-read a token of their own member, which keeps the loads straight-line
+code. Most of those re-reads hit lines already in flight; the rest is the excess."""
+
+
+def write_counters_md(out: dict, algo: dict) -> None:
+    """profiles/hbm_traffic_counters.md from the scaled counters and the
+    algorithmic bytes that the counter run's own workloads reported."""
+    fmt = lambda x: f"{x:,.0f}".replace(",", " ")
+    cal = out["kernels"]["calibration_copy_1GiB"]
+    lines = ["# HBM traffic from counters (FETCH_SIZE, WRITE_SIZE)", "",
+             "Commands (on an MI355X, from the repository root), one counter per run:", "",
+             "```", COUNTER_COMMANDS, "```", "",
+             "`--profile-launches 3` first launches a plain 1 GiB device copy: the collapse "
+             "path with a", "one-token map. It then launches each workload three times. The "
+             "stage-embedding step is", "two launches: the map kernel, then the collapse copy. "
+             "`--launch-info` records each", "workload's algorithmic bytes, computed by the "
+             "same code as the bench's rooflines.", "",
+             f"Calibration: the 1 GiB copy reads as FETCH_SIZE = {fmt(cal['fetch_kib'])} KiB and "
+             f"WRITE_SIZE = {fmt(cal['write_kib'])} KiB", "per dispatch. So:", "",
+             f"- read bytes = FETCH_SIZE × 1024 × {out['fetch_scale']};",
+             f"- write bytes = WRITE_SIZE × 1024 × {out['write_scale']}.", "",
+             "| kernel (workload) | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch | "
+             "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
+    for label, key, workload in COUNTER_TABLE:
+        a = algo.get(workload)
+        if key is None:
+            b = out["bytes_per_launch"]
+            lines.append(f"| {label} | | | | {fmt(b)} | {fmt(a)} | {b / a:.3f} |")
+            continue
+        v = out["kernels"].get(key)
+        if v is None or a is None:
+            continue
+        grid = int(key.split("[grid ")[1].rstrip("]"))
+        b = v["bytes_per_launch"]
+        lines.append(f"| {label} | {fmt(grid)} | {fmt(v['fetch_kib'])} | {fmt(v['write_kib'])} | "
+                     f"{fmt(b)} | {fmt(a)} | {b / a:.3f} |")
+    lines += ["", COUNTERS_NOTES]
+    with open(COUNTERS_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def code_text(text: str) -> str:
     """C++ source without its comments, trailing blanks and empty lines: an
     edit of a comment leaves the kernel, and so its counter figures, as they
@@ -100,10 +184,12 @@ def kernel_short_name(name: str) -> str:
     return name.split("(")[0]
 
 
-def summarize_counters(fetch_csv: str, write_csv: str) -> None:
+def summarize_counters(fetch_csv: str, write_csv: str, launch_info: str | None = None) -> None:
     """Turn two rocprofv3 --pmc runs of ``--profile-launches`` (FETCH_SIZE,
     then WRITE_SIZE, KiB per dispatch) into per-kernel HBM bytes, scaled by
-    what the same counters read for the 1 GiB calibration copy."""
+    what the same counters read for the 1 GiB calibration copy.  With the
+    ``--launch-info`` file of the counter run, also writes the markdown table
+    against each workload's algorithmic bytes."""
     import csv
     import statistics
 
@@ -141,6 +227,9 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
+    if launch_info:
+        with open(launch_info) as f:
+            write_counters_md(out, json.load(f))
     print(json.dumps(out, indent=1))
 
 
@@ -162,6 +251,10 @@ def parse():
     ap.add_argument("--profile-launches", type=int, default=0,
                     help="for counter runs under rocprofv3: launch every workload and a "
                          "plain 1 GiB calibration copy this many times, print no JSON")
+    ap.add_argument("--launch-info", default=None,
+                    help="with --profile-launches: write each workload's algorithmic bytes "
+                         "to this JSON file; with --summarize-counters: read it and write "
+                         "profiles/hbm_traffic_counters.md")
     return ap.parse_args()
 
 
@@ -623,10 +716,14 @@ def setup_calibration_copy(torch, psq, lib, dev, nbytes=1 << 30):
     return call, (src, dst, doc, cu, scal, ws)
 
 
-def profile_launches(torch, psq, lib, synth, dev, n):
+def profile_launches(torch, psq, lib, synth, dev, n, info_path=None):
     """Launch each workload n times (plus the calibration copy) for a
-    counter run; prints what ran, in launch order."""
-    runs = [("calibration_copy_1GiB", lambda: setup_calibration_copy(torch, psq, lib, dev))]
+    counter run; prints what ran, in launch order.  With ``info_path``, writes
+    each workload's algorithmic bytes there (the stage step also split into
+    its collapse copy and its map)."""
+    runs = [("calibration_copy_1GiB",
+             lambda: (lambda c: (c[0], None, 1 << 31, None, c[1]))(
+                 setup_calibration_copy(torch, psq, lib, dev)))]
     for name, setup in (("stage_embedding", lambda: setup_stage_embedding(torch, psq, lib, synth, dev)),
                         ("pack_sources", lambda: setup_pack(torch, psq, lib, synth, dev)),
                         ("thd_tables", lambda: setup_thd(torch, psq, lib, synth, dev)),
@@ -634,15 +731,23 @@ def profile_launches(torch, psq, lib, synth, dev, n):
                         ("thd_split_4", lambda: setup_split(torch, psq, lib, synth, dev)),
                         ("pad_tail_stream", lambda: setup_padids(torch, psq, lib, synth, dev)),
                         ("trainer_rectangle", lambda: setup_rect(torch, psq, lib, synth, dev))):
-        runs.append((name, (lambda st: (lambda: st()[::4]))(setup)))
+        runs.append((name, setup))
+    algo = {}
     for name, setup in runs:
-        call, keep = setup()
+        call, _, algo[name], info, keep = setup()
+        if name == "stage_embedding":
+            T, H = info["B"] * info["S"], info["H"]
+            algo["stage_copy"] = 4 * T * H + 16 * T     # bf16 hidden and int64 positions, read + write
+            algo["stage_map"] = algo[name] - algo["stage_copy"]
         torch.cuda.synchronize()
         for _ in range(n):
             call()
         torch.cuda.synchronize()
         print(f"[profile] {name}: {n} launches", file=sys.stderr, flush=True)
         del keep
+    if info_path:
+        with open(info_path, "w") as f:
+            json.dump(algo, f, indent=1)
 
 
 def roofline(algo_bytes, mean_ms, traffic=None):
@@ -750,7 +855,7 @@ def main():
         summarize_trace(*args.summarize_trace)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, launch_info=args.launch_info)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -770,7 +875,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.profile_launches > 0:
-        profile_launches(torch, psq, lib, synth, dev, args.profile_launches)
+        profile_launches(torch, psq, lib, synth, dev, args.profile_launches, args.launch_info)
         return
 
     call, tokens, algo, info, keep = setup_stage_embedding(torch, psq, lib, synth, dev)
