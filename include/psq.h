@@ -41,12 +41,15 @@
  *    device word *status (0 = success).  Output contents are unspecified
  *    when *status != 0, but every kernel stays inside the buffers described
  *    below whatever the data.
- *  - Workspace: query its size with the matching *_workspace() call, then
- *    zero-fill it once (psq_workspace_init, or any zero fill) before its
- *    first use.  Every call leaves the workspace zero-filled again when it
- *    completes, so the zero fill is needed only once per allocation.  A
- *    query returns 0 for sizes its call would reject (PSQ_ERR_ARG or
- *    PSQ_ERR_OVERFLOW).
+ *  - Workspace: query its size with the matching *_workspace() call; the
+ *    pointer must be 16-byte aligned (any device allocation is).  Zero-fill
+ *    it once (psq_workspace_init, or any zero fill) before its first use.
+ *    Every call leaves the parts it relies on zero-filled again when it
+ *    completes, so the zero fill is needed only once per allocation and one
+ *    workspace can serve every call on a stream.  (The document-map calls
+ *    keep scratch records in bytes 256 .. 256 + 16 KiB, which no other call
+ *    reads; they neither need nor restore zeros there.)  A query returns 0
+ *    for sizes its call would reject (PSQ_ERR_ARG or PSQ_ERR_OVERFLOW).
  *  - Grids: one HIP launch runs fewer than 2^32 threads.  Sizes that would
  *    need more in a call's metadata launch are PSQ_ERR_OVERFLOW; the limits
  *    are given with each call and lie far beyond the memory one GPU holds
@@ -75,7 +78,8 @@ extern "C" {
 #define PSQ_ERR_ARG       1   /* null required pointer, bad enum, bad size   */
 #define PSQ_ERR_OVERFLOW  2   /* a size does not fit int32 boundaries, or a
                                  call's copies do not fit one launch grid    */
-#define PSQ_ERR_WORKSPACE 3   /* workspace missing or smaller than required  */
+#define PSQ_ERR_WORKSPACE 3   /* workspace missing, smaller than required or
+                                 not 16-byte aligned                         */
 #define PSQ_ERR_HIP       4   /* the HIP runtime refused a launch            */
 
 /* data-dependent status bits (device word *status) */
@@ -87,7 +91,9 @@ extern "C" {
 #define PSQ_DATA_EMPTY_PACK     32   /* a pack has no member                  */
 #define PSQ_DATA_BAD_INDEX      64   /* member, pack or source out of range   */
 #define PSQ_DATA_WORKSPACE     128   /* workspace was not zero-filled (a
-                                        bounded wait or a bound check failed) */
+                                        bounded wait or a bound check failed;
+                                        for a document map: the map changed
+                                        during the call) */
 #define PSQ_DATA_PAD_IS_CONTENT 256  /* the pad id occurs before the pad tail */
 
 /* layouts accepted by psq_process_thd */
@@ -120,9 +126,16 @@ int psq_workspace_init(void *workspace, size_t bytes, void *stream);
  *   num_segments  int32 scalar n.
  *   max_seqlen    int32 scalar: the longest segment (padding runs count).
  *   padding_mask  uint8 [B*S] (1 where doc_ids == 0), or NULL to skip it.
- *   status        int32 scalar (only PSQ_DATA_WORKSPACE can occur), or NULL.
+ *   status        int32 scalar, or NULL.  Set to 0: a map has no invalid
+ *                 values.  PSQ_DATA_WORKSPACE reports a failed bound check,
+ *                 possible only when the map changes during the call.
  *   workspace     device scratch of psq_params_from_doc_ids_workspace(B, S)
- *                 bytes, zero-filled before first use.
+ *                 bytes (at most 256 + 16 KiB for any size), 16-byte
+ *                 aligned.  Its contents on entry do not matter.
+ * Two launches: one 16-byte record per workgroup (the range's boundary
+ * count, first and last boundary, and longest inner segment), then the
+ * boundaries, each workgroup starting at the sum of the counts before it.
+ * A map of at most 4096 positions takes one launch.
  * Host errors: PSQ_ERR_ARG (null pointer, B or S < 0, bad dtype),
  * PSQ_ERR_OVERFLOW (B*S >= 2^31), PSQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */

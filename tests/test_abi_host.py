@@ -88,6 +88,21 @@ def test_doc_ids_validation(lib):
     assert _doc(lib, ws=FAKE, wsb=8) == _lib.ERR_WORKSPACE
 
 
+def test_workspace_alignment(lib):
+    """A workspace that is not 16-byte aligned is refused by every call before
+    anything is enqueued (records are read as 16-byte vectors)."""
+    for off in (4, 8, 12):
+        assert _doc(lib, ws=FAKE + off, wsb=1 << 20) == _lib.ERR_WORKSPACE
+        assert _padids(lib, ws=FAKE + off) == _lib.ERR_WORKSPACE
+        assert _pack(lib, ws=FAKE + off) == _lib.ERR_WORKSPACE
+        assert _rect(lib, ws=FAKE + off) == _lib.ERR_WORKSPACE
+        lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, FAKE, FAKE, _lib.I64, 2)
+        assert _thd(lib, lay, ws=FAKE + off, wsb=1 << 20) == _lib.ERR_WORKSPACE
+        doc = _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=FAKE)
+        assert _thd(lib, doc, ws=FAKE + off, wsb=1 << 20) == _lib.ERR_WORKSPACE
+        assert _split(lib, lay, ws=FAKE + off, wsb=1 << 20) == _lib.ERR_WORKSPACE
+
+
 def _thd(lib, layout, copies=None, n_copies=0, **kw):
     a = dict(B=2, S=6, cu=FAKE, cp=None, n=FAKE, mx=FAKE, pb=FAKE, mask=None, st=FAKE,
              ws=FAKE, wsb=0, stream=None)

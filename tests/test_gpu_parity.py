@@ -105,6 +105,40 @@ def test_doc_fuzz(dev, B, S, kind):
         check_doc(dev, d.astype(np.int64) * (1 << 32) + 7, torch.int64)
 
 
+def _long_runs(rng, B, S, mean):
+    """Rows of runs with geometric lengths of the given mean, a tenth of them
+    padding; built with vector operations (the maps here hold millions of
+    positions)."""
+    d = np.empty((B, S), dtype=np.int32)
+    for r in range(B):
+        lens = rng.geometric(1.0 / mean, size=S // max(int(mean) // 4, 1) + 8)
+        ends = np.cumsum(lens)
+        k = int(np.searchsorted(ends, S)) + 1
+        ids = np.arange(1, k + 1, dtype=np.int32)
+        ids[rng.random(k) < 0.1] = 0
+        d[r] = np.repeat(ids, np.diff(np.concatenate([[0], np.minimum(ends[:k], S)])))
+    return d
+
+
+@pytest.mark.parametrize("B,S", [(1, 4096 * 1024 + 1), (3, 2100000), (2, 4200000),
+                                 (1, 3 * 4096 * 1024 + 7)])
+@pytest.mark.parametrize("kind", ["runs", "long_runs", "const", "two_then_one"])
+def test_doc_many_chunks_per_workgroup(dev, B, S, kind):
+    """Maps of more than 1024 chunks of 4096 positions: each workgroup of the
+    two launches walks several chunks, and segments cross workgroups."""
+    rng = np.random.default_rng(S * 7 + B)
+    if kind == "runs":
+        d = _long_runs(rng, B, S, 300)
+    elif kind == "long_runs":
+        d = _long_runs(rng, B, S, 60000)       # most workgroups hold no boundary
+    elif kind == "const":
+        d = np.ones((B, S), dtype=np.int32)     # one segment per row
+    else:
+        d = np.full((B, S), 2, dtype=np.int32)  # every boundary in the first chunk of a row
+        d[:, 0] = 1
+    check_doc(dev, d)
+
+
 def test_doc_unaligned_input(dev):
     # a view that starts 4 bytes into its storage: the scalar-load path
     d = synth.doc_map_medium()
@@ -150,18 +184,49 @@ def test_doc_python_api(dev):
     assert kw["max_length_q"] == kw["max_length_k"] == p.max_seqlen
 
 
+DOC_RECORDS = (256, 256 + 16384)     # the document-map records: scratch, never zeroed
+
+
+def _nonzero_outside(ws, lo, hi):
+    torch.cuda.synchronize()
+    w = ws.clone()
+    w[lo:hi] = 0
+    return int(w.count_nonzero())
+
+
 def test_workspace_left_zeroed(dev):
+    """The parts of the shared workspace that calls rely on finding zero stay
+    zero; the document-map calls write only into their record region (which
+    still holds the records of earlier, larger maps of this process)."""
     d = synth.doc_map_medium()
     run_doc(dev, d)
     ws = psq.workspace_for(dev, 0)
-    torch.cuda.synchronize()
-    assert int(ws.count_nonzero()) == 0
+    assert _nonzero_outside(ws, *DOC_RECORDS) == 0
     L = torch.tensor([[3, 2], [6, V]], device=dev)
     psq.process_input_for_thd({"input_ids": torch.zeros((2, 6), dtype=torch.int64, device=dev),
                                "position_ids": torch.zeros((2, 6), dtype=torch.int64, device=dev),
                                "seq_lens": L})
-    torch.cuda.synchronize()
-    assert int(psq.workspace_for(dev, 0).count_nonzero()) == 0
+    assert _nonzero_outside(psq.workspace_for(dev, 0), *DOC_RECORDS) == 0
+
+
+def test_doc_records_do_not_disturb_tables(dev):
+    """A multi-workgroup table call (look-back descriptors after the record
+    region) on the workspace a large document map has just used."""
+    run_doc(dev, synth.stage_embedding()["doc_ids"])
+    rng = np.random.default_rng(11)
+    B, P, S = 1100, 4, 64
+    L = rng.integers(0, 9, size=(B, P)).astype(np.int64)
+    Lp = L + 8 - L % 8
+    Lp[:, 3] = V
+    L[:, 3] = V
+    say("tables 1100x4 after a document map")
+    got = run_thd_raw(dev, L, Lp, S)
+    ref = oracle.thd_tables(L, Lp, S)
+    assert got["status"] == 0
+    for k in ("cu_seqlens", "cu_seqlens_padded", "padding_mask"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["max_seqlen"] == ref["max_seqlen"]
+    assert _nonzero_outside(psq.workspace_for(dev, 0), *DOC_RECORDS) == 0
 
 
 # ---------------------------------------------------------------------------

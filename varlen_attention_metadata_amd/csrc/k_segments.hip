@@ -1,4 +1,4 @@
-// k_segments.hip -- document map -> segment boundaries, in one pass.
+// k_segments.hip -- document map -> segment boundaries: reduce, then scatter.
 //
 // NeMo AutoModel API, nemo_automodel.components.datasets.packed_seq:
 // packed_seq_params_from_doc_ids.  A segment is a maximal run of one
@@ -9,15 +9,31 @@
 // cu_seqlens); max_seqlen is the longest segment, padding runs included
 // (PackedSeqParams.max_seqlen).  The padding mask marks doc == 0.
 //
-// Layout of the work: a tile of 4096 positions per 256-thread workgroup;
-// each wave owns 1024 consecutive positions, visited as 4 chunks of 256 with
-// 4 consecutive positions per lane (one 16-byte load for int32 maps).  Each
-// lane folds its 4 boundary flags into a bit mask; DPP wave scans turn the
-// popcounts into output slots, and a max scan of "last boundary + 1" gives
-// every boundary the start of the segment before it.  Tiles are chained by
-// a decoupled look-back whose descriptors carry (boundary count, last
-// boundary + 1), so the compaction and the longest-segment reduction finish
-// in the same pass.
+// Layout of the work: a chunk of 4096 positions per pass of a 256-thread
+// workgroup; each wave owns 1024 consecutive positions of the chunk, visited
+// as 4 sub-chunks of 256 with 4 consecutive positions per lane (one 16-byte
+// load for int32 maps).  Each lane folds its 4 boundary flags into a bit
+// mask; DPP wave scans turn the popcounts into output slots, and a max scan
+// of "last boundary + 1" gives every boundary the start of the segment
+// before it.
+//
+// Two launches with no cross-workgroup protocol.  Workgroup g owns `cpw`
+// consecutive chunks (one each, unless the map holds more than 1024 chunks).
+//  1. k_doc_reduce: each workgroup reduces its range to a 16-byte record --
+//     boundary count, first boundary, last boundary + 1, and the longest
+//     segment between two of its own boundaries -- and writes the mask.
+//  2. k_doc_scatter: each workgroup sums the counts of the records before
+//     its own (its first output slot) and takes the latest boundary among
+//     them, then reads its range again (just read by launch 1, so mostly
+//     cached) and writes its boundaries.  The last workgroup closes the axis
+//     and derives max_seqlen from all records: their interior maxima, the
+//     segments that run from one record's last boundary to the next
+//     record's first, and the closing segment.
+// No workgroup waits for another and nothing is counted: the kernel
+// boundary orders launch 1's record stores before launch 2's loads, and the
+// records need no clearing (every call writes before it reads), which also
+// makes the call safe to replay from a HIP graph.  A map of at most one
+// chunk is one workgroup in one launch and uses no records.
 #include "psq_device.hpp"
 #include "psq_internal.hpp"
 
@@ -28,9 +44,19 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kIters = 4;
 constexpr int kPerLane = 4;
-constexpr uint32_t kChunk = kWave * kPerLane;          // 256 positions
-constexpr uint32_t kWaveSpan = kChunk * kIters;        // 1024 positions
-constexpr uint32_t kTile = kWaveSpan * kWaves;         // 4096 positions
+constexpr uint32_t kSub = kWave * kPerLane;            // 256 positions
+constexpr uint32_t kWaveSpan = kSub * kIters;          // 1024 positions
+constexpr uint32_t kChunk = kWaveSpan * kWaves;        // 4096 positions
+constexpr int kRecsPerThread = (int)(kDocMaxGroups / kThreads);
+static_assert(kDocMaxGroups % kThreads == 0, "records are spread evenly over the threads");
+
+// One workgroup's range: boundary count, first boundary, one past the last
+// boundary (0 = none), and the longest segment between two boundaries of the
+// range.  first / last1 / imax are 0 when cnt is 0.
+struct DocRec {
+    uint32_t cnt, first, last1, imax;
+};
+static_assert(sizeof(DocRec) == 16, "records are read as 16-byte vectors");
 
 template <typename T>
 __device__ __forceinline__ int load4(const T *__restrict__ doc, uint32_t pos0, uint32_t total,
@@ -84,149 +110,289 @@ __device__ __forceinline__ T bcast_lane(T x, int lane) {
 }
 
 template <typename T>
-struct DocSegArgs {
+struct DocArgs {
     const T *doc;
-    uint32_t S, total, n_tiles;
+    uint32_t S, total;
+    uint32_t n_chunks, cpw, n_groups;   // chunks of kChunk, chunks per group, groups
     int vec_in, vec_mask;
     int32_t *cu, *cu2, *num_segments, *max_seqlen;
     uint8_t *mask;
     int32_t *status, *pad_between;
-    WsHeader *ws;
+    DocRec *recs;                       // n_groups records (multi-group maps)
 };
 
-// One tile per workgroup; `n_groups` is the number of workgroups running
-// this body (the launch may append copy workgroups after them).
+// Boundary flags of the 1024 positions a wave owns from wave_base (positions
+// at or past `total` are absent).  For sub-chunk j: fm[j] holds the lane's 4
+// flags (bit k: position pos0 + k), off[j] counts the wave's boundaries
+// before the lane's first position, and prv[j] is one past the wave's last
+// boundary before the lane's positions (0: none yet in this wave).  *cnt and
+// *last1 return the wave's count and one past its last boundary (0: none).
+// With `mask`, also writes mask[t] = (doc[t] == 0).
 template <typename T>
-__device__ __forceinline__ void doc_segments_body(
-    const T *__restrict__ doc, uint32_t S, uint32_t total, uint32_t n_tiles, int vec_in,
-    int vec_mask, int32_t *__restrict__ cu, int32_t *__restrict__ cu2,
-    int32_t *__restrict__ num_segments, int32_t *__restrict__ max_seqlen,
-    uint8_t *__restrict__ mask, int32_t *__restrict__ status,
-    int32_t *__restrict__ pad_between, WsHeader *__restrict__ ws, uint32_t n_groups) {
-    __shared__ uint32_t s_slot;
-    __shared__ uint32_t s_wcnt[kWaves], s_wlast[kWaves];
-    __shared__ uint32_t s_ex_a, s_ex_b;
-    __shared__ int32_t s_max;
-    __shared__ uint32_t s_err;
-
-    uint64_t *desc = (uint64_t *)((char *)ws + kWsDescOffset);
-    if (threadIdx.x == 0) {
-        s_max = 0;
-        s_err = 0;
-        s_ex_a = 0;
-        s_ex_b = 0;
-    }
-    // A map of one tile is one workgroup: it needs no ticket, no look-back and
-    // no completion counter, and leaves the workspace untouched.
-    const bool solo = n_groups == 1 && n_tiles <= 1;
-    uint32_t tile = 0;
-    if (solo)
-        __syncthreads();
-    else
-        tile = claim_tile(ws, &s_slot);
-    const int w = threadIdx.x / kWave;
+__device__ __forceinline__ void wave_flags(const T *__restrict__ doc, uint32_t S, uint32_t total,
+                                           int vec_in, uint8_t *__restrict__ mask, int vec_mask,
+                                           uint32_t wave_base, uint32_t (&fm)[kIters],
+                                           uint32_t (&off)[kIters], uint32_t (&prv)[kIters],
+                                           uint32_t *cnt, uint32_t *last1) {
     const int lane = lane_id();
+    T carry = (T)0;
+    if (wave_base > 0 && wave_base < total) carry = doc[wave_base - 1];
 
-    if (total == 0) {
-        // empty map: cu_seqlens = [0], no segments
-        if (threadIdx.x == 0) {
-            cu[0] = 0;
-            if (cu2) cu2[0] = 0;
-            *num_segments = 0;
-        }
-    } else if (tile >= n_tiles) {
-        if (threadIdx.x == 0) s_err = PSQ_DATA_WORKSPACE;
-    } else {
-        // ---------------- phase 1: flags, masks and local scans ----------
-        const uint32_t wave_base = tile * kTile + (uint32_t)w * kWaveSpan;
-        T carry = (T)0;
-        if (wave_base > 0 && wave_base < total) carry = doc[wave_base - 1];
-
-        // All of the wave's loads are issued before any is used.  A wave whose
-        // whole span is in range takes straight-line vector loads (a uniform
-        // branch); per-chunk branches would make the compiler wait for each
-        // load before issuing the next.
-        T dall[kIters][kPerLane];
-        int pres[kIters];
-        if (vec_in && wave_base + kWaveSpan <= total) {
-#pragma unroll
-            for (int j = 0; j < kIters; ++j) {
-                const uint32_t pos0 = wave_base + (uint32_t)j * kChunk + (uint32_t)lane * kPerLane;
-                if constexpr (sizeof(T) == 4) {
-                    const i32x4 v = *(const i32x4 *)(doc + pos0);
-                    dall[j][0] = v.x; dall[j][1] = v.y; dall[j][2] = v.z; dall[j][3] = v.w;
-                } else {
-                    const i64x2 v0 = *(const i64x2 *)(doc + pos0);
-                    const i64x2 v1 = *(const i64x2 *)(doc + pos0 + 2);
-                    dall[j][0] = v0.x; dall[j][1] = v0.y; dall[j][2] = v1.x; dall[j][3] = v1.y;
-                }
-                pres[j] = kPerLane;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kIters; ++j) {
-                const uint32_t pos0 = wave_base + (uint32_t)j * kChunk + (uint32_t)lane * kPerLane;
-                pres[j] = load4(doc, pos0, total, vec_in != 0, dall[j]);
-            }
-        }
-
-        uint32_t fm[kIters], off[kIters], prv[kIters];
-        uint32_t run_c = 0, run_l = 0;
-        const bool small_s = S < (uint32_t)kPerLane;
+    // All of the wave's loads are issued before any is used.  A wave whose
+    // whole span is in range takes straight-line vector loads (a uniform
+    // branch); per-chunk branches would make the compiler wait for each load
+    // before issuing the next.
+    T dall[kIters][kPerLane];
+    int pres[kIters];
+    if (vec_in && wave_base + kWaveSpan <= total) {
 #pragma unroll
         for (int j = 0; j < kIters; ++j) {
-            const uint32_t pos0 = wave_base + (uint32_t)j * kChunk + (uint32_t)lane * kPerLane;
-            const T *d = dall[j];
-            const int present = pres[j];
-
-            if (mask != nullptr && present > 0) {
-                if (present == kPerLane && vec_mask) {
-                    const uint32_t m = (uint32_t)(d[0] == 0) | ((uint32_t)(d[1] == 0) << 8) |
-                                       ((uint32_t)(d[2] == 0) << 16) | ((uint32_t)(d[3] == 0) << 24);
-                    *(uint32_t *)(mask + pos0) = m;
-                } else {
-                    for (int k = 0; k < present; ++k) mask[pos0 + k] = (uint8_t)(d[k] == 0);
-                }
+            const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+            if constexpr (sizeof(T) == 4) {
+                const i32x4 v = *(const i32x4 *)(doc + pos0);
+                dall[j][0] = v.x; dall[j][1] = v.y; dall[j][2] = v.z; dall[j][3] = v.w;
+            } else {
+                const i64x2 v0 = *(const i64x2 *)(doc + pos0);
+                const i64x2 v1 = *(const i64x2 *)(doc + pos0 + 2);
+                dall[j][0] = v0.x; dall[j][1] = v0.y; dall[j][2] = v1.x; dall[j][3] = v1.y;
             }
-
-            const T left = shr1(d[kPerLane - 1], carry);
-            uint32_t f = 0;
-            if (present > 0) {
-                const uint32_t r = pos0 % S;
-#pragma unroll
-                for (int k = 0; k < kPerLane; ++k) {
-                    if (k < present) {
-                        bool row_start;
-                        if (small_s)
-                            row_start = ((pos0 + (uint32_t)k) % S) == 0;
-                        else
-                            row_start = (r + (uint32_t)k == 0) || (r + (uint32_t)k == S);
-                        const T prev = (k == 0) ? left : d[k == 0 ? 0 : k - 1];
-                        const bool new_doc = d[k] != prev;
-                        if (row_start || new_doc) f |= 1u << k;
-                    }
-                }
-            }
-            const uint32_t c = (uint32_t)__builtin_popcount(f);
-            const uint32_t last1 = f ? pos0 + (31u - (uint32_t)__builtin_clz(f)) + 1u : 0u;
-            const uint32_t incl_c = (uint32_t)wave_incl_sum((int)c);
-            const uint32_t incl_l = (uint32_t)wave_incl_max((int)last1);
-            const uint32_t excl_l = (uint32_t)wave_shr1((int)incl_l, 0);
-            fm[j] = f;
-            off[j] = run_c + incl_c - c;
-            prv[j] = excl_l ? excl_l : run_l;
-            run_c += (uint32_t)read_lane((int)incl_c, kWave - 1);
-            const uint32_t tl = (uint32_t)read_lane((int)incl_l, kWave - 1);
-            if (tl) run_l = tl;
-            carry = bcast_lane(d[kPerLane - 1], kWave - 1);
+            pres[j] = kPerLane;
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kIters; ++j) {
+            const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+            pres[j] = load4(doc, pos0, total, vec_in != 0, dall[j]);
+        }
+    }
+
+    uint32_t run_c = 0, run_l = 0;
+    const bool small_s = S < (uint32_t)kPerLane;
+#pragma unroll
+    for (int j = 0; j < kIters; ++j) {
+        const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+        const T *d = dall[j];
+        const int present = pres[j];
+
+        if (mask != nullptr && present > 0) {
+            if (present == kPerLane && vec_mask) {
+                const uint32_t m = (uint32_t)(d[0] == 0) | ((uint32_t)(d[1] == 0) << 8) |
+                                   ((uint32_t)(d[2] == 0) << 16) | ((uint32_t)(d[3] == 0) << 24);
+                *(uint32_t *)(mask + pos0) = m;
+            } else {
+                for (int k = 0; k < present; ++k) mask[pos0 + k] = (uint8_t)(d[k] == 0);
+            }
+        }
+
+        const T left = shr1(d[kPerLane - 1], carry);
+        uint32_t f = 0;
+        if (present > 0) {
+            const uint32_t r = pos0 % S;
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                if (k < present) {
+                    bool row_start;
+                    if (small_s)
+                        row_start = ((pos0 + (uint32_t)k) % S) == 0;
+                    else
+                        row_start = (r + (uint32_t)k == 0) || (r + (uint32_t)k == S);
+                    const T prev = (k == 0) ? left : d[k == 0 ? 0 : k - 1];
+                    if (row_start || d[k] != prev) f |= 1u << k;
+                }
+            }
+        }
+        const uint32_t c = (uint32_t)__builtin_popcount(f);
+        const uint32_t l1 = f ? pos0 + (31u - (uint32_t)__builtin_clz(f)) + 1u : 0u;
+        const uint32_t incl_c = (uint32_t)wave_incl_sum((int)c);
+        const uint32_t incl_l = (uint32_t)wave_incl_max((int)l1);
+        const uint32_t excl_l = (uint32_t)wave_shr1((int)incl_l, 0);
+        fm[j] = f;
+        off[j] = run_c + incl_c - c;
+        prv[j] = excl_l ? excl_l : run_l;
+        run_c += (uint32_t)read_lane((int)incl_c, kWave - 1);
+        const uint32_t tl = (uint32_t)read_lane((int)incl_l, kWave - 1);
+        if (tl) run_l = tl;
+        carry = bcast_lane(d[kPerLane - 1], kWave - 1);
+    }
+    *cnt = run_c;
+    *last1 = run_l;
+}
+
+// ---------------------------------------------------------------------------
+// Launch 1: one record per workgroup, and the padding mask.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_doc_reduce(DocArgs<T> a) {
+    __shared__ uint32_t s_cnt[kWaves], s_first[kWaves], s_last[kWaves], s_imax[kWaves];
+    const int w = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const uint32_t c0 = blockIdx.x * a.cpw;
+    const uint32_t c1 = min(c0 + a.cpw, a.n_chunks);
+    DocRec rec{0u, 0u, 0u, 0u};                 // accumulated by thread 0
+    for (uint32_t c = c0; c < c1; ++c) {
+        const uint32_t wave_base = c * kChunk + (uint32_t)w * kWaveSpan;
+        uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
+        wave_flags(a.doc, a.S, a.total, a.vec_in, a.mask, a.vec_mask, wave_base, fm, off, prv,
+                   &cnt, &last1);
+        // the wave's first boundary, and its longest segment that starts at
+        // one of its own boundaries and ends at the next
+        uint32_t first = 0;
+        bool seen = false;
+        int32_t lmax = 0;
+#pragma unroll
+        for (int j = 0; j < kIters; ++j) {
+            const uint32_t f = fm[j];
+            const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+            const uint64_t any = __ballot(f != 0u);
+            if (!seen && any) {
+                const int l = __builtin_ctzll(any);
+                const uint32_t mine = f ? pos0 + (uint32_t)__builtin_ctz(f) : 0u;
+                first = (uint32_t)read_lane((int)mine, l);
+                seen = true;
+            }
+            uint32_t p = prv[j];
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                if ((f >> k) & 1u) {
+                    const uint32_t pos = pos0 + (uint32_t)k;
+                    if (p) lmax = max(lmax, (int32_t)(pos + 1u - p));
+                    p = pos + 1u;
+                }
+            }
+        }
+        lmax = wave_incl_max(lmax);
+        if (lane == kWave - 1) s_imax[w] = (uint32_t)lmax;
         if (lane == 0) {
-            s_wcnt[w] = run_c;
-            s_wlast[w] = run_l;
+            s_cnt[w] = cnt;
+            s_first[w] = first;
+            s_last[w] = last1;
         }
         __syncthreads();
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                if (s_cnt[v]) {
+                    if (rec.cnt)
+                        rec.imax = max(rec.imax, s_first[v] + 1u - rec.last1);
+                    else
+                        rec.first = s_first[v];
+                    rec.cnt += s_cnt[v];
+                    rec.last1 = s_last[v];
+                }
+                rec.imax = max(rec.imax, s_imax[v]);
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        *(u32x4 *)(a.recs + blockIdx.x) = u32x4{rec.cnt, rec.first, rec.last1, rec.imax};
+}
 
-        // tile aggregate and this wave's prefix inside the tile
+// Block-wide sum of x and maxima of y and z (non-negative), returned to every
+// thread.
+__device__ __forceinline__ void block_sum_max_max(uint32_t &x, uint32_t &y, uint32_t &z,
+                                                  uint32_t (&s)[3][kWaves]) {
+    const int w = threadIdx.x / kWave;
+    x = (uint32_t)read_lane(wave_incl_sum((int)x), kWave - 1);
+    y = (uint32_t)read_lane(wave_incl_max((int)y), kWave - 1);
+    z = (uint32_t)read_lane(wave_incl_max((int)z), kWave - 1);
+    if (lane_id() == 0) {
+        s[0][w] = x;
+        s[1][w] = y;
+        s[2][w] = z;
+    }
+    __syncthreads();
+    x = 0;
+    y = 0;
+    z = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        x += s[0][v];
+        y = max(y, s[1][v]);
+        z = max(z, s[2][v]);
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2 (or the only launch of a one-chunk map, kSolo): the boundaries.
+// ---------------------------------------------------------------------------
+template <typename T, bool kSolo>
+__global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
+    __shared__ uint32_t s_wcnt[kWaves], s_wlast[kWaves];
+    __shared__ uint32_t s_red[3][kWaves];
+    __shared__ int32_t s_max;
+    const int w = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const uint32_t g = blockIdx.x;
+    const bool last = g == a.n_groups - 1;
+
+    // ---- the records before this group: its first output slot (base_c) and
+    // one past the boundary before its range (base_l); the last group also
+    // takes the longest segment the records describe
+    uint32_t base_c = 0, base_l = 0, rec_max = 0;
+    if constexpr (!kSolo) {
+        const uint32_t nread = last ? a.n_groups : g;
+        DocRec r[kRecsPerThread];
+        uint32_t c_sum = 0, l_pre = 0, l_mine = 0;
+#pragma unroll
+        for (int i = 0; i < kRecsPerThread; ++i) {
+            const uint32_t idx = threadIdx.x * (uint32_t)kRecsPerThread + (uint32_t)i;
+            r[i] = DocRec{0u, 0u, 0u, 0u};
+            if (idx < nread) {
+                const u32x4 v = *(const u32x4 *)(a.recs + idx);
+                r[i] = DocRec{v.x, v.y, v.z, v.w};
+            }
+            if (idx < g) {
+                c_sum += r[i].cnt;
+                l_pre = max(l_pre, r[i].last1);
+            }
+            l_mine = max(l_mine, r[i].last1);
+        }
+        uint32_t m = 0;
+        if (last) {
+            // one past the last boundary of the records before this thread's
+            // own: an exclusive max scan over the threads, in record order
+            const uint32_t incl = (uint32_t)wave_incl_max((int)l_mine);
+            if (lane == kWave - 1) s_red[0][w] = incl;
+            __syncthreads();
+            uint32_t p = (uint32_t)wave_shr1((int)incl, 0);
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v)
+                if (v < w) p = max(p, s_red[0][v]);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kRecsPerThread; ++i) {
+                if (r[i].cnt) {
+                    if (p) m = max(m, r[i].first + 1u - p);
+                    m = max(m, r[i].imax);
+                    p = r[i].last1;
+                }
+            }
+        }
+        block_sum_max_max(c_sum, l_pre, m, s_red);
+        base_c = c_sum;
+        base_l = l_pre;
+        rec_max = m;
+    }
+    if (threadIdx.x == 0) s_max = 0;
+
+    // ---- this group's chunks
+    const uint32_t c0 = g * a.cpw;
+    const uint32_t c1 = min(c0 + a.cpw, a.n_chunks);
+    int32_t lmax = 0;
+    bool oob = false;
+    for (uint32_t c = c0; c < c1; ++c) {
+        const uint32_t wave_base = c * kChunk + (uint32_t)w * kWaveSpan;
+        uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
+        wave_flags(a.doc, a.S, a.total, a.vec_in, kSolo ? a.mask : nullptr, a.vec_mask,
+                   wave_base, fm, off, prv, &cnt, &last1);
+        if (lane == 0) {
+            s_wcnt[w] = cnt;
+            s_wlast[w] = last1;
+        }
+        __syncthreads();
+        // the chunk's totals and this wave's prefix inside the chunk
         uint32_t agg_c = 0, agg_l = 0, pc = 0, pl = 0;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
@@ -237,137 +403,99 @@ __device__ __forceinline__ void doc_segments_body(
             agg_c += s_wcnt[v];
             if (s_wlast[v]) agg_l = s_wlast[v];
         }
-
-        // ---------------- decoupled look-back (wave 0) --------------------
-        if (w == 0) {
-            if (tile == 0) {
-                if (lane == 0 && !solo) st_relaxed(desc, desc_pack(kDescIncl, agg_c, agg_l));
-            } else {
-                jitter(5);
-                if (lane == 0) st_relaxed(desc + tile, desc_pack(kDescAgg, agg_c, agg_l));
-                uint32_t ex_a, ex_b;
-                bool timed_out;
-                lookback<false>(desc, tile, &ex_a, &ex_b, &timed_out);
-                if (lane == 0) {
-                    st_relaxed(desc + tile, desc_pack(kDescIncl, ex_a + agg_c, agg_l ? agg_l : ex_b));
-                    s_ex_a = ex_a;
-                    s_ex_b = ex_b;
-                    if (timed_out) s_err = PSQ_DATA_WORKSPACE;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---------------- phase 2: write boundaries ----------------------
-        const uint32_t base_c = s_ex_a + pc;
-        const uint32_t base_l = pl ? pl : s_ex_b;
-        int32_t lmax = 0;
-        bool oob = false;
+        const uint32_t bc = base_c + pc;
+        const uint32_t bl = pl ? pl : base_l;
 #pragma unroll
         for (int j = 0; j < kIters; ++j) {
-            uint32_t f = fm[j];
+            const uint32_t f = fm[j];
             if (f) {
-                const uint32_t pos0 = wave_base + (uint32_t)j * kChunk + (uint32_t)lane * kPerLane;
-                uint32_t o = base_c + off[j];
-                uint32_t p = prv[j] ? prv[j] : base_l;
+                const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+                uint32_t o = bc + off[j];
+                uint32_t p = prv[j] ? prv[j] : bl;
 #pragma unroll
                 for (int k = 0; k < kPerLane; ++k) {
                     if ((f >> k) & 1u) {
                         const uint32_t pos = pos0 + (uint32_t)k;
-                        if (o < total) {
-                            cu[o] = (int32_t)pos;
-                            if (cu2) cu2[o] = (int32_t)pos;
+                        if (o < a.total) {
+                            a.cu[o] = (int32_t)pos;
+                            if (a.cu2) a.cu2[o] = (int32_t)pos;
                         } else {
                             oob = true;
                         }
-                        if (p) lmax = max(lmax, (int32_t)(pos + 1u - p));
+                        if (kSolo && p) lmax = max(lmax, (int32_t)(pos + 1u - p));
                         p = pos + 1u;
                         ++o;
                     }
                 }
             }
         }
-        if (tile == n_tiles - 1 && threadIdx.x == 0) {
-            // the last tile closes the flattened axis
-            const uint32_t n = s_ex_a + agg_c;
-            const uint32_t last1 = agg_l ? agg_l : s_ex_b;
-            if (n <= total) {
-                cu[n] = (int32_t)total;
-                if (cu2) cu2[n] = (int32_t)total;
-                *num_segments = (int32_t)n;
-            } else {
-                oob = true;
-            }
-            if (last1) lmax = max(lmax, (int32_t)(total + 1u - last1));
-        }
-        if (oob) atomicOr(&s_err, (uint32_t)PSQ_DATA_WORKSPACE);
-        // wave max, then one LDS atomic per wave
+        base_c += agg_c;
+        if (agg_l) base_l = agg_l;
+        __syncthreads();
+    }
+    if constexpr (kSolo) {
         lmax = wave_incl_max(lmax);
         if (lane == kWave - 1) atomicMax(&s_max, lmax);
-    }
-    __syncthreads();
-    if (solo) {
-        if (threadIdx.x == 0) {
-            *max_seqlen = s_max;
-            if (status) *status = (int32_t)s_err;
-            if (pad_between) *pad_between = 0;
-        }
-        return;
-    }
-    if (threadIdx.x == 0) {
-        if (s_max > 0) max_relaxed(&ws->max, s_max);
-        if (s_err) or_relaxed(&ws->status, s_err);
-    }
-
-    if (finish_is_last(ws, n_groups, &s_slot)) {
-        if (threadIdx.x == 0) {
-            *max_seqlen = (int32_t)ld_relaxed((const uint32_t *)&ws->max);
-            const uint32_t st = ld_relaxed(&ws->status);
-            if (status) *status = (int32_t)st;
-            if (pad_between) *pad_between = 0;
-            st_relaxed((uint32_t *)&ws->max, 0u);
-            st_relaxed(&ws->status, 0u);
-            st_relaxed(&ws->ticket, 0u);
-        }
-        for (uint32_t i = threadIdx.x; i < n_tiles; i += kThreads) st_relaxed(desc + i, 0ull);
         __syncthreads();
-        if (threadIdx.x == 0) st_relaxed(&ws->done, 0u);
+    }
+    // a failed bound check (the map changed between the launches) is the
+    // only data error this path can meet; it only reaches the status when it
+    // happens in the last group
+    if (last && threadIdx.x == 0) {
+        const uint32_t n = base_c;
+        int32_t mx = kSolo ? s_max : (int32_t)rec_max;
+        uint32_t st = oob ? (uint32_t)PSQ_DATA_WORKSPACE : 0u;
+        if (n <= a.total) {
+            a.cu[n] = (int32_t)a.total;
+            if (a.cu2) a.cu2[n] = (int32_t)a.total;
+            *a.num_segments = (int32_t)n;
+        } else {
+            st = PSQ_DATA_WORKSPACE;
+        }
+        if (base_l) mx = max(mx, (int32_t)(a.total + 1u - base_l));
+        *a.max_seqlen = mx;
+        if (a.status) *a.status = (int32_t)st;
+        if (a.pad_between) *a.pad_between = 0;
     }
 }
 
-#define PSQ_DOC_ARGS(a)                                                                       \
-    a.doc, a.S, a.total, a.n_tiles, a.vec_in, a.vec_mask, a.cu, a.cu2, a.num_segments,       \
-        a.max_seqlen, a.mask, a.status, a.pad_between, a.ws
-
+// The metadata launches, then the collapse copies in one-wave workgroups.
+// The copies are not fused into the metadata grid: on MI355X the 8 GiB
+// collapse of the stage-embedding workload streamed 3 % faster in its own
+// launch of one-wave workgroups (1 KiB each) than as 256-thread workgroups
+// appended to the metadata grid.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_doc_segments(DocSegArgs<T> a) {
-    doc_segments_body<T>(PSQ_DOC_ARGS(a), gridDim.x);
-}
-
-#undef PSQ_DOC_ARGS
-
-// The metadata launch, then the collapse copies in one-wave workgroups.  The
-// copies are not fused into the metadata grid: on MI355X the 8 GiB collapse
-// of the stage-embedding workload streamed 3 % faster in its own launch of
-// one-wave workgroups (1 KiB each) than as 256-thread workgroups appended to
-// the metadata grid, and a fused grid of one-wave workgroups was slower
-// again (the look-back chain over 4x as many tiles).
-template <typename T>
-hipError_t launch_typed(DocSegArgs<T> a, const psq_copy *copies, int n_copies,
+hipError_t launch_typed(DocArgs<T> a, const psq_copy *copies, int n_copies,
                         hipStream_t stream) {
-    const uint32_t n_meta = a.n_tiles > 0 ? a.n_tiles : 1u;
-    hipLaunchKernelGGL(k_doc_segments<T>, dim3(n_meta), dim3(kThreads), 0, stream, a);
+    if (a.n_chunks <= 1) {
+        hipLaunchKernelGGL((k_doc_scatter<T, true>), dim3(1), dim3(kThreads), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(k_doc_reduce<T>, dim3(a.n_groups), dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_doc_scatter<T, false>), dim3(a.n_groups), dim3(kThreads), 0,
+                           stream, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_copies == 0) return e;
     return launch_copies(copies, n_copies, stream);
 }
 
+// Chunks, chunks per group and groups of a map of `total` positions.
+void doc_grid(uint32_t total, uint32_t *n_chunks, uint32_t *cpw, uint32_t *n_groups) {
+    const uint32_t nc = (uint32_t)(((uint64_t)total + kChunk - 1) / kChunk);
+    const uint32_t per = nc > kDocMaxGroups ? (nc + kDocMaxGroups - 1) / kDocMaxGroups : 1u;
+    *n_chunks = nc;
+    *cpw = per;
+    *n_groups = nc <= 1 ? 1u : (nc + per - 1) / per;
+}
+
 }  // namespace
 
 size_t doc_segments_workspace(int64_t B, int64_t S) {
-    const int64_t total = B * S;
-    const int64_t tiles = (total + kTile - 1) / kTile;
-    return round_up(kWsDescOffset + 8 * (size_t)(tiles > 0 ? tiles : 1), 256);
+    uint32_t nc, cpw, ng;
+    doc_grid((uint32_t)(B * S), &nc, &cpw, &ng);
+    return round_up(kWsDocOffset + sizeof(DocRec) * (size_t)ng, 256);
 }
 
 hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_t S,
@@ -376,18 +504,19 @@ hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_
                                int32_t *pad_between, void *workspace, const psq_copy *copies,
                                int n_copies, hipStream_t stream) {
     const uint32_t total = (uint32_t)(B * S);
-    const uint32_t n_tiles = (total + kTile - 1) / kTile;
+    uint32_t nc, cpw, ng;
+    doc_grid(total, &nc, &cpw, &ng);
     const int vec_in = ((uintptr_t)doc % 16) == 0;
     const int vec_mask = ((uintptr_t)mask % 4) == 0;
-    WsHeader *ws = (WsHeader *)workspace;
+    DocRec *recs = (DocRec *)((char *)workspace + kWsDocOffset);
     if (doc_dtype == PSQ_I32) {
-        DocSegArgs<int32_t> a{(const int32_t *)doc, (uint32_t)S, total, n_tiles, vec_in,
-                              vec_mask, cu, cu2, num_segments, max_seqlen, mask, status,
-                              pad_between, ws};
+        DocArgs<int32_t> a{(const int32_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in,
+                           vec_mask, cu, cu2, num_segments, max_seqlen, mask, status,
+                           pad_between, recs};
         return launch_typed(a, copies, n_copies, stream);
     }
-    DocSegArgs<int64_t> a{(const int64_t *)doc, (uint32_t)S, total, n_tiles, vec_in, vec_mask,
-                          cu, cu2, num_segments, max_seqlen, mask, status, pad_between, ws};
+    DocArgs<int64_t> a{(const int64_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in, vec_mask,
+                       cu, cu2, num_segments, max_seqlen, mask, status, pad_between, recs};
     return launch_typed(a, copies, n_copies, stream);
 }
 

@@ -45,6 +45,12 @@ int check_copies(const psq_copy *copies, int n_copies) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PSQ_OK : PSQ_ERR_HIP; }
 
+// A workspace is usable when present, large enough and 16-byte aligned (its
+// records are read as 16-byte vectors, its counters as 64-bit atomics).
+bool workspace_ok(const void *workspace, size_t bytes, size_t need) {
+    return workspace != nullptr && bytes >= need && ((uintptr_t)workspace % 16) == 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -55,7 +61,7 @@ const char *psq_status_string(int code, int is_status) {
             case PSQ_OK: return "ok";
             case PSQ_ERR_ARG: return "invalid argument (null pointer, negative size, bad enum)";
             case PSQ_ERR_OVERFLOW: return "size does not fit int32 boundary arrays";
-            case PSQ_ERR_WORKSPACE: return "workspace missing or too small";
+            case PSQ_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
             case PSQ_ERR_HIP: return "HIP runtime error while enqueuing";
             default: return "unknown error code";
         }
@@ -95,7 +101,7 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
     if (cu_seqlens == nullptr || num_segments == nullptr || max_seqlen == nullptr)
         return PSQ_ERR_ARG;
     if (B * S > 0 && doc_ids == nullptr) return PSQ_ERR_ARG;
-    if (workspace == nullptr || workspace_bytes < psq::doc_segments_workspace(B, S))
+    if (!workspace_ok(workspace, workspace_bytes, psq::doc_segments_workspace(B, S)))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_doc_segments(doc_ids, doc_dtype, B, S, cu_seqlens, nullptr,
                                              num_segments, max_seqlen, padding_mask, status,
@@ -129,7 +135,7 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t 
     if (layout->kind == PSQ_LAYOUT_DOC_IDS) {
         if (!valid_dtype(layout->doc_dtype)) return PSQ_ERR_ARG;
         if (B * S > 0 && layout->doc_ids == nullptr) return PSQ_ERR_ARG;
-        if (workspace == nullptr || workspace_bytes < psq::doc_segments_workspace(B, S))
+        if (!workspace_ok(workspace, workspace_bytes, psq::doc_segments_workspace(B, S)))
             return PSQ_ERR_WORKSPACE;
         return from_hip(psq::launch_doc_segments(layout->doc_ids, layout->doc_dtype, B, S,
                                                  cu_seqlens, cu_seqlens_padded, num_seqs,
@@ -144,7 +150,7 @@ int psq_process_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int32_t 
     if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
     if (!psq::thd_tables_grid_fits(B, layout->P, S, 1, copies, n_copies))
         return PSQ_ERR_OVERFLOW;
-    if (workspace == nullptr || workspace_bytes < psq::thd_tables_workspace(B, layout->P, 1))
+    if (!workspace_ok(workspace, workspace_bytes, psq::thd_tables_workspace(B, layout->P, 1)))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
                                            layout->lens_dtype, B, layout->P, S, 1,
@@ -189,8 +195,8 @@ int psq_split_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int64_t nu
     if (B * layout->P > 0 && layout->seq_lens == nullptr) return PSQ_ERR_ARG;
     if (!psq::thd_tables_grid_fits(B, layout->P, S, num_chunks, copies, n_copies))
         return PSQ_ERR_OVERFLOW;
-    if (workspace == nullptr ||
-        workspace_bytes < psq::thd_tables_workspace(B, layout->P, num_chunks))
+    if (!workspace_ok(workspace, workspace_bytes,
+                      psq::thd_tables_workspace(B, layout->P, num_chunks)))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_thd_tables(layout->seq_lens, layout->seq_lens_padded,
                                            layout->lens_dtype, B, layout->P, S, num_chunks,
@@ -213,7 +219,7 @@ int psq_padding_mask_from_token_ids(const void *input_ids, int ids_dtype, int64_
     if (T >= kI32Limit) return PSQ_ERR_OVERFLOW;
     if (status == nullptr) return PSQ_ERR_ARG;
     if (T > 0 && (input_ids == nullptr || padding_mask == nullptr)) return PSQ_ERR_ARG;
-    if (workspace == nullptr || workspace_bytes < psq::pad_ids_workspace())
+    if (!workspace_ok(workspace, workspace_bytes, psq::pad_ids_workspace()))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_pad_ids(input_ids, ids_dtype, T, pad_id, padding_mask,
                                         num_content, status, workspace, (hipStream_t)stream));
@@ -242,7 +248,7 @@ int psq_pack_rows(const int64_t *src_tokens, int64_t src_len, const int64_t *src
     if (!psq::pack_rows_grid_fits(P, capacity)) return PSQ_ERR_OVERFLOW;
     if (N > 0 && (src_offsets == nullptr || real_len == nullptr)) return PSQ_ERR_ARG;
     if (src_len > 0 && src_tokens == nullptr) return PSQ_ERR_ARG;
-    if (workspace == nullptr || workspace_bytes < psq::pack_rows_workspace())
+    if (!workspace_ok(workspace, workspace_bytes, psq::pack_rows_workspace()))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_pack_rows(src_tokens, src_len, src_offsets, 0, real_len, N,
                                           pad_to, pack_order, pack_start, P, capacity, fold,
@@ -268,7 +274,7 @@ int psq_pack_padded_rows(const int64_t *rows, int64_t W, const int32_t *real_len
     if (!psq::pack_rows_grid_fits(P, capacity)) return PSQ_ERR_OVERFLOW;
     if (N > 0 && real_len == nullptr) return PSQ_ERR_ARG;
     if (N * W > 0 && rows == nullptr) return PSQ_ERR_ARG;
-    if (workspace == nullptr || workspace_bytes < psq::pack_rows_workspace())
+    if (!workspace_ok(workspace, workspace_bytes, psq::pack_rows_workspace()))
         return PSQ_ERR_WORKSPACE;
     return from_hip(psq::launch_pack_rows(rows, N * W, nullptr, W, real_len, N, pad_to,
                                           pack_order, pack_start, P, capacity, fold, pad_token,

@@ -61,10 +61,11 @@ __device__ __forceinline__ void jitter(uint32_t site) {
 }
 
 // ---------------------------------------------------------------------------
-// Workspace.  The first 256 bytes hold the header; per-tile descriptors
-// follow.  Every kernel that uses it leaves it zero-filled on completion (the
-// last workgroup to finish clears what the call used), so a workspace needs
-// one zero fill per allocation.
+// Workspace.  The first 256 bytes hold the header; the document-map records
+// and then the table kernel's per-row descriptors follow.  Every kernel that
+// relies on zeros leaves its part zero-filled on completion (the last
+// workgroup to finish clears what the call used), so a workspace needs one
+// zero fill per allocation.
 // ---------------------------------------------------------------------------
 struct WsHeader {
     uint32_t ticket;     // dynamic tile ids (dispatch order is not guaranteed)
@@ -77,7 +78,15 @@ struct WsHeader {
     int32_t total;
     uint64_t fin;        // finished count (high half) | status bits (low half)
 };
-constexpr size_t kWsDescOffset = 256;
+// The document-map kernels keep one 16-byte record per workgroup (at most
+// kDocMaxGroups) in a scratch region right after the header.  They neither
+// need it zero-filled nor clear it, and no other kernel touches it, so the
+// zero-filled parts of a shared workspace stay zero-filled.
+constexpr size_t kWsDocOffset = 256;
+constexpr uint32_t kDocMaxGroups = 1024;
+constexpr size_t kWsDocBytes = 16 * (size_t)kDocMaxGroups;
+// per-row look-back descriptors of the multi-workgroup table kernel
+constexpr size_t kWsDescOffset = kWsDocOffset + kWsDocBytes;
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
