@@ -27,7 +27,8 @@
  * --------------------------------
  *  - Pointers are DEVICE pointers unless a parameter says "host".  The caller
  *    owns and allocates every buffer, including the workspace; the library
- *    allocates nothing and keeps no state between calls.
+ *    allocates nothing and keeps no state between calls (one exception:
+ *    psq_params_from_doc_ids_noalloc's per-GPU scratch).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  No
  *    call synchronizes: outputs and *status are valid once the stream reaches
  *    the work.  Calls that overlap in time must use distinct workspaces.
@@ -145,6 +146,30 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
                             int32_t *max_seqlen, uint8_t *padding_mask,
                             int32_t *status, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* ------------------------------------------------------------------------
+ * psq_params_from_doc_ids_noalloc
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * operation, arguments and outputs as psq_params_from_doc_ids, without the
+ * workspace: the library uses its own file-scope device scratch of
+ * PSQ_NOALLOC_SCRATCH_BYTES bytes instead, one copy per GPU, held until the
+ * process ends.  The current device's copy is used (hipGetDevice), so
+ * `stream` must belong to the current device.  The call allocates nothing.
+ * Every size psq_params_from_doc_ids accepts fits the scratch (a map needs
+ * at most 1024 records of 16 bytes); a larger need would return
+ * PSQ_ERR_OVERFLOW.  The scratch needs no clearing: each call writes every
+ * record it reads.  Calls that overlap in time on one GPU (several streams
+ * or host threads) share the scratch and race: order them on one stream.
+ * Host errors: as psq_params_from_doc_ids (without PSQ_ERR_WORKSPACE), and
+ * PSQ_ERR_HIP when the scratch's device address cannot be looked up.
+ * ---------------------------------------------------------------------- */
+#define PSQ_NOALLOC_SCRATCH_BYTES 16640
+int psq_params_from_doc_ids_noalloc(const void *doc_ids, int doc_dtype, int64_t B, int64_t S,
+                                    int32_t *cu_seqlens, int32_t *num_segments,
+                                    int32_t *max_seqlen, uint8_t *padding_mask,
+                                    int32_t *status, void *stream);
 
 /* One byte copy of the BSHD -> THD collapse: `rows` rows of `row_bytes`
  * bytes, read at a stride of src_row_stride_bytes and written at a stride of

@@ -88,6 +88,28 @@ def test_doc_ids_validation(lib):
     assert _doc(lib, ws=FAKE, wsb=8) == _lib.ERR_WORKSPACE
 
 
+def _noalloc(lib, **kw):
+    a = dict(doc=FAKE, dt=_lib.I32, B=4, S=64, cu=FAKE, n=FAKE, mx=FAKE, mask=None,
+             st=None, stream=None)
+    a.update(kw)
+    return lib.psq_params_from_doc_ids_noalloc(a["doc"], a["dt"], a["B"], a["S"], a["cu"],
+                                               a["n"], a["mx"], a["mask"], a["st"], a["stream"])
+
+
+def test_doc_ids_noalloc_validation(lib):
+    """The no-allocation entry point rejects what psq_params_from_doc_ids
+    rejects, on the host, before it looks up its scratch."""
+    assert _noalloc(lib, B=-1) == _lib.ERR_ARG
+    assert _noalloc(lib, S=-3) == _lib.ERR_ARG
+    assert _noalloc(lib, dt=7) == _lib.ERR_ARG
+    assert _noalloc(lib, B=1 << 16, S=1 << 15) == _lib.ERR_OVERFLOW
+    assert _noalloc(lib, B=1, S=1 << 31) == _lib.ERR_OVERFLOW
+    assert _noalloc(lib, cu=None) == _lib.ERR_ARG
+    assert _noalloc(lib, n=None) == _lib.ERR_ARG
+    assert _noalloc(lib, mx=None) == _lib.ERR_ARG
+    assert _noalloc(lib, doc=None) == _lib.ERR_ARG
+
+
 def test_workspace_alignment(lib):
     """A workspace that is not 16-byte aligned is refused by every call before
     anything is enqueued (records are read as 16-byte vectors)."""

@@ -90,6 +90,8 @@ def open_library(path: str):
     lib.psq_params_from_doc_ids_workspace.argtypes = [i64, i64]
     lib.psq_params_from_doc_ids.restype = ci
     lib.psq_params_from_doc_ids.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.psq_params_from_doc_ids_noalloc.restype = ci
+    lib.psq_params_from_doc_ids_noalloc.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, vp, vp]
     lib.psq_process_thd_workspace.restype = sz
     lib.psq_process_thd_workspace.argtypes = [ctypes.POINTER(PsqThdLayout), i64, i64]
     lib.psq_process_thd.restype = ci
@@ -140,6 +142,15 @@ def psq_params_from_doc_ids(doc_ids, doc_dtype, B, S, cu_seqlens, num_segments, 
                                         max_seqlen, padding_mask, status, workspace,
                                         workspace_bytes, stream)
     return _check(rc, "psq_params_from_doc_ids") if check else rc
+
+
+def psq_params_from_doc_ids_noalloc(doc_ids, doc_dtype, B, S, cu_seqlens, num_segments,
+                                    max_seqlen, padding_mask, status, stream,
+                                    check=True) -> int:
+    rc = load().psq_params_from_doc_ids_noalloc(doc_ids, doc_dtype, B, S, cu_seqlens,
+                                                num_segments, max_seqlen, padding_mask, status,
+                                                stream)
+    return _check(rc, "psq_params_from_doc_ids_noalloc") if check else rc
 
 
 def make_layout(kind, seq_lens=None, seq_lens_padded=None, lens_dtype=I64, P=0,
