@@ -47,8 +47,6 @@ constexpr int kPerLane = 4;
 constexpr uint32_t kSub = kWave * kPerLane;            // 256 positions
 constexpr uint32_t kWaveSpan = kSub * kIters;          // 1024 positions
 constexpr uint32_t kChunk = kWaveSpan * kWaves;        // 4096 positions
-constexpr int kRecsPerThread = (int)(kDocMaxGroups / kThreads);
-static_assert(kDocMaxGroups % kThreads == 0, "records are spread evenly over the threads");
 
 // One workgroup's range: boundary count, first boundary, one past the last
 // boundary (0 = none), and the longest segment between two boundaries of the
@@ -121,58 +119,73 @@ struct DocArgs {
     DocRec *recs;                       // n_groups records (multi-group maps)
 };
 
-// Boundary flags of the 1024 positions a wave owns from wave_base (positions
-// at or past `total` are absent).  For sub-chunk j: fm[j] holds the lane's 4
-// flags (bit k: position pos0 + k), off[j] counts the wave's boundaries
-// before the lane's first position, and prv[j] is one past the wave's last
-// boundary before the lane's positions (0: none yet in this wave).  *cnt and
-// *last1 return the wave's count and one past its last boundary (0: none).
-// With `mask`, also writes mask[t] = (doc[t] == 0).
+// The map values of the 1024 positions a wave owns from wave_base
+// (positions at or past `total` are absent), and the value before them.
 template <typename T>
-__device__ __forceinline__ void wave_flags(const T *__restrict__ doc, uint32_t S, uint32_t total,
-                                           int vec_in, uint8_t *__restrict__ mask, int vec_mask,
-                                           uint32_t wave_base, uint32_t (&fm)[kIters],
-                                           uint32_t (&off)[kIters], uint32_t (&prv)[kIters],
-                                           uint32_t *cnt, uint32_t *last1) {
-    const int lane = lane_id();
-    T carry = (T)0;
-    if (wave_base > 0 && wave_base < total) carry = doc[wave_base - 1];
-
-    // All of the wave's loads are issued before any is used.  A wave whose
-    // whole span is in range takes straight-line vector loads (a uniform
-    // branch); per-chunk branches would make the compiler wait for each load
-    // before issuing the next.
-    T dall[kIters][kPerLane];
+struct WaveData {
+    T d[kIters][kPerLane];
     int pres[kIters];
+    T left;          // the value before the span, valid when has_left
+    bool has_left;
+};
+
+// Issue the wave's loads (all of them before any is used).  A wave whose
+// whole span is in range takes straight-line vector loads (a uniform
+// branch); per-chunk branches would make the compiler wait for each load
+// before issuing the next.  The value before the span is loaded without a
+// branch too (from position 0 when there is none, then dropped): a load
+// under a branch is waited for at the join, before the loads after it.
+// Requires total > 0.
+template <typename T>
+__device__ __forceinline__ void wave_load(const T *__restrict__ doc, uint32_t total, int vec_in,
+                                          uint32_t wave_base, WaveData<T> &wd) {
+    const int lane = lane_id();
+    wd.has_left = wave_base > 0 && wave_base < total;
+    wd.left = doc[wd.has_left ? wave_base - 1 : 0u];
     if (vec_in && wave_base + kWaveSpan <= total) {
 #pragma unroll
         for (int j = 0; j < kIters; ++j) {
             const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
             if constexpr (sizeof(T) == 4) {
                 const i32x4 v = *(const i32x4 *)(doc + pos0);
-                dall[j][0] = v.x; dall[j][1] = v.y; dall[j][2] = v.z; dall[j][3] = v.w;
+                wd.d[j][0] = v.x; wd.d[j][1] = v.y; wd.d[j][2] = v.z; wd.d[j][3] = v.w;
             } else {
                 const i64x2 v0 = *(const i64x2 *)(doc + pos0);
                 const i64x2 v1 = *(const i64x2 *)(doc + pos0 + 2);
-                dall[j][0] = v0.x; dall[j][1] = v0.y; dall[j][2] = v1.x; dall[j][3] = v1.y;
+                wd.d[j][0] = v0.x; wd.d[j][1] = v0.y; wd.d[j][2] = v1.x; wd.d[j][3] = v1.y;
             }
-            pres[j] = kPerLane;
+            wd.pres[j] = kPerLane;
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kIters; ++j) {
             const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
-            pres[j] = load4(doc, pos0, total, vec_in != 0, dall[j]);
+            wd.pres[j] = load4(doc, pos0, total, vec_in != 0, wd.d[j]);
         }
     }
+}
 
+// Boundary flags of a wave's loaded positions.  For sub-chunk j: fm[j] holds
+// the lane's 4 flags (bit k: position pos0 + k), off[j] counts the wave's
+// boundaries before the lane's first position, and prv[j] is one past the
+// wave's last boundary before the lane's positions (0: none yet in this
+// wave).  *cnt and *last1 return the wave's count and one past its last
+// boundary (0: none).  With `mask`, also writes mask[t] = (doc[t] == 0).
+template <typename T>
+__device__ __forceinline__ void wave_flags(const WaveData<T> &wd, uint32_t S,
+                                           uint8_t *__restrict__ mask, int vec_mask,
+                                           uint32_t wave_base, uint32_t (&fm)[kIters],
+                                           uint32_t (&off)[kIters], uint32_t (&prv)[kIters],
+                                           uint32_t *cnt, uint32_t *last1) {
+    const int lane = lane_id();
+    T carry = wd.has_left ? wd.left : (T)0;   // first use of the loads
     uint32_t run_c = 0, run_l = 0;
     const bool small_s = S < (uint32_t)kPerLane;
 #pragma unroll
     for (int j = 0; j < kIters; ++j) {
         const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
-        const T *d = dall[j];
-        const int present = pres[j];
+        const T *d = wd.d[j];
+        const int present = wd.pres[j];
 
         if (mask != nullptr && present > 0) {
             if (present == kPerLane && vec_mask) {
@@ -180,7 +193,11 @@ __device__ __forceinline__ void wave_flags(const T *__restrict__ doc, uint32_t S
                                    ((uint32_t)(d[2] == 0) << 16) | ((uint32_t)(d[3] == 0) << 24);
                 *(uint32_t *)(mask + pos0) = m;
             } else {
-                for (int k = 0; k < present; ++k) mask[pos0 + k] = (uint8_t)(d[k] == 0);
+                // unrolled with a predicate: a runtime index into d would put
+                // the loaded values in scratch memory
+#pragma unroll
+                for (int k = 0; k < kPerLane; ++k)
+                    if (k < present) mask[pos0 + k] = (uint8_t)(d[k] == 0);
             }
         }
 
@@ -231,9 +248,10 @@ __global__ __launch_bounds__(kThreads) void k_doc_reduce(DocArgs<T> a) {
     DocRec rec{0u, 0u, 0u, 0u};                 // accumulated by thread 0
     for (uint32_t c = c0; c < c1; ++c) {
         const uint32_t wave_base = c * kChunk + (uint32_t)w * kWaveSpan;
+        WaveData<T> wd;
+        wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
         uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
-        wave_flags(a.doc, a.S, a.total, a.vec_in, a.mask, a.vec_mask, wave_base, fm, off, prv,
-                   &cnt, &last1);
+        wave_flags(wd, a.S, a.mask, a.vec_mask, wave_base, fm, off, prv, &cnt, &last1);
         // the wave's first boundary, and its longest segment that starts at
         // one of its own boundaries and ends at the next
         uint32_t first = 0;
@@ -288,30 +306,51 @@ __global__ __launch_bounds__(kThreads) void k_doc_reduce(DocArgs<T> a) {
         *(u32x4 *)(a.recs + blockIdx.x) = u32x4{rec.cnt, rec.first, rec.last1, rec.imax};
 }
 
-// Block-wide sum of x and maxima of y and z (non-negative), returned to every
-// thread.
-__device__ __forceinline__ void block_sum_max_max(uint32_t &x, uint32_t &y, uint32_t &z,
-                                                  uint32_t (&s)[3][kWaves]) {
-    const int w = threadIdx.x / kWave;
-    x = (uint32_t)read_lane(wave_incl_sum((int)x), kWave - 1);
-    y = (uint32_t)read_lane(wave_incl_max((int)y), kWave - 1);
-    z = (uint32_t)read_lane(wave_incl_max((int)z), kWave - 1);
-    if (lane_id() == 0) {
-        s[0][w] = x;
-        s[1][w] = y;
-        s[2][w] = z;
-    }
-    __syncthreads();
-    x = 0;
-    y = 0;
-    z = 0;
+// What a workgroup of launch 2 needs from the records, reduced by each wave
+// on its own (no barrier): the boundary count before the group (its first
+// output slot) and one past the last boundary before it (0: none).  In the
+// last group (`all`) the wave also reads its own and every other record and
+// returns the longest segment they describe, closing segment excepted: the
+// records' inner maxima and each segment that runs from the last boundary
+// of the records before a record to that record's first boundary.  Records
+// are read 64 at a time, lane l taking record 64 i + l of round i; the first
+// four rounds (256 groups) are issued together.
+__device__ __forceinline__ void wave_records(const DocRec *__restrict__ recs, uint32_t g,
+                                             uint32_t n_groups, bool all, uint32_t *base_c,
+                                             uint32_t *base_l, uint32_t *seg_max) {
+    constexpr int kBatch = 4;
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t nread = all ? n_groups : g;
+    uint32_t c_sum = 0, l_pre = 0, run = 0, m = 0;
+    for (uint32_t r0 = 0; r0 < nread; r0 += kBatch * kWave) {
+        u32x4 v[kBatch];
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        x += s[0][v];
-        y = max(y, s[1][v]);
-        z = max(z, s[2][v]);
+        for (int i = 0; i < kBatch; ++i) {
+            const uint32_t idx = r0 + (uint32_t)i * kWave + lane;
+            v[i] = idx < nread ? *(const u32x4 *)(recs + idx) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const uint32_t idx = r0 + (uint32_t)i * kWave + lane;
+            if (idx < g) {
+                c_sum += v[i].x;
+                l_pre = max(l_pre, v[i].z);
+            }
+            if (all) {
+                // one past the last boundary of every record before this one
+                const uint32_t incl = (uint32_t)wave_incl_max((int)v[i].z);
+                const uint32_t p = max(run, (uint32_t)wave_shr1((int)incl, 0));
+                if (v[i].x) {
+                    if (p) m = max(m, v[i].y + 1u - p);
+                    m = max(m, v[i].w);
+                }
+                run = max(run, (uint32_t)read_lane((int)incl, kWave - 1));
+            }
+        }
     }
-    __syncthreads();
+    *base_c = (uint32_t)read_lane(wave_incl_sum((int)c_sum), kWave - 1);
+    *base_l = (uint32_t)read_lane(wave_incl_max((int)l_pre), kWave - 1);
+    *seg_max = all ? (uint32_t)read_lane(wave_incl_max((int)m), kWave - 1) : 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -320,73 +359,30 @@ __device__ __forceinline__ void block_sum_max_max(uint32_t &x, uint32_t &y, uint
 template <typename T, bool kSolo>
 __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
     __shared__ uint32_t s_wcnt[kWaves], s_wlast[kWaves];
-    __shared__ uint32_t s_red[3][kWaves];
     __shared__ int32_t s_max;
     const int w = threadIdx.x / kWave;
     const int lane = lane_id();
     const uint32_t g = blockIdx.x;
     const bool last = g == a.n_groups - 1;
-
-    // ---- the records before this group: its first output slot (base_c) and
-    // one past the boundary before its range (base_l); the last group also
-    // takes the longest segment the records describe
-    uint32_t base_c = 0, base_l = 0, rec_max = 0;
-    if constexpr (!kSolo) {
-        const uint32_t nread = last ? a.n_groups : g;
-        DocRec r[kRecsPerThread];
-        uint32_t c_sum = 0, l_pre = 0, l_mine = 0;
-#pragma unroll
-        for (int i = 0; i < kRecsPerThread; ++i) {
-            const uint32_t idx = threadIdx.x * (uint32_t)kRecsPerThread + (uint32_t)i;
-            r[i] = DocRec{0u, 0u, 0u, 0u};
-            if (idx < nread) {
-                const u32x4 v = *(const u32x4 *)(a.recs + idx);
-                r[i] = DocRec{v.x, v.y, v.z, v.w};
-            }
-            if (idx < g) {
-                c_sum += r[i].cnt;
-                l_pre = max(l_pre, r[i].last1);
-            }
-            l_mine = max(l_mine, r[i].last1);
-        }
-        uint32_t m = 0;
-        if (last) {
-            // one past the last boundary of the records before this thread's
-            // own: an exclusive max scan over the threads, in record order
-            const uint32_t incl = (uint32_t)wave_incl_max((int)l_mine);
-            if (lane == kWave - 1) s_red[0][w] = incl;
-            __syncthreads();
-            uint32_t p = (uint32_t)wave_shr1((int)incl, 0);
-#pragma unroll
-            for (int v = 0; v < kWaves; ++v)
-                if (v < w) p = max(p, s_red[0][v]);
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < kRecsPerThread; ++i) {
-                if (r[i].cnt) {
-                    if (p) m = max(m, r[i].first + 1u - p);
-                    m = max(m, r[i].imax);
-                    p = r[i].last1;
-                }
-            }
-        }
-        block_sum_max_max(c_sum, l_pre, m, s_red);
-        base_c = c_sum;
-        base_l = l_pre;
-        rec_max = m;
-    }
-    if (threadIdx.x == 0) s_max = 0;
-
-    // ---- this group's chunks
     const uint32_t c0 = g * a.cpw;
     const uint32_t c1 = min(c0 + a.cpw, a.n_chunks);
+    if (threadIdx.x == 0) s_max = 0;
+
+    // the first chunk's map loads go out before the records are read, so the
+    // two round trips overlap
+    WaveData<T> wd;
+    if (c0 < c1) wave_load(a.doc, a.total, a.vec_in, c0 * kChunk + (uint32_t)w * kWaveSpan, wd);
+    uint32_t base_c = 0, base_l = 0, rec_max = 0;
+    if constexpr (!kSolo) wave_records(a.recs, g, a.n_groups, last, &base_c, &base_l, &rec_max);
+
     int32_t lmax = 0;
     bool oob = false;
     for (uint32_t c = c0; c < c1; ++c) {
         const uint32_t wave_base = c * kChunk + (uint32_t)w * kWaveSpan;
+        if (c != c0) wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
         uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
-        wave_flags(a.doc, a.S, a.total, a.vec_in, kSolo ? a.mask : nullptr, a.vec_mask,
-                   wave_base, fm, off, prv, &cnt, &last1);
+        wave_flags(wd, a.S, kSolo ? a.mask : nullptr, a.vec_mask, wave_base, fm, off, prv, &cnt,
+                   &last1);
         if (lane == 0) {
             s_wcnt[w] = cnt;
             s_wlast[w] = last1;
