@@ -48,9 +48,10 @@
  *    Every call leaves the parts it relies on zero-filled again when it
  *    completes, so the zero fill is needed only once per allocation and one
  *    workspace can serve every call on a stream.  (The document-map calls
- *    keep scratch records in bytes 256 .. 256 + 16 KiB, which no other call
- *    reads; they neither need nor restore zeros there.)  A query returns 0
- *    for sizes its call would reject (PSQ_ERR_ARG or PSQ_ERR_OVERFLOW).
+ *    keep records and state in bytes 256 .. 49664, which no other call
+ *    reads; there they leave data that the next document-map call expects.)
+ *    A query returns 0 for sizes its call would reject (PSQ_ERR_ARG or
+ *    PSQ_ERR_OVERFLOW).
  *  - Grids: one HIP launch runs fewer than 2^32 threads.  Sizes that would
  *    need more in a call's metadata launch are PSQ_ERR_OVERFLOW; the limits
  *    are given with each call and lie far beyond the memory one GPU holds
@@ -131,12 +132,14 @@ int psq_workspace_init(void *workspace, size_t bytes, void *stream);
  *                 values.  PSQ_DATA_WORKSPACE reports a failed bound check,
  *                 possible only when the map changes during the call.
  *   workspace     device scratch of psq_params_from_doc_ids_workspace(B, S)
- *                 bytes (at most 256 + 16 KiB for any size), 16-byte
- *                 aligned.  Its contents on entry do not matter.
- * Two launches: one 16-byte record per workgroup (the range's boundary
- * count, first and last boundary, and longest inner segment), then the
- * boundaries, each workgroup starting at the sum of the counts before it.
- * A map of at most 4096 positions takes one launch.
+ *                 bytes (at most 49664 for any size), 16-byte aligned,
+ *                 zero-filled once like every workspace.
+ * Each workgroup reduces a range of 4096-position chunks to a 16-byte
+ * record (boundary count, first and last boundary, longest inner segment)
+ * and starts its boundaries at the sum of the counts before it.  Maps of
+ * more than 256 chunks take two launches (records, then boundaries); maps
+ * of 2..256 chunks take one, each workgroup reading the earlier workgroups'
+ * records as they are published; a map of one chunk is one workgroup.
  * Host errors: PSQ_ERR_ARG (null pointer, B or S < 0, bad dtype),
  * PSQ_ERR_OVERFLOW (B*S >= 2^31), PSQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
@@ -156,16 +159,17 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
  * workspace: the library uses its own file-scope device scratch of
  * PSQ_NOALLOC_SCRATCH_BYTES bytes instead, one copy per GPU, held until the
  * process ends.  The current device's copy is used (hipGetDevice), so
- * `stream` must belong to the current device.  The call allocates nothing.
- * Every size psq_params_from_doc_ids accepts fits the scratch (a map needs
- * at most 1024 records of 16 bytes); a larger need would return
- * PSQ_ERR_OVERFLOW.  The scratch needs no clearing: each call writes every
- * record it reads.  Calls that overlap in time on one GPU (several streams
+ * `stream` must belong to the current device.  The call allocates nothing;
+ * its first call on a device also enqueues one fill kernel on `stream` that
+ * zero-fills that device's scratch.  Every size psq_params_from_doc_ids
+ * accepts fits the scratch (the largest document-map workspace); a larger
+ * need would return PSQ_ERR_OVERFLOW.  Each call leaves the scratch ready
+ * for the next one.  Calls that overlap in time on one GPU (several streams
  * or host threads) share the scratch and race: order them on one stream.
  * Host errors: as psq_params_from_doc_ids (without PSQ_ERR_WORKSPACE), and
  * PSQ_ERR_HIP when the scratch's device address cannot be looked up.
  * ---------------------------------------------------------------------- */
-#define PSQ_NOALLOC_SCRATCH_BYTES 16640
+#define PSQ_NOALLOC_SCRATCH_BYTES 49664
 int psq_params_from_doc_ids_noalloc(const void *doc_ids, int doc_dtype, int64_t B, int64_t S,
                                     int32_t *cu_seqlens, int32_t *num_segments,
                                     int32_t *max_seqlen, uint8_t *padding_mask,

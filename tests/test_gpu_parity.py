@@ -139,6 +139,24 @@ def test_doc_many_chunks_per_workgroup(dev, B, S, kind):
     check_doc(dev, d)
 
 
+def test_doc_one_launch_sequence(dev):
+    """Maps of 2..256 chunks take one launch whose workgroups publish tagged
+    records; the tags of a call must never be taken for those of a later one.
+    The sequence changes the chunk count up and down on one workspace (256,
+    then 8, then 256 again reuses tiles 8..255 with the first call's parity;
+    64, 65, 128 and 129 chunks put the last record at either side of a wave's
+    slice), with two-launch maps and a one-chunk map in between."""
+    shapes = [(32, 32768), (8, 4096), (32, 32768), (2, 4097), (1, 64 * 4096 - 1),
+              (7, 9000), (1, 65 * 4096), (129, 4096), (4, 64), (64, 4096), (3, 4096),
+              (128, 4096), (1, 257 * 4096 - 3), (1, 256 * 4096), (16, 16384), (1, 8193),
+              (255, 4096), (32, 32768)]
+    for i, (B, S) in enumerate(shapes):
+        rng = np.random.default_rng(100 + i)
+        d = _long_runs(rng, B, S, [3, 300, 5000][i % 3]) if B * S > 64 else \
+            rng.integers(0, 3, size=(B, S)).astype(np.int32)
+        check_doc(dev, d)
+
+
 def test_doc_unaligned_input(dev):
     # a view that starts 4 bytes into its storage: the scalar-load path
     d = synth.doc_map_medium()
@@ -184,7 +202,7 @@ def test_doc_python_api(dev):
     assert kw["max_length_q"] == kw["max_length_k"] == p.max_seqlen
 
 
-DOC_RECORDS = (256, 256 + 16384)     # the document-map records: scratch, never zeroed
+DOC_RECORDS = (256, 49664)     # the document-map region: records and one-launch state
 
 
 def _nonzero_outside(ws, lo, hi):

@@ -8,13 +8,14 @@ orders in which workgroups reach those steps are therefore shuffled from
 call to call.  Each case runs repeatedly on the same inputs and every run
 must equal the CPU oracle exactly and leave the workspace zero-filled.
 
-The kernels covered: the multi-workgroup length-table kernel with and
-without row groups (ticket, look-back over rows, completion count), the
-squeeze (completion word) and the pad-id mask (completion count).  The
-document-map kernels have no cross-workgroup step (two launches, the second
-reading the first one's records); they run here too, as a repeat check of
-those launches on the same build.  The single-workgroup table kernel has no
-cross-workgroup step.
+The kernels covered: the one-launch document map of 2..256 chunks (tagged
+records, waits on the earlier tiles, the last tile's reset of the state),
+the multi-workgroup length-table kernel with and without row groups (ticket,
+look-back over rows, completion count), the squeeze (completion word) and
+the pad-id mask (completion count).  Larger document maps take two
+launches with no cross-workgroup step (the second reads the first one's
+records); they run here too, as a repeat check.  The single-workgroup table
+kernel has no cross-workgroup step.
 """
 import ctypes
 import os
@@ -58,7 +59,7 @@ def _workspace(dev, nbytes):
 def _assert_zero(ws, scratch=None):
     """Every byte a call relies on finding zero is zero again; ``scratch`` is a
     (start, end) byte range the call may leave holding data (the document-map
-    records)."""
+    region: records and the one-launch state)."""
     torch.cuda.synchronize()
     kept = ws.clone()
     if scratch is not None:
@@ -66,7 +67,8 @@ def _assert_zero(ws, scratch=None):
     assert int(kept.count_nonzero()) == 0, "workspace not left zero-filled"
 
 
-@pytest.mark.parametrize("shape", [(8, 4096), (32, 32768), (3, 100003)])
+@pytest.mark.parametrize("shape", [(8, 4096), (32, 32768), (3, 100003), (16, 16384), (7, 9000),
+                                   (2, 4097), (1, 257 * 4096)])
 def test_doc_map_tiles_under_jitter(jl, dev, shape):
     B, S = shape
     doc_np = synth.stage_embedding(5, B, S)["doc_ids"] if S == 32768 else \
@@ -88,7 +90,32 @@ def test_doc_map_tiles_under_jitter(jl, dev, shape):
         assert n == ref["num_segments"] and mx == ref["max_seqlen"]
         assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
         assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
-        _assert_zero(ws, scratch=(256, 256 + 16384))
+        _assert_zero(ws, scratch=(256, 49664))
+
+
+def test_doc_map_one_launch_sequence_under_jitter(jl, dev):
+    """One workspace, chunk counts going up and down (256, 8, 256, 3, 129, a
+    two-launch map, 256): every call's tagged records must be told apart from
+    the previous calls' under shuffled progress."""
+    shapes = [(32, 32768), (8, 4096), (32, 32768), (3, 4096), (129, 4096), (1, 257 * 4096),
+              (32, 32768)]
+    maps = [synth.doc_map_medium(20 + i, B, S) for i, (B, S) in enumerate(shapes)]
+    refs = [oracle.doc_segments(m) for m in maps]
+    ws = _workspace(dev, max(jl.psq_params_from_doc_ids_workspace(B, S) for B, S in shapes))
+    for rep in range(REPEATS):
+        for (B, S), doc_np, ref in zip(shapes, maps, refs):
+            say(f"jitter doc map sequence {B}x{S} run {rep}")
+            d = torch.from_numpy(doc_np).to(dev)
+            cu = torch.full((B * S + 1,), -7, dtype=torch.int32, device=dev)
+            scal = torch.full((3,), -7, dtype=torch.int32, device=dev)
+            sp = scal.data_ptr()
+            assert jl.psq_params_from_doc_ids(d.data_ptr(), _lib.I32, B, S, cu.data_ptr(), sp,
+                                              sp + 4, None, sp + 8, ws.data_ptr(), ws.numel(),
+                                              _stream(dev)) == 0
+            n, mx, st = scal.cpu().tolist()
+            assert st == 0 and n == ref["num_segments"] and mx == ref["max_seqlen"]
+            assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
+    _assert_zero(ws, scratch=(256, 49664))
 
 
 def _tables(seed, B, P, S):

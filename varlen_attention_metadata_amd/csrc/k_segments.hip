@@ -455,16 +455,268 @@ __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// One launch for maps of 2..kDocSmallTiles chunks (k_doc_small).  Workgroup
+// t reduces tile t to the record of launch 1 and publishes the record as two
+// tagged 64-bit words.  Its waves then wait until every earlier tile has
+// published and reduce those records themselves, one per lane (wave v takes
+// tiles 64 v .. 64 v + 63: no chained look-back).  The last tile also takes
+// max_seqlen from them, as the last group of launch 2 does.  The flags stay
+// in registers, so the tile is read once and no workgroup counts itself
+// finished.
+//
+// Tiles are workgroup ids, not tickets: a workgroup waits only on lower ids,
+// and at most 256 workgroups of 256 threads fit the chip's slots at once
+// (a CU holds several), so every tile waited on gets a slot whatever the
+// dispatch order.  The wait is bounded all the same (a status bit, never a
+// hang).
+//
+// A record is one 64-bit word: bit 63 valid, bit 62 the call's parity, then
+// the tile's boundary count (bits 0..12), first boundary (13..24) and one
+// past its last boundary (25..37), both relative to the tile, and its inner
+// maximum (38..50).  The state word holds the parity (bit 32) and the
+// previous call's tile count (bits 33..42); every
+// workgroup reads it while its map loads are in flight.  Once the last tile
+// has seen every other tile's record, every workgroup has read the state: it
+// clears the words of the tiles the previous call used beyond this call's
+// count and stores the next call's state (the other parity, this call's
+// count).  At the start of a call the word of every tile below its count is
+// therefore zero or tagged with the other parity, and none reads as
+// published before its tile publishes it.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kTagValid = 1ull << 63;
+
+__device__ __forceinline__ uint64_t small_tag(uint32_t parity) {
+    return kTagValid | ((uint64_t)parity << 62);
+}
+__device__ __forceinline__ bool small_published(uint64_t word, uint32_t parity) {
+    return (word >> 62) == (2ull | parity);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *state) {
+    __shared__ uint32_t s_cnt[kWaves], s_first[kWaves], s_last[kWaves], s_imax[kWaves];
+    __shared__ uint32_t s_lb_c[kWaves], s_lb_l[kWaves], s_err;
+    __shared__ int32_t s_max;                   // the last tile's longest segment
+    constexpr uint32_t kStride = kDocSmallLine / 8;     // words per record line
+    uint64_t *desc = state + kStride;           // tile t's word: desc[t * kStride]
+    const int w = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const uint32_t n = a.n_chunks;
+    const uint32_t tile = blockIdx.x;
+    const uint32_t tile_base = tile * kChunk;
+    const uint32_t wave_base = tile_base + (uint32_t)w * kWaveSpan;
+    jitter(1);
+    if (threadIdx.x == 0) {
+        s_err = 0;
+        s_max = 0;
+    }
+
+    // ---- the tile's flags, mask and record (as launch 1); every wave reads
+    // the state word while its map loads are in flight
+    WaveData<T> wd;
+    wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
+    const uint64_t sw = ld_relaxed(state);
+    const uint32_t parity = (uint32_t)(sw >> 32) & 1u;
+    const uint32_t prev_n = min((uint32_t)(sw >> 33) & 1023u, kDocSmallTiles);
+    uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
+    wave_flags(wd, a.S, a.mask, a.vec_mask, wave_base, fm, off, prv, &cnt, &last1);
+    uint32_t first = 0;
+    bool seen = false;
+    int32_t imax = 0;
+#pragma unroll
+    for (int j = 0; j < kIters; ++j) {
+        const uint32_t f = fm[j];
+        const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+        const uint64_t any = __ballot(f != 0u);
+        if (!seen && any) {
+            const int l = __builtin_ctzll(any);
+            const uint32_t mine = f ? pos0 + (uint32_t)__builtin_ctz(f) : 0u;
+            first = (uint32_t)read_lane((int)mine, l);
+            seen = true;
+        }
+        uint32_t p = prv[j];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            if ((f >> k) & 1u) {
+                const uint32_t pos = pos0 + (uint32_t)k;
+                if (p) imax = max(imax, (int32_t)(pos + 1u - p));
+                p = pos + 1u;
+            }
+        }
+    }
+    imax = wave_incl_max(imax);
+    if (lane == kWave - 1) s_imax[w] = (uint32_t)imax;
+    if (lane == 0) {
+        s_cnt[w] = cnt;
+        s_first[w] = first;
+        s_last[w] = last1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        DocRec rec{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            if (s_cnt[v]) {
+                if (rec.cnt)
+                    rec.imax = max(rec.imax, s_first[v] + 1u - rec.last1);
+                else
+                    rec.first = s_first[v];
+                rec.cnt += s_cnt[v];
+                rec.last1 = s_last[v];
+            }
+            rec.imax = max(rec.imax, s_imax[v]);
+        }
+        // relative to the tile: count and last1 <= 4096 (13 bits), first
+        // < 4096 (12 bits), the inner maximum < 4096 (13 bits)
+        const uint64_t f_rel = rec.cnt ? rec.first - tile_base : 0u;
+        const uint64_t l_rel = rec.cnt ? rec.last1 - tile_base : 0u;
+        jitter(5);
+        st_relaxed(desc + tile * kStride, small_tag(parity) | (uint64_t)rec.cnt | (f_rel << 13) |
+                                              (l_rel << 25) | ((uint64_t)rec.imax << 38));
+    }
+
+    // ---- the records of the earlier tiles: wave v waits for tiles
+    // 64 v .. 64 v + 63, one per lane
+    {
+        jitter(4);
+        const uint32_t rt = (uint32_t)w * kWave + (uint32_t)lane;     // record's tile
+        uint64_t d = 0;
+        bool expired = false;
+        if (rt < tile) {
+            uint32_t spins = 0;
+            d = ld_relaxed(desc + rt * kStride);
+            while (!small_published(d, parity)) {
+                if (++spins > kSpinLimit) {
+                    expired = true;
+                    d = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                d = ld_relaxed(desc + rt * kStride);
+            }
+        }
+        const uint32_t c = (uint32_t)d & 0x1fffu;
+        const uint32_t f_abs = rt * kChunk + ((uint32_t)(d >> 13) & 0xfffu);
+        const uint32_t l_rel = (uint32_t)(d >> 25) & 0x1fffu;
+        const uint32_t l_abs = l_rel ? rt * kChunk + l_rel : 0u;
+        const uint32_t im = (uint32_t)(d >> 38) & 0x1fffu;
+        const uint32_t incl = (uint32_t)wave_incl_max((int)l_abs);
+        const uint32_t csum = (uint32_t)read_lane(wave_incl_sum((int)c), kWave - 1);
+        const bool bad = __ballot(expired) != 0;
+        if (lane == kWave - 1) {
+            s_lb_c[w] = csum;
+            s_lb_l[w] = incl;
+        }
+        if (bad && lane == 0) atomicOr(&s_err, (uint32_t)PSQ_DATA_WORKSPACE);
+        __syncthreads();
+        if (tile == n - 1) {
+            // segments that end at an earlier tile's first boundary, and the
+            // earlier tiles' inner maxima
+            uint32_t p = (uint32_t)wave_shr1((int)incl, 0);
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v)
+                if (v < w) p = max(p, s_lb_l[v]);
+            uint32_t m = im;
+            if (c && p) m = max(m, f_abs + 1u - p);
+            m = (uint32_t)read_lane(wave_incl_max((int)m), kWave - 1);
+            if (lane == 0) atomicMax(&s_max, (int32_t)m);
+        }
+    }
+    uint32_t base_c = 0, base_l = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        base_c += s_lb_c[v];
+        base_l = max(base_l, s_lb_l[v]);
+    }
+
+    // ---- the boundaries, from the flags still in registers
+    uint32_t agg_c = 0, agg_l = 0, pc = 0, pl = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        if (v == w) {
+            pc = agg_c;
+            pl = agg_l;
+        }
+        agg_c += s_cnt[v];
+        if (s_last[v]) agg_l = s_last[v];
+    }
+    const bool last = tile == n - 1;
+    const uint32_t bc = base_c + pc;
+    const uint32_t bl = pl ? pl : base_l;
+    int32_t lmax = 0;
+    bool oob = false;
+#pragma unroll
+    for (int j = 0; j < kIters; ++j) {
+        const uint32_t f = fm[j];
+        if (f) {
+            const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+            uint32_t o = bc + off[j];
+            uint32_t p = prv[j] ? prv[j] : bl;
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                if ((f >> k) & 1u) {
+                    const uint32_t pos = pos0 + (uint32_t)k;
+                    if (o < a.total) {
+                        a.cu[o] = (int32_t)pos;
+                        if (a.cu2) a.cu2[o] = (int32_t)pos;
+                    } else {
+                        oob = true;
+                    }
+                    if (last && p) lmax = max(lmax, (int32_t)(pos + 1u - p));
+                    p = pos + 1u;
+                    ++o;
+                }
+            }
+        }
+    }
+    if (!last) return;
+
+    // ---- the last tile: scalars, then the state of the next call
+    lmax = wave_incl_max(lmax);
+    if (lane == kWave - 1) atomicMax(&s_max, lmax);
+    if (oob) atomicOr(&s_err, (uint32_t)PSQ_DATA_WORKSPACE);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t nseg = base_c + agg_c;
+        const uint32_t last_l = agg_l ? agg_l : base_l;
+        int32_t mx = s_max;
+        uint32_t st = s_err;
+        if (nseg <= a.total) {
+            a.cu[nseg] = (int32_t)a.total;
+            if (a.cu2) a.cu2[nseg] = (int32_t)a.total;
+            *a.num_segments = (int32_t)nseg;
+        } else {
+            st |= PSQ_DATA_WORKSPACE;
+        }
+        if (last_l) mx = max(mx, (int32_t)(a.total + 1u - last_l));
+        *a.max_seqlen = mx;
+        if (a.status) *a.status = (int32_t)st;
+        if (a.pad_between) *a.pad_between = 0;
+    }
+    if (w == 0) {
+        for (uint32_t t = n + (uint32_t)lane; t < prev_n; t += kWave)
+            st_relaxed(desc + t * kStride, 0ull);
+        if (lane == 0) {
+            jitter(2);
+            st_relaxed(state, ((uint64_t)n << 33) | ((uint64_t)(parity ^ 1u) << 32));
+        }
+    }
+}
+
 // The metadata launches, then the collapse copies in one-wave workgroups.
 // The copies are not fused into the metadata grid: on MI355X the 8 GiB
 // collapse of the stage-embedding workload streamed 3 % faster in its own
 // launch of one-wave workgroups (1 KiB each) than as 256-thread workgroups
 // appended to the metadata grid.
 template <typename T>
-hipError_t launch_typed(DocArgs<T> a, const psq_copy *copies, int n_copies,
-                        hipStream_t stream) {
+hipError_t launch_typed(DocArgs<T> a, uint64_t *small_state, const psq_copy *copies,
+                        int n_copies, hipStream_t stream) {
     if (a.n_chunks <= 1) {
         hipLaunchKernelGGL((k_doc_scatter<T, true>), dim3(1), dim3(kThreads), 0, stream, a);
+    } else if (a.n_chunks <= kDocSmallTiles) {
+        hipLaunchKernelGGL(k_doc_small<T>, dim3(a.n_chunks), dim3(kThreads), 0, stream, a,
+                           small_state);
     } else {
         hipLaunchKernelGGL(k_doc_reduce<T>, dim3(a.n_groups), dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
@@ -491,6 +743,7 @@ void doc_grid(uint32_t total, uint32_t *n_chunks, uint32_t *cpw, uint32_t *n_gro
 size_t doc_segments_workspace(int64_t B, int64_t S) {
     uint32_t nc, cpw, ng;
     doc_grid((uint32_t)(B * S), &nc, &cpw, &ng);
+    if (nc >= 2 && nc <= kDocSmallTiles) return kWsDocEnd;
     return round_up(kWsDocOffset + sizeof(DocRec) * (size_t)ng, 256);
 }
 
@@ -505,15 +758,16 @@ hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_
     const int vec_in = ((uintptr_t)doc % 16) == 0;
     const int vec_mask = ((uintptr_t)mask % 4) == 0;
     DocRec *recs = (DocRec *)((char *)workspace + kWsDocOffset);
+    uint64_t *small_state = (uint64_t *)((char *)workspace + kWsDocSmallOffset);
     if (doc_dtype == PSQ_I32) {
         DocArgs<int32_t> a{(const int32_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in,
                            vec_mask, cu, cu2, num_segments, max_seqlen, mask, status,
                            pad_between, recs};
-        return launch_typed(a, copies, n_copies, stream);
+        return launch_typed(a, small_state, copies, n_copies, stream);
     }
     DocArgs<int64_t> a{(const int64_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in, vec_mask,
                        cu, cu2, num_segments, max_seqlen, mask, status, pad_between, recs};
-    return launch_typed(a, copies, n_copies, stream);
+    return launch_typed(a, small_state, copies, n_copies, stream);
 }
 
 }  // namespace psq

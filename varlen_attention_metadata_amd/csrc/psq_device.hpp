@@ -78,15 +78,25 @@ struct WsHeader {
     int32_t total;
     uint64_t fin;        // finished count (high half) | status bits (low half)
 };
-// The document-map kernels keep one 16-byte record per workgroup (at most
-// kDocMaxGroups) in a scratch region right after the header.  They neither
-// need it zero-filled nor clear it, and no other kernel touches it, so the
-// zero-filled parts of a shared workspace stay zero-filled.
+// The document-map region follows the header; no other kernel touches it,
+// so the zero-filled parts of a shared workspace stay zero-filled.
+//  - Records of the two-launch path: one 16 bytes per workgroup, at most
+//    kDocMaxGroups.  Written before they are read; never cleared.
+//  - State of the one-launch path for maps of 2..kDocSmallTiles chunks: a
+//    64-bit word (call parity, previous tile count) on a 128-byte line of its
+//    own, then one tagged 64-bit record word per tile, each on its own line
+//    (every workgroup reads the lines of all tiles before it: spread over
+//    many lines, those reads do not queue on a few).  Zero-filled once with
+//    the workspace; every call leaves it consistent for the next.
 constexpr size_t kWsDocOffset = 256;
 constexpr uint32_t kDocMaxGroups = 1024;
-constexpr size_t kWsDocBytes = 16 * (size_t)kDocMaxGroups;
+constexpr uint32_t kDocSmallTiles = 256;
+constexpr size_t kDocSmallLine = 128;
+constexpr size_t kWsDocSmallOffset = kWsDocOffset + 16 * (size_t)kDocMaxGroups;
+constexpr size_t kWsDocSmallBytes = kDocSmallLine * (1 + (size_t)kDocSmallTiles);
+constexpr size_t kWsDocEnd = (kWsDocSmallOffset + kWsDocSmallBytes + 255) / 256 * 256;
 // per-row look-back descriptors of the multi-workgroup table kernel
-constexpr size_t kWsDescOffset = kWsDocOffset + kWsDocBytes;
+constexpr size_t kWsDescOffset = kWsDocEnd;
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

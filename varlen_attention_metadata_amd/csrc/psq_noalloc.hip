@@ -10,11 +10,12 @@
 // that device current) on the first call there, and only that address is
 // ever handed to a kernel.
 //
-// The kernels keep one 16-byte record per workgroup in the scratch, at most
-// 1024 of them whatever the map's size, and write every record they read in
-// the same call, so the array needs no clearing: whatever an earlier call
-// left there is overwritten before it is read.  Calls that overlap in time on
-// one GPU (two streams, two host threads) share the array and race.
+// The kernels keep their records (at most 1024 of 16 bytes, whatever the
+// map's size) and the small maps' protocol state in the scratch.  The state
+// must start zero-filled, so the first call on a device enqueues one fill
+// kernel on its stream before its own kernels; every call then leaves the
+// scratch ready for the next.  Calls that overlap in time on one GPU (two
+// streams, two host threads) share the array and race.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -26,7 +27,7 @@
 namespace {
 
 constexpr size_t kScratchBytes = PSQ_NOALLOC_SCRATCH_BYTES;
-static_assert(kScratchBytes >= psq::kWsDocOffset + psq::kWsDocBytes,
+static_assert(kScratchBytes >= psq::kWsDocEnd,
               "the scratch holds the largest document-map workspace");
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
@@ -35,8 +36,10 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mutex;
 void *g_scratch[kMaxDevices];   // per device: the device address of `scratch`
 
-// The current device's copy of `scratch`.  Returns PSQ_OK or PSQ_ERR_HIP.
-int scratch_address(void **out) {
+// The current device's copy of `scratch`; on the first call on a device,
+// its address is looked up and a zero fill is enqueued on `stream`.  Returns
+// PSQ_OK or PSQ_ERR_HIP.
+int scratch_address(hipStream_t stream, void **out) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PSQ_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mutex);
@@ -44,6 +47,7 @@ int scratch_address(void **out) {
         void *p = nullptr;
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
             return PSQ_ERR_HIP;
+        if (psq::launch_zero_fill(p, kScratchBytes, stream) != hipSuccess) return PSQ_ERR_HIP;
         g_scratch[dev] = p;
     }
     *out = g_scratch[dev];
@@ -67,7 +71,7 @@ extern "C" int psq_params_from_doc_ids_noalloc(const void *doc_ids, int doc_dtyp
     // the array's bound explicit should that ever change
     if (psq::doc_segments_workspace(B, S) > kScratchBytes) return PSQ_ERR_OVERFLOW;
     void *ws = nullptr;
-    const int rc = scratch_address(&ws);
+    const int rc = scratch_address((hipStream_t)stream, &ws);
     if (rc != PSQ_OK) return rc;
     const hipError_t e = psq::launch_doc_segments(doc_ids, doc_dtype, B, S, cu_seqlens, nullptr,
                                                   num_segments, max_seqlen, padding_mask,
