@@ -46,26 +46,26 @@ METRIC = "packed tokens/sec (G tok/s) + achieved HBM GB/s vs MI355X peak, per co
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stage_embedding.json")
 
 
-# the sources of the stage-embedding step's two kernels (k_doc_segments, then
-# the collapse copy k_copies)
+# the sources of the stage-embedding step's two kernels (the one-launch map
+# k_doc_small, then the collapse copy k_copies)
 STAGE_KERNEL_SOURCES = ("k_segments.hip", "k_copy.hip", "psq_copy.hpp", "psq_device.hpp")
 
-# launch grids (work-items) of the stage step's kernels: 256 metadata tiles of
-# 256 threads, and one 64-lane workgroup per KiB of the 8 GiB + 8 MiB collapse
-STAGE_GRIDS = {"psq::k_doc_segments<int>": "65536",
+# launch grids (work-items) of the stage step's kernels: 256 map tiles of 256
+# threads, and one 64-lane workgroup per KiB of the 8 GiB + 8 MiB collapse
+STAGE_GRIDS = {"psq::k_doc_small<int>": "65536",
                "psq::k_copies<u32x4, true>": "537395200"}
 # the 1 GiB calibration copy: a one-token map, then 2^26 copy lanes
 CALIB_GRID = str((1 << 30) // 16)
 
 # per-config workloads whose launch has a grid no other launch of a counter run
 # shares, and the sources that kernel is built from (the doc_map_small map
-# shares its grid with the calibration copy's map, and thd_split_4 its grid
-# with thd_tables, so neither is listed)
+# shares its grid with the calibration copy's one-token map, and thd_split_4
+# its grid with thd_tables, so neither is listed)
 WORKLOAD_COUNTERS = {
     "pack_sources": ("psq::k_pack_rows<896u> [grid 4263296]", ("k_pack.hip", "psq_device.hpp")),
     "trainer_rectangle": ("psq::k_pack_rows<256u> [grid 61440]", ("k_pack.hip", "psq_device.hpp")),
     "pad_tail_stream": ("psq::k_pad_ids<long> [grid 16384]", ("k_padids.hip", "psq_device.hpp")),
-    "doc_map_medium": ("psq::k_doc_segments<int> [grid 2048]", ("k_segments.hip", "psq_device.hpp")),
+    "doc_map_medium": ("psq::k_doc_small<int> [grid 2048]", ("k_segments.hip", "psq_device.hpp")),
 }
 
 
@@ -75,8 +75,8 @@ WORKLOAD_COUNTERS = {
 COUNTER_TABLE = [
     ("k_copies<u32x4, true> (stage_embedding, launch 2: the collapse)",
      "psq::k_copies<u32x4, true> [grid 537395200]", "stage_copy"),
-    ("k_doc_segments<int> (stage_embedding, launch 1: the map)",
-     "psq::k_doc_segments<int> [grid 65536]", "stage_map"),
+    ("k_doc_small<int> (stage_embedding, launch 1: the map)",
+     "psq::k_doc_small<int> [grid 65536]", "stage_map"),
     ("stage_embedding step (both launches)", None, "stage_embedding"),
     ("k_pack_rows<896> (pack_sources)", WORKLOAD_COUNTERS["pack_sources"][0], "pack_sources"),
     ("k_pack_rows<256> (trainer_rectangle)", WORKLOAD_COUNTERS["trainer_rectangle"][0],
@@ -85,7 +85,7 @@ COUNTER_TABLE = [
      "psq::k_thd_small<long, 0> [grid 214016]", "thd_tables"),
     ("k_pad_ids<long> (pad_tail_stream)", WORKLOAD_COUNTERS["pad_tail_stream"][0],
      "pad_tail_stream"),
-    ("k_doc_segments<int> (doc_map_medium)", WORKLOAD_COUNTERS["doc_map_medium"][0],
+    ("k_doc_small<int> (doc_map_medium)", WORKLOAD_COUNTERS["doc_map_medium"][0],
      "doc_map_medium"),
 ]
 
@@ -120,19 +120,30 @@ def write_counters_md(out: dict, algo: dict) -> None:
     """profiles/hbm_traffic_counters.md from the scaled counters and the
     algorithmic bytes that the counter run's own workloads reported."""
     fmt = lambda x: f"{x:,.0f}".replace(",", " ")
-    cal = out["kernels"]["calibration_copy_1GiB"]
+    ks = out["kernels"]
+    cal = ks["calibration_copy_1GiB"]
+    cross = out["library_copy_1GiB_cross_check"]
     lines = ["# HBM traffic from counters (FETCH_SIZE, WRITE_SIZE)", "",
              "Commands (on an MI355X, from the repository root), one counter per run:", "",
              "```", COUNTER_COMMANDS, "```", "",
-             "`--profile-launches 3` first launches a plain 1 GiB device copy: the collapse "
-             "path with a", "one-token map. It then launches each workload three times. The "
-             "stage-embedding step is", "two launches: the map kernel, then the collapse copy. "
-             "`--launch-info` records each", "workload's algorithmic bytes, computed by the "
-             "same code as the bench's rooflines.", "",
-             f"Calibration: the 1 GiB copy reads as FETCH_SIZE = {fmt(cal['fetch_kib'])} KiB and "
-             f"WRITE_SIZE = {fmt(cal['write_kib'])} KiB", "per dispatch. So:", "",
-             f"- read bytes = FETCH_SIZE × 1024 × {out['fetch_scale']};",
-             f"- write bytes = WRITE_SIZE × 1024 × {out['write_scale']}.", "",
+             "`--profile-launches 3` first launches torch's `zero_` and `sum` over a 1 GiB "
+             "int64 tensor", "(the calibration) and the library's own 1 GiB copy (the "
+             "collapse path with a one-token", "map, a cross-check), three times each. It then "
+             "launches each workload three times.", "The stage-embedding step is two launches: "
+             "the map kernel, then the collapse copy.", "`--launch-info` records each "
+             "workload's algorithmic bytes, computed by the same code as", "the bench's "
+             "rooflines.", "",
+             "Calibration, on kernels this library did not write, over one 1 GiB int64 tensor:",
+             "",
+             f"- torch `sum` reads it once: FETCH_SIZE = "
+             f"{fmt(ks['calibration_sum_1GiB']['fetch_kib'])} KiB per dispatch, so read bytes = "
+             f"FETCH_SIZE × 1024 × {out['fetch_scale']};",
+             f"- torch `zero_` writes it once: WRITE_SIZE = "
+             f"{fmt(ks['calibration_fill_1GiB']['write_kib'])} KiB per dispatch, so write bytes "
+             f"= WRITE_SIZE × 1024 × {out['write_scale']}.", "",
+             f"Cross-check: the library's own 1 GiB copy (FETCH_SIZE = {fmt(cal['fetch_kib'])} KiB, "
+             f"WRITE_SIZE = {fmt(cal['write_kib'])} KiB) then reads {cross['read_ratio']} GiB and "
+             f"writes {cross['write_ratio']} GiB per GiB copied.", "",
              "| kernel (workload) | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch | "
              "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
     for label, key, workload in COUNTER_TABLE:
@@ -196,19 +207,36 @@ def summarize_counters(fetch_csv: str, write_csv: str, launch_info: str | None =
 
     def load(path):
         per = {}
+        torch_calib = {}       # key -> (grid, [values]) of the largest grid seen
         for r in csv.DictReader(open(path)):
-            if "psq::" not in r["Kernel_Name"]:
+            name = r["Kernel_Name"]
+            if "psq::" not in name:
+                # torch's kernels over the 1 GiB int64 tensor: the largest
+                # fill of int64 and the largest sum reduction of the run
+                key = ("calibration_fill_1GiB" if "FillFunctor<long>" in name else
+                       "calibration_sum_1GiB" if "reduce_kernel" in name and "sum_functor" in name
+                       else None)
+                if key is not None:
+                    g = int(r["Grid_Size"])
+                    cur = torch_calib.get(key)
+                    if cur is None or g > cur[0]:
+                        torch_calib[key] = (g, [float(r["Counter_Value"])])
+                    elif g == cur[0]:
+                        cur[1].append(float(r["Counter_Value"]))
                 continue
-            short = kernel_short_name(r["Kernel_Name"])
+            short = kernel_short_name(name)
             # one kernel can serve several workloads: the grid tells them apart
             key = ("calibration_copy_1GiB" if r["Grid_Size"] == CALIB_GRID and "k_copies" in short
                    else f"{short} [grid {r['Grid_Size']}]")
             per.setdefault(key, []).append(float(r["Counter_Value"]))
+        for key, (_, v) in torch_calib.items():
+            per[key] = v
         return {k: statistics.median(v) for k, v in per.items()}
 
     fetch, write = load(fetch_csv), load(write_csv)
-    f_scale = (1 << 30) / 1024 / fetch["calibration_copy_1GiB"]
-    w_scale = (1 << 30) / 1024 / write["calibration_copy_1GiB"]
+    # independent scales: reads from torch's sum, writes from torch's zero_
+    f_scale = (1 << 30) / 1024 / fetch["calibration_sum_1GiB"]
+    w_scale = (1 << 30) / 1024 / write["calibration_fill_1GiB"]
     rows = {}
     for k in fetch:
         if k in write:
@@ -220,9 +248,16 @@ def summarize_counters(fetch_csv: str, write_csv: str, launch_info: str | None =
     workloads = {name: {"kernel": key, "source_hash": source_hash(srcs),
                         "bytes_per_launch": rows[key]["bytes_per_launch"]}
                  for name, (key, srcs) in WORKLOAD_COUNTERS.items() if key in rows}
+    cal = rows.get("calibration_copy_1GiB")
+    cross = None if cal is None else {
+        "read_ratio": round(cal["read_bytes"] / (1 << 30), 4),
+        "write_ratio": round(cal["write_bytes"] / (1 << 30), 4)}
     out = {"source_hash": source_hash(), "kernel": " + ".join(STAGE_GRIDS),
            "workload": "stage_embedding", "bytes_per_launch": sum(stage),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "calibration": "reads: torch sum over a 1 GiB int64 tensor (FETCH_SIZE); writes: "
+                          "torch zero_ of it (WRITE_SIZE)",
+           "library_copy_1GiB_cross_check": cross,
            "workloads": workloads, "kernels": rows}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
@@ -481,7 +516,7 @@ def setup_rect(torch, psq, lib, synth, dev):
     rows_np, rl_np, bins, q = w["rows"], w["real_len"], w["bins"], w["q"]
     N, W = rows_np.shape
     P = len(bins)
-    C = max(sum(-(-int(rl_np[i]) // q) * q for i in b) for b in bins)
+    C = w["width"]              # chosen by the host packer with the bins
     members = [i for b in bins for i in b]
     order = torch.zeros(N, dtype=torch.int32)
     order[: len(members)] = torch.tensor(members, dtype=torch.int32)
@@ -664,6 +699,24 @@ def check_outputs(torch, name, keep):
     return "bit-exact"
 
 
+def library_copy_ceiling(torch, psq, lib, dev, nbytes=4 << 30):
+    """The library's own collapse copy of 4 GiB (one-wave 1 KiB workgroups,
+    behind a one-token map: psq_process_thd with one copy), timed like the
+    stage step: the practical copy ceiling for this traffic on the chip."""
+    call, keep = setup_calibration_copy(torch, psq, lib, dev, nbytes)
+    call()
+    timer = Timer(torch)
+    for _ in range(10):
+        with timer:
+            call()
+    m, mn = timer.mean_ms()
+    del keep
+    return {"what": "the library's one-wave collapse copy of 4 GiB (psq_process_thd, one-token "
+                    "map plus one copy; the map's one workgroup is inside the timed region)",
+            "gbs_mean": round(2 * nbytes / (m * 1e-3) / 1e9, 1),
+            "gbs_best": round(2 * nbytes / (mn * 1e-3) / 1e9, 1)}
+
+
 def copy_ceiling(torch, dev, nbytes=4 << 30):
     """A device-to-device hipMemcpyAsync (torch copy_ of contiguous tensors) of
     4 GiB: context for the collapse copy's rate."""
@@ -721,6 +774,19 @@ def profile_launches(torch, psq, lib, synth, dev, n, info_path=None):
     counter run; prints what ran, in launch order.  With ``info_path``, writes
     each workload's algorithmic bytes there (the stage step also split into
     its collapse copy and its map)."""
+    # counter calibration on kernels this library did not write: torch's
+    # zero_ of a 1 GiB int64 tensor writes 1 GiB once, and torch's sum over
+    # it reads 1 GiB once
+    big = torch.empty(1 << 27, dtype=torch.int64, device=dev)
+    for _ in range(n):
+        big.zero_()
+    torch.cuda.synchronize()
+    for _ in range(n):
+        big.sum()
+    torch.cuda.synchronize()
+    print(f"[profile] torch zero_ and sum over 1 GiB: {n} launches each", file=sys.stderr,
+          flush=True)
+    del big
     runs = [("calibration_copy_1GiB",
              lambda: (lambda c: (c[0], None, 1 << 31, None, c[1]))(
                  setup_calibration_copy(torch, psq, lib, dev)))]
@@ -754,6 +820,67 @@ def roofline(algo_bytes, mean_ms, traffic=None):
     gbs = algo_bytes / (mean_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def oracle_workload(name, synth):
+    """The CPU oracle on a per-config workload: (run, description).  ``run``
+    makes the computation of the GPU call on the same seeded inputs (drawn
+    again from the same generators)."""
+    import oracle
+    if name in ("doc_map_small", "doc_map_medium"):
+        d = synth.doc_map_small() if name == "doc_map_small" else synth.doc_map_medium()
+        return (lambda: oracle.doc_segments(d, want_mask=False)), \
+            f"segmentation of the whole map {list(d.shape)}"
+    if name in ("thd_tables", "thd_split_4"):
+        w = synth.thd_tables()
+        L, Lp, S = w["seq_lens"], w["seq_lens_padded"], w["S"]
+        keys = ("input_ids", "labels", "position_ids")
+
+        def run():
+            if name == "thd_tables":
+                oracle.thd_tables(L, Lp, S)
+            else:
+                oracle.split_thd(L, Lp, S, 4)
+            for k in keys:
+                oracle.copy_rows(w[k], 1, w[k].nbytes, w[k].nbytes)
+        what = "metadata and mask" if name == "thd_tables" else "metadata and mask in 4 row groups"
+        return run, f"the whole batch {list(L.shape)}, S={S}: {what}, three int64 collapses"
+    if name == "pack_sources":
+        w = synth.pack_sources()
+        return (lambda: oracle.pack(w["src"], w["src_off"], w["real_len"], w["q"],
+                                    w["pack_start"], w["capacity"], fold=True)), \
+            f"all {w['real_len'].size} sources into {w['pack_start'].size - 1} packs"
+    if name == "pad_tail_stream":
+        w = synth.pad_tail_stream()
+        return (lambda: oracle.pad_mask_from_ids(w["input_ids"], w["pad_id"])), \
+            f"the whole stream of {w['input_ids'].size} ids"
+    if name == "trainer_rectangle":
+        w = synth.trainer_rectangle()
+        return (lambda: oracle.pack_rect(w["rows"], w["real_len"], w["q"], w["bins"],
+                                         width=w["width"])), \
+            f"all {w['real_len'].size} rows into {len(w['bins'])} bins"
+    raise KeyError(name)
+
+
+def time_oracle(run, reps=3):
+    """One warm-up run, then the median of ``reps`` runs (seconds)."""
+    run()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2]
+
+
+def per_config_cpu_baseline(name, synth, tokens, gpu_ms, host):
+    run, what = oracle_workload(name, synth)
+    t = time_oracle(run)
+    return {"value": round(tokens / t / 1e9, 6), "unit": "Gtok/s", "seconds": round(t, 6),
+            "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload on the same seeded inputs ({what}), one warm-up then "
+                      f"the median of 3, single-threaded C at -O2",
+            "gpu_speedup": round(t / (gpu_ms * 1e-3), 1), "host": host}
 
 
 def cpu_baseline(torch, keep):
@@ -793,7 +920,10 @@ WORKLOAD_OF = {
     "k_thd_small": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses "
                    "(whole batch, and split into 4 row groups)",
     "k_thd_tables_copy": "length tables above 2048 entries, with collapses",
-    "k_doc_segments": "doc_map_small [4,64] and doc_map_medium [8,4096]",
+    "k_doc_small": "document maps of 2..256 chunks of 4096 positions (one launch)",
+    "k_doc_scatter": "document maps of one chunk (one workgroup), or launch 2 of maps above "
+                     "256 chunks",
+    "k_doc_reduce": "launch 1 of document maps above 256 chunks",
     "k_pad_ids": "pad_tail_stream: 131072 int64 ids with a pad tail",
     "k_zero_fill": "workspace zero fill (once per workspace)",
 }
@@ -803,13 +933,15 @@ WORKLOAD_OF = {
 GRID_LABEL = {
     ("k_pack_rows", "4263296"): "pack_sources: 65536 sources -> 3506 packs of 16384 slots",
     ("k_pack_rows", "61440"): "trainer_rectangle: 256 rows -> 15 token-budget bins",
-    ("k_doc_segments", "256"): "doc_map_small [4,64]",
-    ("k_doc_segments", "2048"): "doc_map_medium [8,4096]",
-    ("k_doc_segments", "65536"): "stage_embedding step, launch 1: doc map [32,32768] -> "
-                                 "cu_seqlens, max_seqlen, mask",
+    ("k_doc_scatter", "256"): "doc_map_small [4,64] (and the one-token maps of the copy "
+                              "calibrations and ceiling)",
+    ("k_doc_small", "2048"): "doc_map_medium [8,4096]",
+    ("k_doc_small", "65536"): "stage_embedding step, launch 1: doc map [32,32768] -> "
+                              "cu_seqlens, max_seqlen, mask",
     ("k_copies", "537395200"): "stage_embedding step, launch 2: bf16 [32,32768,4096] + int64 "
                                "positions collapse (8 GiB + 8 MiB)",
     ("k_copies", "67108864"): "1 GiB calibration copy (counter runs only)",
+    ("k_copies", "268435456"): "4 GiB one-wave copy: the library's copy ceiling",
     ("k_zero_fill", "64"): "launch floor: psq_workspace_init of 256 bytes (isolated, back to "
                            "back and in a HIP graph)",
 }
@@ -924,19 +1056,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int32",
+        "dtype": "int32 map; bf16 hidden and int64 positions copied bitwise",
         "data": "synthetic (seeded generators; bf16 hidden N(0,1) drawn on the device)",
         "parity": parity,
         "config": dict(info, **{"algorithmic_bytes_per_step": algo,
                                 "hbm_gbs_per_step": round(algo / (ms_per_step * 1e-3) / 1e9, 1)}),
         "roofline": dict(roofline(algo, k_mean, traffic),
-                         kernel="k_doc_segments<int> + k_copies<u32x4,true>: one psq_process_thd "
+                         kernel="k_doc_small<int> + k_copies<u32x4,true>: one psq_process_thd "
                                 "call, the metadata launch then the collapse copy (HIP events "
                                 "bracket both)",
                          kernel_ms_mean=round(k_mean, 4), kernel_ms_median=round(timer.median_ms(), 4),
                          kernel_ms_min=round(k_min, 4)),
     }
 
+    host = host_cpu()
     if not args.no_per_config:
         per = {}
         flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -968,14 +1101,20 @@ def main():
                 "gtok_s": round(c_tok / (m * 1e-3) / 1e9, 4), "tokens_per_call": c_tok,
                 "algorithmic_bytes": c_algo, "roofline": roofline(c_algo, m, workload_traffic(name)),
                 "parity": parity})
-            print(f"[bench] {name}: {m * 1e3:.2f} us, parity {parity}", file=sys.stderr, flush=True)
             del c_keep
+            if not args.no_cpu_baseline:
+                per[name]["cpu_baseline"] = per_config_cpu_baseline(name, synth, c_tok, m, host)
+            print(f"[bench] {name}: {m * 1e3:.2f} us, parity {parity}"
+                  + (f", oracle {per[name]['cpu_baseline']['seconds'] * 1e3:.2f} ms"
+                     if "cpu_baseline" in per[name] else ""), file=sys.stderr, flush=True)
         per["stage_embedding"] = {"us_mean": round(k_mean * 1e3, 2), "gtok_s": result["value"],
                                   "roofline": roofline(algo, k_mean, traffic),
-                                  "parity": result["parity"]}
+                                  "parity": result["parity"],
+                                  "cpu_baseline": "the top-level cpu_baseline"}
         result["per_config"] = per
         del flush_buf
         result["copy_ceiling"] = copy_ceiling(torch, dev)
+        result["copy_ceiling_library"] = library_copy_ceiling(torch, psq, lib, dev)
         result["launch_floor"] = launch_floor(torch, lib, dev, args.per_config_iters)
 
     if not args.no_cpu_baseline:

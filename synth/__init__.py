@@ -167,10 +167,11 @@ def pack_sources(seed: int = 4, N: int = 65536, capacity: int = 16384, q: int = 
             "pack_start": pack_start, "q": q, "capacity": capacity}
 
 
-def token_budget_bins(padded_len, budget: int) -> list:
+def token_budget_bins(padded_len, budget: int) -> tuple:
     """First-fit decreasing on the host: longest padded source first, each
     into the first bin with room for it.  Returns each bin's source indices
-    in the order they were placed."""
+    in the order they were placed, and each bin's fill (the padded slots it
+    holds, from the packer's own room bookkeeping)."""
     padded = np.asarray(padded_len, dtype=np.int64)
     order = sorted(range(padded.size), key=lambda i: (-int(padded[i]), i))
     bins, room = [], []
@@ -186,21 +187,23 @@ def token_budget_bins(padded_len, budget: int) -> list:
         else:
             bins.append([i])
             room.append(budget - n)
-    return bins
+    return bins, [budget - r for r in room]
 
 
 def trainer_rectangle(seed: int = 6, N: int = 256, q: int = 64, budget: int = 16384,
                       median: float = 400.0, sigma: float = 1.2, max_len: int = 8192) -> dict:
-    """A trainer micro-batch: padded rectangle, lengths, token-budget bins."""
+    """A trainer micro-batch: padded rectangle, lengths, token-budget bins,
+    and the packed row width the packer chose (its fullest bin's fill: the
+    row is as wide as the batch needs)."""
     rng_len, rng_tok = _streams(seed)
     real = _lognormal_int(rng_len, median, sigma, 1, max_len, size=N)
     W = int(real.max()) if N > 0 else 0
     rows = np.zeros((N, W), dtype=np.int64)
     for i in range(N):
         rows[i, :real[i]] = rng_tok.integers(0, TOKEN_HIGH + 1, size=int(real[i]))
-    bins = token_budget_bins(_round_up(real, q), budget)
+    bins, fill = token_budget_bins(_round_up(real, q), budget)
     return {"rows": rows, "real_len": real.astype(np.int32), "bins": bins, "q": q,
-            "budget": budget}
+            "budget": budget, "width": max(fill, default=0)}
 
 
 def pad_tail_stream(seed: int = 7, T: int = 131072, tail_hi: int = 8192) -> dict:

@@ -315,7 +315,7 @@ def test_python_api_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         psq.thd_padding_mask_from_token_ids(torch.zeros(4, dtype=torch.int64), 0)
     with pytest.raises(ValueError, match="GPU"):
-        psq.pack_padded_rows(torch.zeros((2, 4), dtype=torch.int64), [1, 2], [[0, 1]], 4)
+        psq.pack_padded_rows(torch.zeros((2, 4), dtype=torch.int64), [1, 2], [[0, 1]], 4, 8)
 
 
 def test_header_is_c_and_matches_the_binding(tmp_path):

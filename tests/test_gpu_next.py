@@ -423,7 +423,7 @@ def test_rect_page_example(dev):
     rows[1, :10] = np.arange(201, 211)
     check_rect(dev, rows, [5, 10], 4, [[0, 1]])
     say("rect page example via pack_padded_rows")
-    out = psq.pack_padded_rows(torch.from_numpy(rows).to(dev), [5, 10], [[0, 1]], 4)
+    out = psq.pack_padded_rows(torch.from_numpy(rows).to(dev), [5, 10], [[0, 1]], 4, width=20)
     assert out["width"] == 20 and tuple(out["input_ids"].shape) == (1, 20)
     assert out["cu_seqlens"][0].cpu().tolist() == [0, 5, 15]
     assert out["cu_seqlens_padded"][0].cpu().tolist() == [0, 8, 20]
@@ -455,11 +455,29 @@ def test_rect_trainer_workload(dev):
     check_rect(dev, w["rows"], w["real_len"], w["q"], w["bins"])
     say("trainer workload via pack_padded_rows")
     out = psq.pack_padded_rows(torch.from_numpy(w["rows"]).to(dev), w["real_len"], w["bins"],
-                               w["q"])
+                               w["q"], width=w["width"])
     ref = oracle.pack_rect(w["rows"], w["real_len"], w["q"], w["bins"])
-    assert out["width"] == ref["width"]
+    assert ref["status"] == 0 and out["width"] == ref["width"] == w["width"]
     assert np.array_equal(out["input_ids"].cpu().numpy(), ref["packed"])
+    assert np.array_equal(out["token_mask"].cpu().numpy(), ref["token_mask"])
     assert np.array_equal(out["cu_seqlens_flat"].cpu().numpy(), ref["cu_seqlens"])
+    assert np.array_equal(out["cu_seqlens_padded_flat"].cpu().numpy(), ref["cu_seqlens_padded"])
+    # the per-bin views are the CSR slices, each starting at 0
+    k = 0
+    for b, (c, cp) in enumerate(zip(out["cu_seqlens"], out["cu_seqlens_padded"])):
+        n = len(w["bins"][b]) + 1
+        assert c.cpu().tolist() == ref["cu_seqlens"][k:k + n].tolist()
+        assert cp.cpu().tolist() == ref["cu_seqlens_padded"][k:k + n].tolist()
+        k += n
+
+
+def test_pack_padded_rows_rejects_bad_widths_and_lengths(dev):
+    rows = torch.zeros((2, 10), dtype=torch.int64, device=dev)
+    say("pack_padded_rows: width too small, length beyond int32")
+    with pytest.raises(ValueError, match="capacity"):
+        psq.pack_padded_rows(rows, [5, 10], [[0, 1]], 4, width=19)
+    with pytest.raises(ValueError, match="int32"):
+        psq.pack_padded_rows(rows, [5, 1 << 31], [[0, 1]], 4, width=20)
 
 
 @pytest.mark.parametrize("seed", range(24))

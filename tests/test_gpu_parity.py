@@ -587,8 +587,13 @@ def test_pack_many_members_per_pack(dev):
 
 
 @pytest.mark.parametrize("case", ["overflow", "empty", "pack_range", "order_range",
-                                  "src_range", "neg_len"])
+                                  "src_range", "neg_len", "neg_len_bad_off", "neg_len_neg_off",
+                                  "neg_len_and_other_src_range", "neg_off"])
 def test_pack_error_bits(dev, case):
+    """Each status word is compared exactly with the oracle's, also when one
+    member has several faults: a member whose length is bad is not checked
+    further (its offset is not looked at), another member's faults still
+    count."""
     src = np.arange(1, 7)
     off = np.array([0, 3, 4])
     rl = np.array([3, 1, 2])
@@ -605,6 +610,14 @@ def test_pack_error_bits(dev, case):
         off = np.array([0, 3, 5])
     elif case == "neg_len":
         rl = np.array([3, -2, 2])
+    elif case == "neg_len_bad_off":
+        rl, off = np.array([3, -2, 2]), np.array([0, 100, 4])
+    elif case == "neg_len_neg_off":
+        rl, off = np.array([3, -2, 2]), np.array([0, -5, 4])
+    elif case == "neg_len_and_other_src_range":
+        rl, off = np.array([3, -2, 2]), np.array([0, 3, 5])
+    elif case == "neg_off":
+        off = np.array([0, -1, 4])
     check_pack(dev, src, off, rl, q, ps, C, True, order=order, what=case)
 
 

@@ -21,8 +21,10 @@ from varlen_attention_metadata_amd import _build
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-@pytest.mark.parametrize("source", ["k_copy.hip", "k_pack.hip", "k_thd.hip"])
+@pytest.mark.parametrize("source", ["k_copy.hip", "k_thd.hip"])
 def test_wide_streaming_stores_carry_two_wait_states(tmp_path, source):
+    """The collapse copy (alone, and fused into the table kernel) uses the
+    inline 16-byte form."""
     out = str(tmp_path / (source + ".s"))
     cmd = [_build._hipcc(), *_build.HIP_FLAGS, "--cuda-device-only", "-S",
            os.path.join(_build.CSRC, source), "-o", out]
@@ -35,3 +37,17 @@ def test_wide_streaming_stores_carry_two_wait_states(tmp_path, source):
         nxt = lines[i + 1]
         m = re.match(r"s_nop\s+(\d+)", nxt)
         assert m and int(m.group(1)) >= 1, f"{source}: '{lines[i]}' followed by '{nxt}'"
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_squeeze_uses_the_compiler_stores(tmp_path):
+    """The squeeze's stores are the compiler's non-temporal stores (the inline
+    form gained less than 1 % there), so its hazards are the compiler's."""
+    out = str(tmp_path / "k_pack.hip.s")
+    cmd = [_build._hipcc(), *_build.HIP_FLAGS, "--cuda-device-only", "-S",
+           os.path.join(_build.CSRC, "k_pack.hip"), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = open(out).read()
+    assert not re.search(r"global_store_dword\S*.*sc1 nt", text)
+    assert re.search(r"global_store_dwordx2 .* nt", text)

@@ -1,6 +1,7 @@
 """Checks on the seeded input generators (CPU only)."""
 import numpy as np
 
+import oracle
 import synth
 
 
@@ -61,13 +62,16 @@ def test_run_positions():
 
 def test_token_budget_bins():
     padded = np.array([64, 128, 16384, 64, 8192, 8192, 192])
-    bins = synth.token_budget_bins(padded, 16384)
+    bins, fill = synth.token_budget_bins(padded, 16384)
     flat = sorted(i for b in bins for i in b)
     assert flat == list(range(padded.size))
     assert all(int(padded[b].sum()) <= 16384 for b in bins)
+    assert fill == [int(padded[b].sum()) for b in bins]
     assert bins[0] == [2]                     # the longest source opens the first bin
     w = synth.trainer_rectangle()
     rows, rl = w["rows"], w["real_len"]
+    # the packer's width is the fullest bin's padded sum, as the oracle computes it
+    assert w["width"] == oracle.trainer_width(rl, w["bins"], w["q"])
     assert rows.shape == (256, int(rl.max()))
     assert sorted(i for b in w["bins"] for i in b) == list(range(256))
     for i in range(0, 256, 17):               # zero past each length

@@ -408,17 +408,17 @@ def thd_padding_mask_from_token_ids(input_ids: torch.Tensor, padding_token_id: i
     return mask
 
 
-def pack_padded_rows(input_ids: torch.Tensor, input_lengths, bins, pad_to: int,
-                     width: int | None = None, fold: bool = False, pad_token: int = 0) -> dict:
+def pack_padded_rows(input_ids: torch.Tensor, input_lengths, bins, pad_to: int, width: int,
+                     fold: bool = False, pad_token: int = 0) -> dict:
     """Trainer packs: squeeze the padded rectangle ``input_ids [N, W]`` into bins.
 
     ``bins`` lists each bin's row indices (chosen on the host, e.g. by token
     budget).  Row ``i`` holds ``input_lengths[i]`` real tokens; each is padded
-    to a multiple of ``pad_to`` and a bin's rows are laid end to end.  The
-    output row width defaults to the widest bin's padded sum (the row is as
-    wide as the batch needs), computed on the host from ``input_lengths``;
-    the trainer path leaves ``fold`` off.  Returns the keys of
-    :func:`pack_rows` plus ``width``.
+    to a multiple of ``pad_to`` and a bin's rows are laid end to end in an
+    output row of ``width`` slots.  The host packer that chose the bins knows
+    the width the batch needs (its fullest bin's padded sum); a bin that does
+    not fit raises ``ValueError``.  The trainer path leaves ``fold`` off.
+    Returns the keys of :func:`pack_rows` plus ``width``.
     """
     _require_gpu(input_ids, "input_ids")
     if input_ids.dtype != torch.int64 or input_ids.dim() != 2 or not input_ids.is_contiguous():
@@ -428,10 +428,9 @@ def pack_padded_rows(input_ids: torch.Tensor, input_lengths, bins, pad_to: int,
     lens_host = torch.as_tensor(input_lengths, dtype=torch.int64).cpu()
     if lens_host.numel() != N:
         raise ValueError("input_lengths must hold one length per row")
+    if N and (int(lens_host.min()) < -(1 << 31) or int(lens_host.max()) >= (1 << 31)):
+        raise ValueError("input_lengths must fit int32")
     bins = [list(map(int, b)) for b in bins]
-    if width is None:
-        lh = lens_host.tolist()
-        width = max((sum(-(-lh[i] // pad_to) * pad_to for i in b) for b in bins), default=0)
     width = int(width)
     if width < 1:
         raise ValueError("the packed row width must be at least 1")

@@ -19,23 +19,21 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
-// Streaming stores: non-temporal, at agent scope (sc1 nt).  Data that is
-// written once and not read again by the kernel.  On MI355X an 8 GiB copy of
-// one-wave 1 KiB workgroups streamed at 6.73 TB/s with these stores, against
-// 6.67 TB/s with plain non-temporal stores (nt) and 6.58 TB/s with default
-// stores; the loads stay non-temporal either way.
+// Streaming stores: non-temporal, at agent scope (sc1 nt), for the 16-byte
+// units of the collapse copy (data written once and not read again).  On
+// MI355X the stage-embedding step (an 8 GiB copy of one-wave 1 KiB
+// workgroups) took 2.550 ms with these stores against 2.601 ms with the
+// compiler's non-temporal stores (nt only), 2 % apart in two alternating
+// runs each; the squeeze gained only 0.4 % from them and uses the builtin.
 // The compiler's hazard tracking does not see inside inline assembly: on
 // gfx940 and later a store of more than 8 bytes needs two wait states before
-// a VALU instruction may write its data registers, so the 16-byte form
-// carries its own s_nop 1 (two wait states).  With one wait state a squeeze
-// build whose scheduler placed a register move right after the mask store
-// wrote wrong mask bytes.
+// a VALU instruction may write its data registers, so the store carries its
+// own s_nop 1 (two wait states).  With one wait state a squeeze build whose
+// scheduler placed a register move right after the mask store wrote wrong
+// mask bytes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void store_stream(u32x4 *p, u32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ void store_stream(int64_t *p, int64_t v) {
-    asm volatile("global_store_dwordx2 %0, %1, off sc1 nt" : : "v"(p), "v"(v) : "memory");
 }
 
 // ---------------------------------------------------------------------------
