@@ -1235,7 +1235,10 @@ hipError_t launch_thd_tables(const void *L, const void *Lp, int lens_dtype, int6
                              int32_t *pad_between, int32_t *cu_width, uint8_t *mask,
                              int32_t *status, void *workspace, const psq_copy *copies,
                              int n_copies, hipStream_t stream) {
-    const uint32_t n_chunks = S > 0 ? (uint32_t)((S + kSlots - 1) / kSlots) : 1u;
+    // with no rows the row length changes no output; any S is accepted there
+    // (B * S = 0), so it is not carried into the kernels' 32-bit arithmetic
+    if (B == 0) S = 0;
+    const uint32_t n_chunks = S > 0 ? (uint32_t)(((uint64_t)S + kSlots - 1) / kSlots) : 1u;
     const uint64_t groups = (uint64_t)B * n_chunks;
     const uint32_t n_meta = (uint32_t)(groups > 0 ? groups : 1);
     const int vec_mask = ((uintptr_t)mask % 16) == 0;

@@ -240,7 +240,7 @@ int psq_pack_rows(const int64_t *src_tokens, int64_t src_len, const int64_t *src
                   size_t workspace_bytes, void *stream) {
     if (N < 0 || P < 0 || src_len < 0 || pad_to < 1 || capacity < 1) return PSQ_ERR_ARG;
     if (capacity > (1 << 30)) return PSQ_ERR_ARG;
-    if (N + P >= kI32Limit) return PSQ_ERR_OVERFLOW;
+    if (N >= kI32Limit || P >= kI32Limit - N) return PSQ_ERR_OVERFLOW;   // N + P, unformed
     if (pack_start == nullptr || status == nullptr) return PSQ_ERR_ARG;
     if (P > 0 && (packed == nullptr || token_mask == nullptr || cu_seqlens == nullptr ||
                   cu_seqlens_padded == nullptr))
@@ -265,7 +265,7 @@ int psq_pack_padded_rows(const int64_t *rows, int64_t W, const int32_t *real_len
                          size_t workspace_bytes, void *stream) {
     if (N < 0 || P < 0 || W < 0 || pad_to < 1 || capacity < 1) return PSQ_ERR_ARG;
     if (capacity > (1 << 30)) return PSQ_ERR_ARG;
-    if (N + P >= kI32Limit) return PSQ_ERR_OVERFLOW;
+    if (N >= kI32Limit || P >= kI32Limit - N) return PSQ_ERR_OVERFLOW;   // N + P, unformed
     if (W > 0 && N > ((int64_t)1 << 62) / W) return PSQ_ERR_OVERFLOW;
     if (pack_start == nullptr || status == nullptr) return PSQ_ERR_ARG;
     if (P > 0 && (packed == nullptr || token_mask == nullptr || cu_seqlens == nullptr ||
