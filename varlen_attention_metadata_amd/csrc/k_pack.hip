@@ -10,11 +10,14 @@
 //
 // Work layout: one single-wave workgroup (64 threads) per (pack, chunk of
 // 896 slots; 256 when 896-slot chunks would give fewer than 1024
-// workgroups: a trainer batch of 15 bins then takes 9.5 instead of 11.6 us).  The wave scans its pack's member lengths into LDS (64
-// members per batch; a saturating scan so an overfull pack is detected
-// exactly), marks each member's start slot in a per-chunk owner map and
-// fills the map with one max scan, so every slot finds its member with one
-// LDS read and takes either the member's token or the pad token.  Lane l
+// workgroups: a trainer batch of 15 bins then takes 9.5 instead of 11.6 us).
+// The wave scans its pack's member lengths into LDS (64 members per batch;
+// a saturating scan so an overfull pack is detected exactly).  Each lane
+// then finds its slots' owners among the few members that meet the chunk,
+// comparing their starts in registers (on MI355X 0.4 % faster on the
+// 65536-source workload than a per-chunk owner map filled in LDS by a max
+// scan, 3 % on the trainer batch), and every slot takes either its member's
+// token or the pad token.  Lane l
 // owns slots l, l+64, l+128, ... of the chunk, so every load and store
 // instruction of the wave covers 64 consecutive slots.  Every slot issues
 // its load (a pad slot re-reads a token of its own member, which is already
@@ -74,9 +77,9 @@ __device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
     return x;
 }
 
-// At most 128 VGPRs (4 waves per SIMD): the register budget it was tuned at.
+// 4 to 5 waves per SIMD: 5 measured best for this shape (6 were slower).
 template <uint32_t kSlots>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_pack_rows(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 5))) void k_pack_rows(
     const int64_t *__restrict__ src, int64_t src_len, const int64_t *__restrict__ src_off,
     int64_t src_stride, const int32_t *__restrict__ real_len, int64_t N, int32_t q,
     const int32_t *__restrict__ order, const int64_t *__restrict__ pack_start, int64_t P,
@@ -84,13 +87,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     uint8_t *__restrict__ tmask, int32_t *__restrict__ cu, int32_t *__restrict__ cp,
     int32_t *__restrict__ status, WsHeader *__restrict__ ws, uint32_t n_chunks, int vec_mask) {
     constexpr int kPerThread = (int)(kSlots / kThreads);   // slots per thread: one round
-    constexpr int kOwnWords = (int)(kSlots / kThreads / 2);  // owner-map words per thread
-    static_assert(kSlots % 16 == 0 && kOwnWords >= 1, "whole 16-byte LDS stores");
+    static_assert(kSlots % 16 == 0 && kSlots % kThreads == 0, "whole 16-byte LDS stores");
     __shared__ uint32_t m_start[kMembers];
     __shared__ uint32_t m_real[kMembers];
     __shared__ int64_t m_so[kMembers];
     __shared__ __attribute__((aligned(16))) uint8_t s_mask[kSlots];
-    __shared__ __attribute__((aligned(16))) uint16_t s_own[kSlots];
     __shared__ uint32_t s_wsum[2][kWaves];
     __shared__ uint32_t s_err;
 
@@ -193,57 +194,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const uint32_t r_lo = max(lo, first);
         const uint32_t r_hi = last_batch ? hi : min(hi, carry_pos);
         if (r_lo < r_hi) {   // uniform: r_lo, r_hi come from block-wide values
-            // Owner map: s_own[s - lo] = 1 + the last member starting at or
-            // before slot s.  Members mark their start slot, then one
-            // block-wide max scan fills the gaps (starts are non-decreasing,
-            // so a larger index is always the later member).
-            for (uint32_t e = threadIdx.x * 8u; e < kSlots; e += kThreads * 8u)
-                *(u32x4 *)(s_own + e) = u32x4{0u, 0u, 0u, 0u};
+            // Owners: slot s belongs to the last member starting at or before
+            // it (starts are non-decreasing; of equal starts, the later one).
+            // Only members j0 .. upto-1 can own a slot of [r_lo, r_hi): the
+            // last one starting at or before lo (or the batch's first), up to
+            // the last one starting before r_hi -- about 3 for this chunk
+            // size -- so each lane takes its slots' owners from their starts
+            // in registers, with no per-chunk map in LDS.
             const uint32_t my_start = m_start[threadIdx.x];
             const bool mine = (int64_t)threadIdx.x < nb;
             const int before = __syncthreads_count(mine && my_start <= lo);
-            if (mine && my_start > lo && my_start < hi &&
-                (threadIdx.x + 1 >= (uint32_t)nb || m_start[threadIdx.x + 1] != my_start))
-                s_own[my_start - lo] = (uint16_t)(threadIdx.x + 1);
-            __syncthreads();
-            {
-                // thread t owns kOwnWords consecutive words (2 entries each)
-                uint32_t v[kOwnWords];
-                const uint32_t *own_w = (const uint32_t *)s_own + threadIdx.x * kOwnWords;
-#pragma unroll
-                for (int e = 0; e < kOwnWords; ++e) v[e] = own_w[e];
-                uint32_t run = 0;
-#pragma unroll
-                for (int e = 0; e < kOwnWords; ++e) {
-                    const uint32_t a0 = max(run, v[e] & 0xffffu);
-                    const uint32_t a1 = max(a0, v[e] >> 16);
-                    run = a1;
-                    v[e] = a0 | (a1 << 16);
-                }
-                const uint32_t incl = (uint32_t)wave_incl_max((int)run);
-                if (lane == kWave - 1) s_wsum[0][w] = incl;
-                __syncthreads();
-                uint32_t pre = (uint32_t)before;
-#pragma unroll
-                for (int q2 = 0; q2 < kWaves; ++q2)
-                    if (q2 < w) pre = max(pre, s_wsum[0][q2]);
-                pre = max(pre, (uint32_t)wave_shr1((int)incl, 0));
-                uint32_t *own_o = (uint32_t *)s_own + threadIdx.x * kOwnWords;
-#pragma unroll
-                for (int e = 0; e < kOwnWords; ++e)
-                    own_o[e] = max(v[e] & 0xffffu, pre) | (max(v[e] >> 16, pre) << 16);
-            }
-            __syncthreads();
-
+            const int upto = __syncthreads_count(mine && my_start < r_hi);
+            const int j0 = before > 0 ? before - 1 : 0;
             for (uint32_t ub = r_lo; ub < r_hi; ub += kSlots) {
                 int64_t val[kPerThread];
                 bool in[kPerThread];
+                uint32_t own[kPerThread];
+#pragma unroll
+                for (int t = 0; t < kPerThread; ++t) own[t] = (uint32_t)j0;
+                for (int j = j0 + 1; j < upto; ++j) {
+                    const uint32_t st = (uint32_t)read_lane((int)my_start, j);
+#pragma unroll
+                    for (int t = 0; t < kPerThread; ++t) {
+                        const uint32_t s = ub + threadIdx.x + (uint32_t)kThreads * (uint32_t)t;
+                        own[t] = s >= st ? (uint32_t)j : own[t];
+                    }
+                }
 #pragma unroll
                 for (int t = 0; t < kPerThread; ++t) {
                     const uint32_t s = ub + threadIdx.x + (uint32_t)kThreads * (uint32_t)t;
                     in[t] = s < r_hi;
-                    // o1 >= 1 for every slot in [r_lo, r_hi)
-                    const uint32_t o1 = in[t] ? (uint32_t)s_own[s - lo] : 0u;
+                    const uint32_t o1 = in[t] ? own[t] + 1u : 0u;
                     bool tok = false;
                     int64_t idx = 0;
                     if (o1 != 0u) {
