@@ -15,7 +15,10 @@
 // load for int32 maps).  Each lane folds its 4 boundary flags into a bit
 // mask; DPP wave scans turn the popcounts into output slots, and a max scan
 // of "last boundary + 1" gives every boundary the start of the segment
-// before it.
+// before it.  A chunk's boundaries are staged in LDS in output order and
+// then written as consecutive 4-byte stores, a wave's 64 slots per store:
+// stored straight from the flags, most lanes would idle in each of up to 16
+// scattered stores per lane.
 //
 // Two launches with no cross-workgroup protocol.  Workgroup g owns `cpw`
 // consecutive chunks (one each, unless the map holds more than 1024 chunks).
@@ -127,6 +130,7 @@ struct WaveData {
     int pres[kIters];
     T left;          // the value before the span, valid when has_left
     bool has_left;
+    bool full;       // every position of the span is present (uniform)
 };
 
 // Issue the wave's loads (all of them before any is used).  A wave whose
@@ -141,8 +145,10 @@ __device__ __forceinline__ void wave_load(const T *__restrict__ doc, uint32_t to
                                           uint32_t wave_base, WaveData<T> &wd) {
     const int lane = lane_id();
     wd.has_left = wave_base > 0 && wave_base < total;
-    wd.left = doc[wd.has_left ? wave_base - 1 : 0u];
-    if (vec_in && wave_base + kWaveSpan <= total) {
+    wd.full = wave_base + kWaveSpan <= total;
+    // expected: laid out first, so no wait for the loads of the other path
+    // is placed before these loads
+    if (__builtin_expect(vec_in && wd.full, 1)) {
 #pragma unroll
         for (int j = 0; j < kIters; ++j) {
             const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
@@ -163,6 +169,12 @@ __device__ __forceinline__ void wave_load(const T *__restrict__ doc, uint32_t to
             wd.pres[j] = load4(doc, pos0, total, vec_in != 0, wd.d[j]);
         }
     }
+    // after the span's loads, as a vector load like them (the index is the
+    // same in every lane; as a scalar load it would be waited for before the
+    // loads issued after it)
+    uint32_t li = wd.has_left ? wave_base - 1 : 0u;
+    asm volatile("" : "+v"(li));
+    wd.left = doc[li];
 }
 
 // Boundary flags of a wave's loaded positions.  For sub-chunk j: fm[j] holds
@@ -181,40 +193,67 @@ __device__ __forceinline__ void wave_flags(const WaveData<T> &wd, uint32_t S,
     T carry = wd.has_left ? wd.left : (T)0;   // first use of the loads
     uint32_t run_c = 0, run_l = 0;
     const bool small_s = S < (uint32_t)kPerLane;
+    // A whole span with rows of at least 4 positions (uniform) takes
+    // straight-line code: each lane's row offset r = pos0 % S is advanced by
+    // kSub per sub-chunk, and a row starts inside the lane's 4 positions at
+    // k = 0 when r == 0, or at k = S - r when that is below 4.
+    const bool fast = wd.full && !small_s;
+    uint32_t r = 0, step = 0;
+    if (fast) {
+        r = (wave_base + (uint32_t)lane * kPerLane) % S;
+        step = kSub % S;
+    }
 #pragma unroll
     for (int j = 0; j < kIters; ++j) {
         const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
         const T *d = wd.d[j];
-        const int present = wd.pres[j];
-
-        if (mask != nullptr && present > 0) {
-            if (present == kPerLane && vec_mask) {
-                const uint32_t m = (uint32_t)(d[0] == 0) | ((uint32_t)(d[1] == 0) << 8) |
-                                   ((uint32_t)(d[2] == 0) << 16) | ((uint32_t)(d[3] == 0) << 24);
-                *(uint32_t *)(mask + pos0) = m;
-            } else {
-                // unrolled with a predicate: a runtime index into d would put
-                // the loaded values in scratch memory
-#pragma unroll
-                for (int k = 0; k < kPerLane; ++k)
-                    if (k < present) mask[pos0 + k] = (uint8_t)(d[k] == 0);
-            }
-        }
-
         const T left = shr1(d[kPerLane - 1], carry);
         uint32_t f = 0;
-        if (present > 0) {
-            const uint32_t r = pos0 % S;
+        if (fast) {
+            if (mask != nullptr) {
+                const uint32_t m = (uint32_t)(d[0] == 0) | ((uint32_t)(d[1] == 0) << 8) |
+                                   ((uint32_t)(d[2] == 0) << 16) | ((uint32_t)(d[3] == 0) << 24);
+                if (vec_mask) {
+                    *(uint32_t *)(mask + pos0) = m;
+                } else {
 #pragma unroll
-            for (int k = 0; k < kPerLane; ++k) {
-                if (k < present) {
-                    bool row_start;
-                    if (small_s)
-                        row_start = ((pos0 + (uint32_t)k) % S) == 0;
-                    else
-                        row_start = (r + (uint32_t)k == 0) || (r + (uint32_t)k == S);
-                    const T prev = (k == 0) ? left : d[k == 0 ? 0 : k - 1];
-                    if (row_start || d[k] != prev) f |= 1u << k;
+                    for (int k = 0; k < kPerLane; ++k) mask[pos0 + k] = (uint8_t)(m >> (8 * k));
+                }
+            }
+            const uint32_t to_end = S - r;    // 1 .. S
+            f = (uint32_t)(d[0] != left) | ((uint32_t)(d[1] != d[0]) << 1) |
+                ((uint32_t)(d[2] != d[1]) << 2) | ((uint32_t)(d[3] != d[2]) << 3) |
+                (r == 0 ? 1u : 0u) | (to_end < (uint32_t)kPerLane ? 1u << to_end : 0u);
+            r += step;
+            r = r >= S ? r - S : r;
+        } else {
+            const int present = wd.pres[j];
+            if (mask != nullptr && present > 0) {
+                if (present == kPerLane && vec_mask) {
+                    const uint32_t m = (uint32_t)(d[0] == 0) | ((uint32_t)(d[1] == 0) << 8) |
+                                       ((uint32_t)(d[2] == 0) << 16) | ((uint32_t)(d[3] == 0) << 24);
+                    *(uint32_t *)(mask + pos0) = m;
+                } else {
+                    // unrolled with a predicate: a runtime index into d would put
+                    // the loaded values in scratch memory
+#pragma unroll
+                    for (int k = 0; k < kPerLane; ++k)
+                        if (k < present) mask[pos0 + k] = (uint8_t)(d[k] == 0);
+                }
+            }
+            if (present > 0) {
+                const uint32_t rr = pos0 % S;
+#pragma unroll
+                for (int k = 0; k < kPerLane; ++k) {
+                    if (k < present) {
+                        bool row_start;
+                        if (small_s)
+                            row_start = ((pos0 + (uint32_t)k) % S) == 0;
+                        else
+                            row_start = (rr + (uint32_t)k == 0) || (rr + (uint32_t)k == S);
+                        const T prev = (k == 0) ? left : d[k == 0 ? 0 : k - 1];
+                        if (row_start || d[k] != prev) f |= 1u << k;
+                    }
                 }
             }
         }
@@ -235,13 +274,98 @@ __device__ __forceinline__ void wave_flags(const WaveData<T> &wd, uint32_t S,
     *last1 = run_l;
 }
 
+// The wave's first boundary (0 when it has none) and its longest segment
+// that starts at one of its own boundaries and ends at the next, before the
+// wave maximum.  Selects, not branches: a branch per position costs more
+// than the arithmetic it skips.
+__device__ __forceinline__ void wave_first_inner(const uint32_t (&fm)[kIters],
+                                                 const uint32_t (&prv)[kIters],
+                                                 uint32_t wave_base, uint32_t *first,
+                                                 int32_t *inner) {
+    const int lane = lane_id();
+    uint32_t fst = 0;
+    bool seen = false;
+    int32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kIters; ++j) {
+        const uint32_t f = fm[j];
+        const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+        const uint64_t any = __ballot(f != 0u);
+        if (!seen && any) {
+            const int l = __builtin_ctzll(any);
+            const uint32_t mine = f ? pos0 + (uint32_t)__builtin_ctz(f) : 0u;
+            fst = (uint32_t)read_lane((int)mine, l);
+            seen = true;
+        }
+        uint32_t p = prv[j];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const bool b = (f >> k) & 1u;
+            const uint32_t pos1 = pos0 + (uint32_t)k + 1u;
+            m = max(m, (b && p) ? (int32_t)(pos1 - p) : 0);
+            p = b ? pos1 : p;
+        }
+    }
+    *first = fst;
+    *inner = m;
+}
+
+// Stage a wave's boundary positions in LDS: the chunk's boundaries in order,
+// s_pos[i] the i-th, the wave's first at index `base` (the count of the
+// chunk's earlier waves).  Every index is below the chunk's boundary count,
+// at most kChunk.
+__device__ __forceinline__ void stage_positions(uint32_t *s_pos, uint32_t base,
+                                                uint32_t wave_base,
+                                                const uint32_t (&fm)[kIters],
+                                                const uint32_t (&off)[kIters]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int j = 0; j < kIters; ++j) {
+        const uint32_t f = fm[j];
+        if (f) {
+            const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
+            uint32_t o = base + off[j];
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k)
+                if ((f >> k) & 1u) s_pos[o++] = pos0 + (uint32_t)k;
+        }
+    }
+}
+
+// Write a chunk's `cnt` staged boundaries to cu[base_c ..] (and cu2), one
+// slot per thread and pass, so each wave stores 256 consecutive bytes.  With
+// `lengths`, returns the longest segment starting at one of them (the last
+// one runs to the end of the axis); otherwise 0.  *oob is set when a slot
+// falls outside the output.
+template <typename T>
+__device__ __forceinline__ int32_t flush_positions(const DocArgs<T> &a, const uint32_t *s_pos,
+                                                   uint32_t cnt, uint32_t base_c, bool lengths,
+                                                   bool *oob) {
+    int32_t lmax = 0;
+    for (uint32_t i = threadIdx.x; i < cnt; i += kThreads) {
+        const uint32_t pos = s_pos[i];
+        const uint32_t o = base_c + i;
+        if (o < a.total) {
+            a.cu[o] = (int32_t)pos;
+            if (a.cu2) a.cu2[o] = (int32_t)pos;
+        } else {
+            *oob = true;
+        }
+        if (lengths) {
+            const uint32_t nxt = i + 1u < cnt ? s_pos[i + 1u] : a.total;
+            lmax = max(lmax, (int32_t)(nxt - pos));
+        }
+    }
+    return lmax;
+}
+
 // ---------------------------------------------------------------------------
 // Launch 1: one record per workgroup, and the padding mask.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_doc_reduce(DocArgs<T> a) {
     __shared__ uint32_t s_cnt[kWaves], s_first[kWaves], s_last[kWaves], s_imax[kWaves];
-    const int w = threadIdx.x / kWave;
+    const int w = wave_id();
     const int lane = lane_id();
     const uint32_t c0 = blockIdx.x * a.cpw;
     const uint32_t c1 = min(c0 + a.cpw, a.n_chunks);
@@ -252,32 +376,9 @@ __global__ __launch_bounds__(kThreads) void k_doc_reduce(DocArgs<T> a) {
         wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
         uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
         wave_flags(wd, a.S, a.mask, a.vec_mask, wave_base, fm, off, prv, &cnt, &last1);
-        // the wave's first boundary, and its longest segment that starts at
-        // one of its own boundaries and ends at the next
-        uint32_t first = 0;
-        bool seen = false;
-        int32_t lmax = 0;
-#pragma unroll
-        for (int j = 0; j < kIters; ++j) {
-            const uint32_t f = fm[j];
-            const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
-            const uint64_t any = __ballot(f != 0u);
-            if (!seen && any) {
-                const int l = __builtin_ctzll(any);
-                const uint32_t mine = f ? pos0 + (uint32_t)__builtin_ctz(f) : 0u;
-                first = (uint32_t)read_lane((int)mine, l);
-                seen = true;
-            }
-            uint32_t p = prv[j];
-#pragma unroll
-            for (int k = 0; k < kPerLane; ++k) {
-                if ((f >> k) & 1u) {
-                    const uint32_t pos = pos0 + (uint32_t)k;
-                    if (p) lmax = max(lmax, (int32_t)(pos + 1u - p));
-                    p = pos + 1u;
-                }
-            }
-        }
+        uint32_t first;
+        int32_t lmax;
+        wave_first_inner(fm, prv, wave_base, &first, &lmax);
         lmax = wave_incl_max(lmax);
         if (lane == kWave - 1) s_imax[w] = (uint32_t)lmax;
         if (lane == 0) {
@@ -359,8 +460,9 @@ __device__ __forceinline__ void wave_records(const DocRec *__restrict__ recs, ui
 template <typename T, bool kSolo>
 __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
     __shared__ uint32_t s_wcnt[kWaves], s_wlast[kWaves];
+    __shared__ uint32_t s_pos[kChunk];          // the chunk's boundaries, in order
     __shared__ int32_t s_max;
-    const int w = threadIdx.x / kWave;
+    const int w = wave_id();
     const int lane = lane_id();
     const uint32_t g = blockIdx.x;
     const bool last = g == a.n_groups - 1;
@@ -389,42 +491,17 @@ __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
         }
         __syncthreads();
         // the chunk's totals and this wave's prefix inside the chunk
-        uint32_t agg_c = 0, agg_l = 0, pc = 0, pl = 0;
+        uint32_t agg_c = 0, agg_l = 0, pc = 0;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            if (v == w) {
-                pc = agg_c;
-                pl = agg_l;
-            }
+            if (v == w) pc = agg_c;
             agg_c += s_wcnt[v];
             if (s_wlast[v]) agg_l = s_wlast[v];
         }
-        const uint32_t bc = base_c + pc;
-        const uint32_t bl = pl ? pl : base_l;
-#pragma unroll
-        for (int j = 0; j < kIters; ++j) {
-            const uint32_t f = fm[j];
-            if (f) {
-                const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
-                uint32_t o = bc + off[j];
-                uint32_t p = prv[j] ? prv[j] : bl;
-#pragma unroll
-                for (int k = 0; k < kPerLane; ++k) {
-                    if ((f >> k) & 1u) {
-                        const uint32_t pos = pos0 + (uint32_t)k;
-                        if (o < a.total) {
-                            a.cu[o] = (int32_t)pos;
-                            if (a.cu2) a.cu2[o] = (int32_t)pos;
-                        } else {
-                            oob = true;
-                        }
-                        if (kSolo && p) lmax = max(lmax, (int32_t)(pos + 1u - p));
-                        p = pos + 1u;
-                        ++o;
-                    }
-                }
-            }
-        }
+        stage_positions(s_pos, pc, wave_base, fm, off);
+        __syncthreads();
+        // a one-chunk map's segments all start at one of its boundaries
+        lmax = max(lmax, flush_positions(a, s_pos, agg_c, base_c, kSolo, &oob));
         base_c += agg_c;
         if (agg_l) base_l = agg_l;
         __syncthreads();
@@ -457,13 +534,13 @@ __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
 
 // ---------------------------------------------------------------------------
 // One launch for maps of 2..kDocSmallTiles chunks (k_doc_small).  Workgroup
-// t reduces tile t to the record of launch 1 and publishes the record as two
-// tagged 64-bit words.  Its waves then wait until every earlier tile has
-// published and reduce those records themselves, one per lane (wave v takes
-// tiles 64 v .. 64 v + 63: no chained look-back).  The last tile also takes
-// max_seqlen from them, as the last group of launch 2 does.  The flags stay
-// in registers, so the tile is read once and no workgroup counts itself
-// finished.
+// t reduces tile t to the record of launch 1 and publishes the record as one
+// tagged 64-bit word.  It stages its boundaries in LDS, in order, while its
+// waves wait until every earlier tile has published and reduce those records
+// themselves, one per lane (wave v takes tiles 64 v .. 64 v + 63: no chained
+// look-back); then it writes them out as consecutive stores.  The last tile
+// also takes max_seqlen from the records, as the last group of launch 2
+// does.  The tile is read once and no workgroup counts itself finished.
 //
 // Tiles are workgroup ids, not tickets: a workgroup waits only on lower ids,
 // and at most 256 workgroups of 256 threads fit the chip's slots at once
@@ -474,9 +551,11 @@ __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
 // A record is one 64-bit word: bit 63 valid, bit 62 the call's parity, then
 // the tile's boundary count (bits 0..12), first boundary (13..24) and one
 // past its last boundary (25..37), both relative to the tile, and its inner
-// maximum (38..50).  The state word holds the parity (bit 32) and the
-// previous call's tile count (bits 33..42); every
-// workgroup reads it while its map loads are in flight.  Once the last tile
+// maximum (38..50).  The 32-bit state word, on the line before the records,
+// holds the parity (bit 0) and the previous call's tile count (bits 1..10);
+// every workgroup reads it while its map loads are in flight (a 32-bit word:
+// with a 64-bit one whose low half goes unused, the compiler reused that
+// half's register and so waited for this uncached load before the flags).  Once the last tile
 // has seen every other tile's record, every workgroup has read the state: it
 // clears the words of the tiles the previous call used beyond this call's
 // count and stores the next call's state (the other parity, this call's
@@ -494,13 +573,14 @@ __device__ __forceinline__ bool small_published(uint64_t word, uint32_t parity) 
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *state) {
+__global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *state,
+                                                       uint64_t *desc) {
     __shared__ uint32_t s_cnt[kWaves], s_first[kWaves], s_last[kWaves], s_imax[kWaves];
     __shared__ uint32_t s_lb_c[kWaves], s_lb_l[kWaves], s_err;
     __shared__ int32_t s_max;                   // the last tile's longest segment
+    __shared__ uint32_t s_pos[kChunk];          // the tile's boundaries, in order
     constexpr uint32_t kStride = kDocSmallLine / 8;     // words per record line
-    uint64_t *desc = state + kStride;           // tile t's word: desc[t * kStride]
-    const int w = threadIdx.x / kWave;
+    const int w = wave_id();
     const int lane = lane_id();
     const uint32_t n = a.n_chunks;
     const uint32_t tile = blockIdx.x;
@@ -516,35 +596,14 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *
     // the state word while its map loads are in flight
     WaveData<T> wd;
     wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
-    const uint64_t sw = ld_relaxed(state);
-    const uint32_t parity = (uint32_t)(sw >> 32) & 1u;
-    const uint32_t prev_n = min((uint32_t)(sw >> 33) & 1023u, kDocSmallTiles);
+    const uint32_t sw = ld_relaxed(state);
+    const uint32_t parity = sw & 1u;
+    const uint32_t prev_n = min((sw >> 1) & 1023u, kDocSmallTiles);
     uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
     wave_flags(wd, a.S, a.mask, a.vec_mask, wave_base, fm, off, prv, &cnt, &last1);
-    uint32_t first = 0;
-    bool seen = false;
-    int32_t imax = 0;
-#pragma unroll
-    for (int j = 0; j < kIters; ++j) {
-        const uint32_t f = fm[j];
-        const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
-        const uint64_t any = __ballot(f != 0u);
-        if (!seen && any) {
-            const int l = __builtin_ctzll(any);
-            const uint32_t mine = f ? pos0 + (uint32_t)__builtin_ctz(f) : 0u;
-            first = (uint32_t)read_lane((int)mine, l);
-            seen = true;
-        }
-        uint32_t p = prv[j];
-#pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            if ((f >> k) & 1u) {
-                const uint32_t pos = pos0 + (uint32_t)k;
-                if (p) imax = max(imax, (int32_t)(pos + 1u - p));
-                p = pos + 1u;
-            }
-        }
-    }
+    uint32_t first;
+    int32_t imax;
+    wave_first_inner(fm, prv, wave_base, &first, &imax);
     imax = wave_incl_max(imax);
     if (lane == kWave - 1) s_imax[w] = (uint32_t)imax;
     if (lane == 0) {
@@ -575,6 +634,16 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *
         st_relaxed(desc + tile * kStride, small_tag(parity) | (uint64_t)rec.cnt | (f_rel << 13) |
                                               (l_rel << 25) | ((uint64_t)rec.imax << 38));
     }
+    // the tile's totals, and its boundaries staged in LDS while the earlier
+    // tiles' records are awaited
+    uint32_t agg_c = 0, agg_l = 0, pc = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        if (v == w) pc = agg_c;
+        agg_c += s_cnt[v];
+        if (s_last[v]) agg_l = s_last[v];
+    }
+    stage_positions(s_pos, pc, wave_base, fm, off);
 
     // ---- the records of the earlier tiles: wave v waits for tiles
     // 64 v .. 64 v + 63, one per lane
@@ -630,46 +699,11 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *
         base_l = max(base_l, s_lb_l[v]);
     }
 
-    // ---- the boundaries, from the flags still in registers
-    uint32_t agg_c = 0, agg_l = 0, pc = 0, pl = 0;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        if (v == w) {
-            pc = agg_c;
-            pl = agg_l;
-        }
-        agg_c += s_cnt[v];
-        if (s_last[v]) agg_l = s_last[v];
-    }
+    // ---- the boundaries, staged before the wait; in the last tile also the
+    // segments that start at them (the last one closes the axis)
     const bool last = tile == n - 1;
-    const uint32_t bc = base_c + pc;
-    const uint32_t bl = pl ? pl : base_l;
-    int32_t lmax = 0;
     bool oob = false;
-#pragma unroll
-    for (int j = 0; j < kIters; ++j) {
-        const uint32_t f = fm[j];
-        if (f) {
-            const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
-            uint32_t o = bc + off[j];
-            uint32_t p = prv[j] ? prv[j] : bl;
-#pragma unroll
-            for (int k = 0; k < kPerLane; ++k) {
-                if ((f >> k) & 1u) {
-                    const uint32_t pos = pos0 + (uint32_t)k;
-                    if (o < a.total) {
-                        a.cu[o] = (int32_t)pos;
-                        if (a.cu2) a.cu2[o] = (int32_t)pos;
-                    } else {
-                        oob = true;
-                    }
-                    if (last && p) lmax = max(lmax, (int32_t)(pos + 1u - p));
-                    p = pos + 1u;
-                    ++o;
-                }
-            }
-        }
-    }
+    int32_t lmax = flush_positions(a, s_pos, agg_c, base_c, last, &oob);
     if (!last) return;
 
     // ---- the last tile: scalars, then the state of the next call
@@ -681,6 +715,8 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *
         const uint32_t nseg = base_c + agg_c;
         const uint32_t last_l = agg_l ? agg_l : base_l;
         int32_t mx = s_max;
+        // the segment that runs into the tile and ends at its first boundary
+        if (agg_c && base_l) mx = max(mx, (int32_t)(s_pos[0] + 1u - base_l));
         uint32_t st = s_err;
         if (nseg <= a.total) {
             a.cu[nseg] = (int32_t)a.total;
@@ -699,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *
             st_relaxed(desc + t * kStride, 0ull);
         if (lane == 0) {
             jitter(2);
-            st_relaxed(state, ((uint64_t)n << 33) | ((uint64_t)(parity ^ 1u) << 32));
+            st_relaxed(state, (n << 1) | (parity ^ 1u));
         }
     }
 }
@@ -710,13 +746,13 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint64_t *
 // launch of one-wave workgroups (1 KiB each) than as 256-thread workgroups
 // appended to the metadata grid.
 template <typename T>
-hipError_t launch_typed(DocArgs<T> a, uint64_t *small_state, const psq_copy *copies,
-                        int n_copies, hipStream_t stream) {
+hipError_t launch_typed(DocArgs<T> a, uint32_t *small_state, uint64_t *small_desc,
+                        const psq_copy *copies, int n_copies, hipStream_t stream) {
     if (a.n_chunks <= 1) {
         hipLaunchKernelGGL((k_doc_scatter<T, true>), dim3(1), dim3(kThreads), 0, stream, a);
     } else if (a.n_chunks <= kDocSmallTiles) {
         hipLaunchKernelGGL(k_doc_small<T>, dim3(a.n_chunks), dim3(kThreads), 0, stream, a,
-                           small_state);
+                           small_state, small_desc);
     } else {
         hipLaunchKernelGGL(k_doc_reduce<T>, dim3(a.n_groups), dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
@@ -758,16 +794,17 @@ hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_
     const int vec_in = ((uintptr_t)doc % 16) == 0;
     const int vec_mask = ((uintptr_t)mask % 4) == 0;
     DocRec *recs = (DocRec *)((char *)workspace + kWsDocOffset);
-    uint64_t *small_state = (uint64_t *)((char *)workspace + kWsDocSmallOffset);
+    uint32_t *small_state = (uint32_t *)((char *)workspace + kWsDocSmallOffset);
+    uint64_t *small_desc = (uint64_t *)((char *)workspace + kWsDocSmallOffset + kDocSmallLine);
     if (doc_dtype == PSQ_I32) {
         DocArgs<int32_t> a{(const int32_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in,
                            vec_mask, cu, cu2, num_segments, max_seqlen, mask, status,
                            pad_between, recs};
-        return launch_typed(a, small_state, copies, n_copies, stream);
+        return launch_typed(a, small_state, small_desc, copies, n_copies, stream);
     }
     DocArgs<int64_t> a{(const int64_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in, vec_mask,
                        cu, cu2, num_segments, max_seqlen, mask, status, pad_between, recs};
-    return launch_typed(a, small_state, copies, n_copies, stream);
+    return launch_typed(a, small_state, small_desc, copies, n_copies, stream);
 }
 
 }  // namespace psq

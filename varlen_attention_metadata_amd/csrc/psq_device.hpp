@@ -208,6 +208,14 @@ __device__ __forceinline__ int wave_shr1(int x, int first) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// The wave's index in its workgroup, as a scalar: the compiler cannot tell
+// that threadIdx.x / 64 is the same in every lane, and a branch on a value it
+// takes for per-lane is laid out as both sides run in turn under the exec
+// mask, with waits for the loads of one side placed before the other.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
 __device__ __forceinline__ int read_lane(int v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);
 }
