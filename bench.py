@@ -52,7 +52,7 @@ STAGE_KERNEL_SOURCES = ("k_segments.hip", "k_copy.hip", "psq_copy.hpp", "psq_dev
 
 # launch grids (work-items) of the stage step's kernels: 256 map tiles of 256
 # threads, and one 64-lane workgroup per KiB of the 8 GiB + 8 MiB collapse
-STAGE_GRIDS = {"psq::k_doc_small<int>": "65536",
+STAGE_GRIDS = {"psq::k_doc_small<int, 4>": "65536",
                "psq::k_copies<u32x4, true>": "537395200"}
 # the 1 GiB calibration copy: a one-token map, then 2^26 copy lanes
 CALIB_GRID = str((1 << 30) // 16)
@@ -65,7 +65,7 @@ WORKLOAD_COUNTERS = {
     "pack_sources": ("psq::k_pack_rows<896u> [grid 4263296]", ("k_pack.hip", "psq_device.hpp")),
     "trainer_rectangle": ("psq::k_pack_rows<256u> [grid 61440]", ("k_pack.hip", "psq_device.hpp")),
     "pad_tail_stream": ("psq::k_pad_ids<long> [grid 16384]", ("k_padids.hip", "psq_device.hpp")),
-    "doc_map_medium": ("psq::k_doc_small<int> [grid 2048]", ("k_segments.hip", "psq_device.hpp")),
+    "doc_map_medium": ("psq::k_doc_small<int, 1> [grid 8192]", ("k_segments.hip", "psq_device.hpp")),
 }
 
 
@@ -75,8 +75,8 @@ WORKLOAD_COUNTERS = {
 COUNTER_TABLE = [
     ("k_copies<u32x4, true> (stage_embedding, launch 2: the collapse)",
      "psq::k_copies<u32x4, true> [grid 537395200]", "stage_copy"),
-    ("k_doc_small<int> (stage_embedding, launch 1: the map)",
-     "psq::k_doc_small<int> [grid 65536]", "stage_map"),
+    ("k_doc_small<int, 4> (stage_embedding, launch 1: the map)",
+     "psq::k_doc_small<int, 4> [grid 65536]", "stage_map"),
     ("stage_embedding step (both launches)", None, "stage_embedding"),
     ("k_pack_rows<896> (pack_sources)", WORKLOAD_COUNTERS["pack_sources"][0], "pack_sources"),
     ("k_pack_rows<256> (trainer_rectangle)", WORKLOAD_COUNTERS["trainer_rectangle"][0],
@@ -85,7 +85,7 @@ COUNTER_TABLE = [
      "psq::k_thd_small<long, 0> [grid 214016]", "thd_tables"),
     ("k_pad_ids<long> (pad_tail_stream)", WORKLOAD_COUNTERS["pad_tail_stream"][0],
      "pad_tail_stream"),
-    ("k_doc_small<int> (doc_map_medium)", WORKLOAD_COUNTERS["doc_map_medium"][0],
+    ("k_doc_small<int, 1> (doc_map_medium)", WORKLOAD_COUNTERS["doc_map_medium"][0],
      "doc_map_medium"),
 ]
 
@@ -920,10 +920,11 @@ WORKLOAD_OF = {
     "k_thd_small": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses "
                    "(whole batch, and split into 4 row groups)",
     "k_thd_tables_copy": "length tables above 2048 entries, with collapses",
-    "k_doc_small": "document maps of 2..256 chunks of 4096 positions (one launch)",
-    "k_doc_scatter": "document maps of one chunk (one workgroup), or launch 2 of maps above "
-                     "256 chunks",
-    "k_doc_reduce": "launch 1 of document maps above 256 chunks",
+    "k_doc_small": "document maps of 4097 .. 1048576 positions (one launch over up to 256 "
+                   "tiles of 1024, 2048 or 4096 positions)",
+    "k_doc_scatter": "document maps of up to 4096 positions (one workgroup), or launch 2 of "
+                     "larger maps than one launch takes",
+    "k_doc_reduce": "launch 1 of document maps above 1048576 positions",
     "k_pad_ids": "pad_tail_stream: 131072 int64 ids with a pad tail",
     "k_zero_fill": "workspace zero fill (once per workspace)",
 }
@@ -935,9 +936,9 @@ GRID_LABEL = {
     ("k_pack_rows", "61440"): "trainer_rectangle: 256 rows -> 15 token-budget bins",
     ("k_doc_scatter", "256"): "doc_map_small [4,64] (and the one-token maps of the copy "
                               "calibrations and ceiling)",
-    ("k_doc_small", "2048"): "doc_map_medium [8,4096]",
-    ("k_doc_small", "65536"): "stage_embedding step, launch 1: doc map [32,32768] -> "
-                              "cu_seqlens, max_seqlen, mask",
+    ("k_doc_small", "8192"): "doc_map_medium [8,4096] (32 tiles of 1024 positions)",
+    ("k_doc_small", "65536"): "stage_embedding step, launch 1: doc map [32,32768] (256 tiles "
+                              "of 4096 positions) -> cu_seqlens, max_seqlen, mask",
     ("k_copies", "537395200"): "stage_embedding step, launch 2: bf16 [32,32768,4096] + int64 "
                                "positions collapse (8 GiB + 8 MiB)",
     ("k_copies", "67108864"): "1 GiB calibration copy (counter runs only)",
@@ -1062,7 +1063,7 @@ def main():
         "config": dict(info, **{"algorithmic_bytes_per_step": algo,
                                 "hbm_gbs_per_step": round(algo / (ms_per_step * 1e-3) / 1e9, 1)}),
         "roofline": dict(roofline(algo, k_mean, traffic),
-                         kernel="k_doc_small<int> + k_copies<u32x4,true>: one psq_process_thd "
+                         kernel="k_doc_small<int, 4> + k_copies<u32x4,true>: one psq_process_thd "
                                 "call, the metadata launch then the collapse copy (HIP events "
                                 "bracket both)",
                          kernel_ms_mean=round(k_mean, 4), kernel_ms_median=round(timer.median_ms(), 4),

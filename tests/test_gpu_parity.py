@@ -140,21 +140,40 @@ def test_doc_many_chunks_per_workgroup(dev, B, S, kind):
 
 
 def test_doc_one_launch_sequence(dev):
-    """Maps of 2..256 chunks take one launch whose workgroups publish tagged
-    records; the tags of a call must never be taken for those of a later one.
-    The sequence changes the chunk count up and down on one workspace (256,
-    then 8, then 256 again reuses tiles 8..255 with the first call's parity;
-    64, 65, 128 and 129 chunks put the last record at either side of a wave's
-    slice), with two-launch maps and a one-chunk map in between."""
+    """Maps of up to 256 chunks of 4096 positions take one launch, over the
+    smallest tiles (1024, 2048 or 4096 positions) that need at most 256 of
+    them, whose workgroups publish tagged records; the tags of a call must
+    never be taken for those of a later one.  The sequence changes the tile
+    count and size up and down on one workspace (256 tiles, then 32, then 256
+    again reuses tiles 32..255 with the first call's parity; 64, 65, 128 and
+    129 tiles put the last record at either side of a wave's slice), with
+    two-launch maps and one-chunk maps in between."""
     shapes = [(32, 32768), (8, 4096), (32, 32768), (2, 4097), (1, 64 * 4096 - 1),
               (7, 9000), (1, 65 * 4096), (129, 4096), (4, 64), (64, 4096), (3, 4096),
               (128, 4096), (1, 257 * 4096 - 3), (1, 256 * 4096), (16, 16384), (1, 8193),
-              (255, 4096), (32, 32768)]
+              (255, 4096), (16, 4096), (1, 65537), (32, 4096), (1, 131073), (1, 262145),
+              (1, 524289), (1, 2000), (32, 32768)]
     for i, (B, S) in enumerate(shapes):
         rng = np.random.default_rng(100 + i)
         d = _long_runs(rng, B, S, [3, 300, 5000][i % 3]) if B * S > 64 else \
             rng.integers(0, 3, size=(B, S)).astype(np.int32)
         check_doc(dev, d)
+
+
+@pytest.mark.parametrize("total", [1024, 1025, 2048, 2049, 4096, 4097, 65536, 65537, 131072,
+                                   131073, 262144, 262145, 524288, 524289, 1048576, 1048577])
+def test_doc_tile_size_boundaries(dev, total):
+    """Each side of every change of tile size and path: one chunk of 1024,
+    2048 or 4096 positions, one launch over tiles of 1024 (up to 256 of
+    them), 2048 or 4096 positions, then two launches.  Each total runs as
+    one row and as several rows (its smallest divisor above 1, when it has
+    one), so row starts fall inside tiles."""
+    rows = [1] + [r for r in range(2, 64) if total % r == 0][:1]
+    for B in rows:
+        S = total // B
+        rng = np.random.default_rng(total * 3 + B)
+        check_doc(dev, _long_runs(rng, B, S, 40))
+        check_doc(dev, rng.integers(0, 3, size=(B, S)).astype(np.int32))
 
 
 def test_doc_unaligned_input(dev):

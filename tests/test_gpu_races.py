@@ -8,8 +8,9 @@ orders in which workgroups reach those steps are therefore shuffled from
 call to call.  Each case runs repeatedly on the same inputs and every run
 must equal the CPU oracle exactly and leave the workspace zero-filled.
 
-The kernels covered: the one-launch document map of 2..256 chunks (tagged
-records, waits on the earlier tiles, the last tile's reset of the state),
+The kernels covered: the one-launch document map of up to 256 tiles of
+1024, 2048 or 4096 positions (tagged records, waits on the earlier tiles,
+the last tile's reset of the state),
 the multi-workgroup length-table kernel with and without row groups (ticket,
 look-back over rows, completion count), the squeeze (completion word) and
 the pad-id mask (completion count).  Larger document maps take two
@@ -67,6 +68,8 @@ def _assert_zero(ws, scratch=None):
     assert int(kept.count_nonzero()) == 0, "workspace not left zero-filled"
 
 
+# tiles of 1024 positions: (8, 4096) 32, (16, 16384) 256, (7, 9000) 62, (2, 4097) 9;
+# of 2048: (3, 100003) 147; of 4096: (32, 32768) 256; (1, 257 * 4096) takes two launches
 @pytest.mark.parametrize("shape", [(8, 4096), (32, 32768), (3, 100003), (16, 16384), (7, 9000),
                                    (2, 4097), (1, 257 * 4096)])
 def test_doc_map_tiles_under_jitter(jl, dev, shape):
@@ -94,8 +97,9 @@ def test_doc_map_tiles_under_jitter(jl, dev, shape):
 
 
 def test_doc_map_one_launch_sequence_under_jitter(jl, dev):
-    """One workspace, chunk counts going up and down (256, 8, 256, 3, 129, a
-    two-launch map, 256): every call's tagged records must be told apart from
+    """One workspace, tile counts and sizes going up and down (256 of 4096
+    positions, 32 of 1024, 256 of 4096, 12 of 1024, 129 of 4096, a two-launch
+    map, 256 of 4096): every call's tagged records must be told apart from
     the previous calls' under shuffled progress."""
     shapes = [(32, 32768), (8, 4096), (32, 32768), (3, 4096), (129, 4096), (1, 257 * 4096),
               (32, 32768)]

@@ -45,11 +45,17 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kIters = 4;
 constexpr int kPerLane = 4;
 constexpr uint32_t kSub = kWave * kPerLane;            // 256 positions
-constexpr uint32_t kWaveSpan = kSub * kIters;          // 1024 positions
-constexpr uint32_t kChunk = kWaveSpan * kWaves;        // 4096 positions
+// A wave visits kIt sub-chunks of 256 positions, so a chunk holds
+// 1024 kIt positions.  The two-launch path takes kIt = 4 (4096 positions);
+// one-launch maps take the smallest kIt of 1, 2, 4 that needs at most 256
+// chunks, and one-chunk maps the smallest that holds the map: less work per
+// wave before its record is out, and more workgroups.
+constexpr int kIters = 4;
+template <int kIt> constexpr uint32_t wave_span() { return kSub * (uint32_t)kIt; }
+template <int kIt> constexpr uint32_t chunk_of() { return wave_span<kIt>() * kWaves; }
+constexpr uint32_t kChunk = chunk_of<kIters>();        // 4096 positions
 
 // One workgroup's range: boundary count, first boundary, one past the last
 // boundary (0 = none), and the longest segment between two boundaries of the
@@ -114,7 +120,7 @@ template <typename T>
 struct DocArgs {
     const T *doc;
     uint32_t S, total;
-    uint32_t n_chunks, cpw, n_groups;   // chunks of kChunk, chunks per group, groups
+    uint32_t n_chunks, cpw, n_groups;   // chunks (of the launch's size), chunks per group, groups
     int vec_in, vec_mask;
     int32_t *cu, *cu2, *num_segments, *max_seqlen;
     uint8_t *mask;
@@ -124,10 +130,10 @@ struct DocArgs {
 
 // The map values of the 1024 positions a wave owns from wave_base
 // (positions at or past `total` are absent), and the value before them.
-template <typename T>
+template <typename T, int kIt>
 struct WaveData {
-    T d[kIters][kPerLane];
-    int pres[kIters];
+    T d[kIt][kPerLane];
+    int pres[kIt];
     T left;          // the value before the span, valid when has_left
     bool has_left;
     bool full;       // every position of the span is present (uniform)
@@ -140,17 +146,17 @@ struct WaveData {
 // branch too (from position 0 when there is none, then dropped): a load
 // under a branch is waited for at the join, before the loads after it.
 // Requires total > 0.
-template <typename T>
+template <int kIt, typename T>
 __device__ __forceinline__ void wave_load(const T *__restrict__ doc, uint32_t total, int vec_in,
-                                          uint32_t wave_base, WaveData<T> &wd) {
+                                          uint32_t wave_base, WaveData<T, kIt> &wd) {
     const int lane = lane_id();
     wd.has_left = wave_base > 0 && wave_base < total;
-    wd.full = wave_base + kWaveSpan <= total;
+    wd.full = wave_base + wave_span<kIt>() <= total;
     // expected: laid out first, so no wait for the loads of the other path
     // is placed before these loads
     if (__builtin_expect(vec_in && wd.full, 1)) {
 #pragma unroll
-        for (int j = 0; j < kIters; ++j) {
+        for (int j = 0; j < kIt; ++j) {
             const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
             if constexpr (sizeof(T) == 4) {
                 const i32x4 v = *(const i32x4 *)(doc + pos0);
@@ -164,7 +170,7 @@ __device__ __forceinline__ void wave_load(const T *__restrict__ doc, uint32_t to
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < kIters; ++j) {
+        for (int j = 0; j < kIt; ++j) {
             const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
             wd.pres[j] = load4(doc, pos0, total, vec_in != 0, wd.d[j]);
         }
@@ -183,11 +189,11 @@ __device__ __forceinline__ void wave_load(const T *__restrict__ doc, uint32_t to
 // wave's last boundary before the lane's positions (0: none yet in this
 // wave).  *cnt and *last1 return the wave's count and one past its last
 // boundary (0: none).  With `mask`, also writes mask[t] = (doc[t] == 0).
-template <typename T>
-__device__ __forceinline__ void wave_flags(const WaveData<T> &wd, uint32_t S,
+template <int kIt, typename T>
+__device__ __forceinline__ void wave_flags(const WaveData<T, kIt> &wd, uint32_t S,
                                            uint8_t *__restrict__ mask, int vec_mask,
-                                           uint32_t wave_base, uint32_t (&fm)[kIters],
-                                           uint32_t (&off)[kIters], uint32_t (&prv)[kIters],
+                                           uint32_t wave_base, uint32_t (&fm)[kIt],
+                                           uint32_t (&off)[kIt], uint32_t (&prv)[kIt],
                                            uint32_t *cnt, uint32_t *last1) {
     const int lane = lane_id();
     T carry = wd.has_left ? wd.left : (T)0;   // first use of the loads
@@ -204,7 +210,7 @@ __device__ __forceinline__ void wave_flags(const WaveData<T> &wd, uint32_t S,
         step = kSub % S;
     }
 #pragma unroll
-    for (int j = 0; j < kIters; ++j) {
+    for (int j = 0; j < kIt; ++j) {
         const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
         const T *d = wd.d[j];
         const T left = shr1(d[kPerLane - 1], carry);
@@ -278,8 +284,9 @@ __device__ __forceinline__ void wave_flags(const WaveData<T> &wd, uint32_t S,
 // that starts at one of its own boundaries and ends at the next, before the
 // wave maximum.  Selects, not branches: a branch per position costs more
 // than the arithmetic it skips.
-__device__ __forceinline__ void wave_first_inner(const uint32_t (&fm)[kIters],
-                                                 const uint32_t (&prv)[kIters],
+template <int kIt>
+__device__ __forceinline__ void wave_first_inner(const uint32_t (&fm)[kIt],
+                                                 const uint32_t (&prv)[kIt],
                                                  uint32_t wave_base, uint32_t *first,
                                                  int32_t *inner) {
     const int lane = lane_id();
@@ -287,7 +294,7 @@ __device__ __forceinline__ void wave_first_inner(const uint32_t (&fm)[kIters],
     bool seen = false;
     int32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < kIters; ++j) {
+    for (int j = 0; j < kIt; ++j) {
         const uint32_t f = fm[j];
         const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
         const uint64_t any = __ballot(f != 0u);
@@ -313,14 +320,15 @@ __device__ __forceinline__ void wave_first_inner(const uint32_t (&fm)[kIters],
 // Stage a wave's boundary positions in LDS: the chunk's boundaries in order,
 // s_pos[i] the i-th, the wave's first at index `base` (the count of the
 // chunk's earlier waves).  Every index is below the chunk's boundary count,
-// at most kChunk.
+// at most the chunk's size.
+template <int kIt>
 __device__ __forceinline__ void stage_positions(uint32_t *s_pos, uint32_t base,
                                                 uint32_t wave_base,
-                                                const uint32_t (&fm)[kIters],
-                                                const uint32_t (&off)[kIters]) {
+                                                const uint32_t (&fm)[kIt],
+                                                const uint32_t (&off)[kIt]) {
     const int lane = lane_id();
 #pragma unroll
-    for (int j = 0; j < kIters; ++j) {
+    for (int j = 0; j < kIt; ++j) {
         const uint32_t f = fm[j];
         if (f) {
             const uint32_t pos0 = wave_base + (uint32_t)j * kSub + (uint32_t)lane * kPerLane;
@@ -371,8 +379,8 @@ __global__ __launch_bounds__(kThreads) void k_doc_reduce(DocArgs<T> a) {
     const uint32_t c1 = min(c0 + a.cpw, a.n_chunks);
     DocRec rec{0u, 0u, 0u, 0u};                 // accumulated by thread 0
     for (uint32_t c = c0; c < c1; ++c) {
-        const uint32_t wave_base = c * kChunk + (uint32_t)w * kWaveSpan;
-        WaveData<T> wd;
+        const uint32_t wave_base = c * kChunk + (uint32_t)w * wave_span<kIters>();
+        WaveData<T, kIters> wd;
         wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
         uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
         wave_flags(wd, a.S, a.mask, a.vec_mask, wave_base, fm, off, prv, &cnt, &last1);
@@ -457,10 +465,12 @@ __device__ __forceinline__ void wave_records(const DocRec *__restrict__ recs, ui
 // ---------------------------------------------------------------------------
 // Launch 2 (or the only launch of a one-chunk map, kSolo): the boundaries.
 // ---------------------------------------------------------------------------
-template <typename T, bool kSolo>
+template <typename T, bool kSolo, int kIt>
 __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
+    static_assert(kSolo || kIt == kIters, "launch 2 takes the chunks of launch 1");
+    constexpr uint32_t kCh = chunk_of<kIt>();
     __shared__ uint32_t s_wcnt[kWaves], s_wlast[kWaves];
-    __shared__ uint32_t s_pos[kChunk];          // the chunk's boundaries, in order
+    __shared__ uint32_t s_pos[kCh];             // the chunk's boundaries, in order
     __shared__ int32_t s_max;
     const int w = wave_id();
     const int lane = lane_id();
@@ -472,17 +482,17 @@ __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
 
     // the first chunk's map loads go out before the records are read, so the
     // two round trips overlap
-    WaveData<T> wd;
-    if (c0 < c1) wave_load(a.doc, a.total, a.vec_in, c0 * kChunk + (uint32_t)w * kWaveSpan, wd);
+    WaveData<T, kIt> wd;
+    if (c0 < c1) wave_load(a.doc, a.total, a.vec_in, c0 * kCh + (uint32_t)w * wave_span<kIt>(), wd);
     uint32_t base_c = 0, base_l = 0, rec_max = 0;
     if constexpr (!kSolo) wave_records(a.recs, g, a.n_groups, last, &base_c, &base_l, &rec_max);
 
     int32_t lmax = 0;
     bool oob = false;
     for (uint32_t c = c0; c < c1; ++c) {
-        const uint32_t wave_base = c * kChunk + (uint32_t)w * kWaveSpan;
+        const uint32_t wave_base = c * kCh + (uint32_t)w * wave_span<kIt>();
         if (c != c0) wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
-        uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
+        uint32_t fm[kIt], off[kIt], prv[kIt], cnt, last1;
         wave_flags(wd, a.S, kSolo ? a.mask : nullptr, a.vec_mask, wave_base, fm, off, prv, &cnt,
                    &last1);
         if (lane == 0) {
@@ -572,20 +582,21 @@ __device__ __forceinline__ bool small_published(uint64_t word, uint32_t parity) 
     return (word >> 62) == (2ull | parity);
 }
 
-template <typename T>
+template <typename T, int kIt>
 __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *state,
                                                        uint64_t *desc) {
+    constexpr uint32_t kCh = chunk_of<kIt>();
     __shared__ uint32_t s_cnt[kWaves], s_first[kWaves], s_last[kWaves], s_imax[kWaves];
     __shared__ uint32_t s_lb_c[kWaves], s_lb_l[kWaves], s_err;
     __shared__ int32_t s_max;                   // the last tile's longest segment
-    __shared__ uint32_t s_pos[kChunk];          // the tile's boundaries, in order
+    __shared__ uint32_t s_pos[kCh];             // the tile's boundaries, in order
     constexpr uint32_t kStride = kDocSmallLine / 8;     // words per record line
     const int w = wave_id();
     const int lane = lane_id();
     const uint32_t n = a.n_chunks;
     const uint32_t tile = blockIdx.x;
-    const uint32_t tile_base = tile * kChunk;
-    const uint32_t wave_base = tile_base + (uint32_t)w * kWaveSpan;
+    const uint32_t tile_base = tile * kCh;
+    const uint32_t wave_base = tile_base + (uint32_t)w * wave_span<kIt>();
     jitter(1);
     if (threadIdx.x == 0) {
         s_err = 0;
@@ -594,12 +605,12 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *
 
     // ---- the tile's flags, mask and record (as launch 1); every wave reads
     // the state word while its map loads are in flight
-    WaveData<T> wd;
+    WaveData<T, kIt> wd;
     wave_load(a.doc, a.total, a.vec_in, wave_base, wd);
     const uint32_t sw = ld_relaxed(state);
     const uint32_t parity = sw & 1u;
     const uint32_t prev_n = min((sw >> 1) & 1023u, kDocSmallTiles);
-    uint32_t fm[kIters], off[kIters], prv[kIters], cnt, last1;
+    uint32_t fm[kIt], off[kIt], prv[kIt], cnt, last1;
     wave_flags(wd, a.S, a.mask, a.vec_mask, wave_base, fm, off, prv, &cnt, &last1);
     uint32_t first;
     int32_t imax;
@@ -666,9 +677,9 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *
             }
         }
         const uint32_t c = (uint32_t)d & 0x1fffu;
-        const uint32_t f_abs = rt * kChunk + ((uint32_t)(d >> 13) & 0xfffu);
+        const uint32_t f_abs = rt * kCh + ((uint32_t)(d >> 13) & 0xfffu);
         const uint32_t l_rel = (uint32_t)(d >> 25) & 0x1fffu;
-        const uint32_t l_abs = l_rel ? rt * kChunk + l_rel : 0u;
+        const uint32_t l_abs = l_rel ? rt * kCh + l_rel : 0u;
         const uint32_t im = (uint32_t)(d >> 38) & 0x1fffu;
         const uint32_t incl = (uint32_t)wave_incl_max((int)l_abs);
         const uint32_t csum = (uint32_t)read_lane(wave_incl_sum((int)c), kWave - 1);
@@ -745,33 +756,84 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *
 // collapse of the stage-embedding workload streamed 3 % faster in its own
 // launch of one-wave workgroups (1 KiB each) than as 256-thread workgroups
 // appended to the metadata grid.
-template <typename T>
-hipError_t launch_typed(DocArgs<T> a, uint32_t *small_state, uint64_t *small_desc,
-                        const psq_copy *copies, int n_copies, hipStream_t stream) {
-    if (a.n_chunks <= 1) {
-        hipLaunchKernelGGL((k_doc_scatter<T, true>), dim3(1), dim3(kThreads), 0, stream, a);
-    } else if (a.n_chunks <= kDocSmallTiles) {
-        hipLaunchKernelGGL(k_doc_small<T>, dim3(a.n_chunks), dim3(kThreads), 0, stream, a,
-                           small_state, small_desc);
-    } else {
-        hipLaunchKernelGGL(k_doc_reduce<T>, dim3(a.n_groups), dim3(kThreads), 0, stream, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((k_doc_scatter<T, false>), dim3(a.n_groups), dim3(kThreads), 0,
-                           stream, a);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n_copies == 0) return e;
-    return launch_copies(copies, n_copies, stream);
+template <typename T, int kIt>
+void launch_solo_or_small(const DocArgs<T> &a, bool solo, uint32_t *small_state,
+                          uint64_t *small_desc, hipStream_t stream) {
+    if (solo)
+        hipLaunchKernelGGL((k_doc_scatter<T, true, kIt>), dim3(1), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_doc_small<T, kIt>), dim3(a.n_chunks), dim3(kThreads), 0, stream,
+                           a, small_state, small_desc);
 }
 
-// Chunks, chunks per group and groups of a map of `total` positions.
+// How a map is cut.  Maps of at most 256 chunks of 4096 positions take one
+// launch: a one-chunk map one workgroup, and others k_doc_small; both take
+// the smallest chunk of 1024 kit positions (kit 1, 2 or 4) that keeps the
+// map in one chunk or in at most 256.  Larger maps take the two launches
+// over chunks of 4096 positions (kit 4).
+struct DocPlan {
+    bool solo, small;
+    int kit;
+    uint32_t n_chunks, cpw, n_groups;
+};
+
+// Chunks, chunks per group and groups of the two-launch path.
 void doc_grid(uint32_t total, uint32_t *n_chunks, uint32_t *cpw, uint32_t *n_groups) {
     const uint32_t nc = (uint32_t)(((uint64_t)total + kChunk - 1) / kChunk);
     const uint32_t per = nc > kDocMaxGroups ? (nc + kDocMaxGroups - 1) / kDocMaxGroups : 1u;
     *n_chunks = nc;
     *cpw = per;
     *n_groups = nc <= 1 ? 1u : (nc + per - 1) / per;
+}
+
+DocPlan doc_plan(uint32_t total) {
+    DocPlan p{};
+    doc_grid(total, &p.n_chunks, &p.cpw, &p.n_groups);
+    p.kit = kIters;
+    if (p.n_chunks > kDocSmallTiles) return p;
+    p.solo = p.n_chunks <= 1;
+    p.small = !p.solo;
+    const uint32_t limit = p.solo ? 1u : kDocSmallTiles;
+    for (int k = 1; k <= kIters; k *= 2) {
+        const uint64_t ch = (uint64_t)kSub * kWaves * (uint64_t)k;
+        const uint64_t tiles = ((uint64_t)total + ch - 1) / ch;
+        if (tiles <= limit) {
+            p.kit = k;
+            p.n_chunks = (uint32_t)tiles;
+            break;
+        }
+    }
+    p.cpw = 1;
+    p.n_groups = 1;
+    return p;
+}
+
+// The metadata launches, then the collapse copies in one-wave workgroups.
+// The copies are not fused into the metadata grid: on MI355X the 8 GiB
+// collapse of the stage-embedding workload streamed 3 % faster in its own
+// launch of one-wave workgroups (1 KiB each) than as 256-thread workgroups
+// appended to the metadata grid.
+template <typename T>
+hipError_t launch_typed(DocArgs<T> a, const DocPlan &p, uint32_t *small_state,
+                        uint64_t *small_desc, const psq_copy *copies, int n_copies,
+                        hipStream_t stream) {
+    if (p.solo || p.small) {
+        if (p.kit == 1)
+            launch_solo_or_small<T, 1>(a, p.solo, small_state, small_desc, stream);
+        else if (p.kit == 2)
+            launch_solo_or_small<T, 2>(a, p.solo, small_state, small_desc, stream);
+        else
+            launch_solo_or_small<T, 4>(a, p.solo, small_state, small_desc, stream);
+    } else {
+        hipLaunchKernelGGL(k_doc_reduce<T>, dim3(a.n_groups), dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_doc_scatter<T, false, kIters>), dim3(a.n_groups), dim3(kThreads),
+                           0, stream, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_copies == 0) return e;
+    return launch_copies(copies, n_copies, stream);
 }
 
 }  // namespace
@@ -789,22 +851,22 @@ hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_
                                int32_t *pad_between, void *workspace, const psq_copy *copies,
                                int n_copies, hipStream_t stream) {
     const uint32_t total = (uint32_t)(B * S);
-    uint32_t nc, cpw, ng;
-    doc_grid(total, &nc, &cpw, &ng);
+    const DocPlan p = doc_plan(total);
     const int vec_in = ((uintptr_t)doc % 16) == 0;
     const int vec_mask = ((uintptr_t)mask % 4) == 0;
     DocRec *recs = (DocRec *)((char *)workspace + kWsDocOffset);
     uint32_t *small_state = (uint32_t *)((char *)workspace + kWsDocSmallOffset);
     uint64_t *small_desc = (uint64_t *)((char *)workspace + kWsDocSmallOffset + kDocSmallLine);
     if (doc_dtype == PSQ_I32) {
-        DocArgs<int32_t> a{(const int32_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in,
-                           vec_mask, cu, cu2, num_segments, max_seqlen, mask, status,
-                           pad_between, recs};
-        return launch_typed(a, small_state, small_desc, copies, n_copies, stream);
+        DocArgs<int32_t> a{(const int32_t *)doc, (uint32_t)S, total, p.n_chunks, p.cpw,
+                           p.n_groups, vec_in, vec_mask, cu, cu2, num_segments, max_seqlen,
+                           mask, status, pad_between, recs};
+        return launch_typed(a, p, small_state, small_desc, copies, n_copies, stream);
     }
-    DocArgs<int64_t> a{(const int64_t *)doc, (uint32_t)S, total, nc, cpw, ng, vec_in, vec_mask,
-                       cu, cu2, num_segments, max_seqlen, mask, status, pad_between, recs};
-    return launch_typed(a, small_state, small_desc, copies, n_copies, stream);
+    DocArgs<int64_t> a{(const int64_t *)doc, (uint32_t)S, total, p.n_chunks, p.cpw, p.n_groups,
+                       vec_in, vec_mask, cu, cu2, num_segments, max_seqlen, mask, status,
+                       pad_between, recs};
+    return launch_typed(a, p, small_state, small_desc, copies, n_copies, stream);
 }
 
 }  // namespace psq
