@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 5))
     const int64_t p = blockIdx.x / n_chunks;
     const uint32_t c = blockIdx.x % n_chunks;
     const bool leader = (c == 0);
-    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int w = wave_id(), lane = lane_id();
     const uint32_t sat = (uint32_t)C + 1u;
     const uint32_t lo = c * kSlots;
     const uint32_t hi = min((uint32_t)C, lo + kSlots);

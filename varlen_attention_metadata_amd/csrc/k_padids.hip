@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void k_pad_ids(const TI *__restrict__ ids
         }
     }
 
-    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int w = wave_id(), lane = lane_id();
     fp = wave_incl_max(fp);
     ln = wave_incl_max(ln);
     if (lane == kWave - 1) {

@@ -74,7 +74,7 @@ struct RowLds {
 template <int kW = kWaves>
 __device__ __forceinline__ void block_scan3(uint32_t (&wsum)[3][kW], uint32_t v0, uint32_t v1,
                                             uint32_t v2, uint32_t (&ex)[3], uint32_t (&tot)[3]) {
-    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int w = wave_id(), lane = lane_id();
     const uint32_t in[3] = {v0, v1, v2};
     uint32_t inc[3];
 #pragma unroll
@@ -205,7 +205,7 @@ static_assert(kSlots % (kThreads * 8) == 0, "owner map is zeroed 16 bytes per th
 
 __device__ __forceinline__ void fill_owner_map(RowLds &s, uint16_t *s_own, uint32_t &s_before,
                                                uint32_t nb, uint32_t lo, uint32_t hi) {
-    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int w = wave_id(), lane = lane_id();
     for (uint32_t e = threadIdx.x * 8u; e < kSlots; e += kThreads * 8u)
         *(u32x4 *)(s_own + e) = u32x4{0u, 0u, 0u, 0u};
     if (threadIdx.x == 0) s_before = 0;
@@ -611,7 +611,7 @@ __device__ __forceinline__ void thd_small_meta(const ThdArgs<TL> &args, SmallMet
     const TL *__restrict__ Lq = args.Lp ? args.Lp : args.L;
     int32_t *__restrict__ cu = args.cu;
     int32_t *__restrict__ cp = args.cp;
-    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int w = wave_id(), lane = lane_id();
 
     for (uint32_t g = threadIdx.x; g < G; g += kSmallThreads) {
         m.g_last[g] = 0;
@@ -916,7 +916,7 @@ __device__ __forceinline__ void thd_rows_meta(const ThdArgs<TL> &args, RowsMeta 
     const bool has_lp = args.Lp != nullptr;
     int32_t *__restrict__ cu = args.cu;
     int32_t *__restrict__ cp = args.cp;
-    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x / (uint32_t)kWave);
+    const uint32_t w = (uint32_t)wave_id();
     const uint32_t j = (uint32_t)lane_id();
 
     if (threadIdx.x < kSmallGroups) {
@@ -1086,7 +1086,7 @@ __device__ __forceinline__ void thd_small_mask(const ThdArgs<TL> &args, uint32_t
                                                uint32_t n_mchunks) {
     const uint32_t P = args.P, S = args.S;
     const uint32_t r = wg / n_mchunks, c = wg % n_mchunks;
-    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int w = wave_id(), lane = lane_id();
     constexpr uint32_t kWaveSlots = kSmallSlots / kSmallWaves;
     const uint32_t lo = c * kSmallSlots + (uint32_t)w * kWaveSlots;
     const uint32_t hi = min(S, lo + kWaveSlots);
