@@ -1,4 +1,4 @@
-// k_segments.hip -- document map -> segment boundaries: reduce, then scatter.
+// k_segments.hip -- document map -> segment boundaries, max_seqlen and mask.
 //
 // NeMo AutoModel API, nemo_automodel.components.datasets.packed_seq:
 // packed_seq_params_from_doc_ids.  A segment is a maximal run of one
@@ -9,34 +9,40 @@
 // cu_seqlens); max_seqlen is the longest segment, padding runs included
 // (PackedSeqParams.max_seqlen).  The padding mask marks doc == 0.
 //
-// Layout of the work: a chunk of 4096 positions per pass of a 256-thread
-// workgroup; each wave owns 1024 consecutive positions of the chunk, visited
-// as 4 sub-chunks of 256 with 4 consecutive positions per lane (one 16-byte
-// load for int32 maps).  Each lane folds its 4 boundary flags into a bit
-// mask; DPP wave scans turn the popcounts into output slots, and a max scan
-// of "last boundary + 1" gives every boundary the start of the segment
-// before it.  A chunk's boundaries are staged in LDS in output order and
-// then written as consecutive 4-byte stores, a wave's 64 slots per store:
-// stored straight from the flags, most lanes would idle in each of up to 16
-// scattered stores per lane.
+// Layout of the work: a chunk of 1024 k positions (k = 1, 2 or 4) per pass
+// of a 256-thread workgroup; each wave owns 256 k consecutive positions of
+// the chunk, visited as k sub-chunks of 256 with 4 consecutive positions per
+// lane (one 16-byte load for int32 maps).  Each lane folds its 4 boundary
+// flags into a bit mask; DPP wave scans turn the popcounts into output
+// slots, and a max scan of "last boundary + 1" gives every boundary the
+// start of the segment before it.  A chunk's boundaries are staged in LDS in
+// output order and then written as consecutive 4-byte stores, a wave's 64
+// slots per store: stored straight from the flags, most lanes would idle in
+// each of up to 16 scattered stores per lane.
 //
-// Two launches with no cross-workgroup protocol.  Workgroup g owns `cpw`
-// consecutive chunks (one each, unless the map holds more than 1024 chunks).
-//  1. k_doc_reduce: each workgroup reduces its range to a 16-byte record --
-//     boundary count, first boundary, last boundary + 1, and the longest
-//     segment between two of its own boundaries -- and writes the mask.
-//  2. k_doc_scatter: each workgroup sums the counts of the records before
-//     its own (its first output slot) and takes the latest boundary among
-//     them, then reads its range again (just read by launch 1, so mostly
-//     cached) and writes its boundaries.  The last workgroup closes the axis
-//     and derives max_seqlen from all records: their interior maxima, the
-//     segments that run from one record's last boundary to the next
-//     record's first, and the closing segment.
-// No workgroup waits for another and nothing is counted: the kernel
-// boundary orders launch 1's record stores before launch 2's loads, and the
-// records need no clearing (every call writes before it reads), which also
-// makes the call safe to replay from a HIP graph.  A map of at most one
-// chunk is one workgroup in one launch and uses no records.
+// Three paths, by the map's size (doc_plan):
+//  - at most 4096 positions: one workgroup does everything (k_doc_scatter
+//    with kSolo), over the smallest chunk that holds the map;
+//  - up to 256 chunks of 4096 positions: one launch of one workgroup per
+//    chunk that exchange records through memory (k_doc_small, below), over
+//    the smallest chunk that needs at most 256 of them;
+//  - larger maps: two launches over chunks of 4096 positions, with no
+//    cross-workgroup protocol.  Workgroup g owns `cpw` consecutive chunks
+//    (one each, unless the map holds more than 1024 chunks).
+//     1. k_doc_reduce: each workgroup reduces its range to a 16-byte record
+//        -- boundary count, first boundary, last boundary + 1, and the
+//        longest segment between two of its own boundaries -- and writes
+//        the mask.
+//     2. k_doc_scatter: each workgroup sums the counts of the records
+//        before its own (its first output slot) and takes the latest
+//        boundary among them, then reads its range again (just read by
+//        launch 1, so mostly cached) and writes its boundaries.  The last
+//        workgroup closes the axis and derives max_seqlen from all records:
+//        their interior maxima, the segments that run from one record's
+//        last boundary to the next record's first, and the closing segment.
+//     No workgroup waits for another and nothing is counted: the kernel
+//     boundary orders launch 1's record stores before launch 2's loads, and
+//     the records need no clearing (every call writes before it reads).
 #include "psq_device.hpp"
 #include "psq_internal.hpp"
 
@@ -128,7 +134,7 @@ struct DocArgs {
     DocRec *recs;                       // n_groups records (multi-group maps)
 };
 
-// The map values of the 1024 positions a wave owns from wave_base
+// The map values of the 256 kIt positions a wave owns from wave_base
 // (positions at or past `total` are absent), and the value before them.
 template <typename T, int kIt>
 struct WaveData {
