@@ -318,7 +318,10 @@ def test_padids_hand_cases(dev, ids, pad, dtype):
     check_padids(dev, np.array(ids, dtype=np.int64), pad, dtype)
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 4095, 4096, 4097, 8191, 8193, 65537, 131072, 1048579])
+# 4194305 int64 ids need 2049 tiles and 9000001 int32 ids 2198: more than the
+# 2048 workgroups of a launch, so workgroups take several tiles
+@pytest.mark.parametrize("T", [1, 2, 3, 4095, 4096, 4097, 8191, 8193, 65537, 131072, 1048579,
+                               4194305, 9000001])
 @pytest.mark.parametrize("kind", ["tail", "collide_early", "collide_late", "none", "all"])
 @pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
 def test_padids_fuzz(dev, T, kind, dtype):

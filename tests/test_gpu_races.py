@@ -13,7 +13,7 @@ The kernels covered: the one-launch document map of up to 256 tiles of
 the last tile's reset of the state),
 the multi-workgroup length-table kernel with and without row groups (ticket,
 look-back over rows, completion count), the squeeze (completion word) and
-the pad-id mask (completion count).  Larger document maps take two
+the pad-id mask (tagged words, read and zeroed by the last workgroup).  Larger document maps take two
 launches with no cross-workgroup step (the second reads the first one's
 records); they run here too, as a repeat check.  The single-workgroup table
 kernel has no cross-workgroup step.
@@ -214,19 +214,19 @@ def test_pack_under_jitter(jl, dev):
         _assert_zero(ws)
 
 
+@pytest.mark.parametrize("T", [1 << 20, 5_000_000])
 @pytest.mark.parametrize("kind", ["tail", "collide"])
-def test_pad_ids_under_jitter(jl, dev, kind):
-    w = synth.pad_tail_stream(7, T=1 << 20)
+def test_pad_ids_under_jitter(jl, dev, kind, T):
+    w = synth.pad_tail_stream(7, T=T)
     ids = w["input_ids"].copy()
     pad = w["pad_id"]
     if kind == "collide":
         ids[1000] = pad
     ref = oracle.pad_mask_from_ids(ids, pad)
     t = torch.from_numpy(ids).to(dev)
-    T = ids.size
     ws = _workspace(dev, jl.psq_padding_mask_from_token_ids_workspace(T))
     for rep in range(REPEATS):
-        say(f"jitter pad ids {kind} run {rep}")
+        say(f"jitter pad ids {kind} T={T} run {rep}")
         mask = torch.full((T,), 7, dtype=torch.uint8, device=dev)
         scal = torch.full((2,), -7, dtype=torch.int32, device=dev)
         sp = scal.data_ptr()
