@@ -910,6 +910,7 @@ __device__ __forceinline__ void thd_rows_meta(const ThdArgs<TL> &args, RowsMeta 
     const uint32_t B = args.B, P = args.P, S = args.S, G = args.G, Bc = args.Bc;
     const uint32_t Tc = Bc * S;     // tokens of one group (< 2^31)
     const uint32_t sat = S + 1u;    // clamp of a length, and of a row's padded sum
+    const bool small_s = S < (1u << 25);
     const int64_t pv = args.pad_value;
     const TL *__restrict__ L = args.L;
     const TL *__restrict__ Lq = args.Lp ? args.Lp : args.L;
@@ -918,6 +919,8 @@ __device__ __forceinline__ void thd_rows_meta(const ThdArgs<TL> &args, RowsMeta 
     int32_t *__restrict__ cp = args.cp;
     const uint32_t w = (uint32_t)wave_id();
     const uint32_t j = (uint32_t)lane_id();
+    // a row's group (uniform; no division when there is one group)
+    auto group_of = [G, Bc](uint32_t r) -> uint32_t { return G == 1 ? 0u : r / Bc; };
 
     if (threadIdx.x < kSmallGroups) {
         m.g_flag[threadIdx.x] = 0;
@@ -962,17 +965,30 @@ __device__ __forceinline__ void thd_rows_meta(const ThdArgs<TL> &args, RowsMeta 
         exc[i] = exr[i] = exq[i] = 0;
         if (r < B) {   // uniform
             const uint64_t vm = __ballot(valid);
-            const uint32_t sum = (uint32_t)read_lane((int)wave_incl_sat(p_c, sat), kWave - 1);
-            const int32_t mx = read_lane(wave_incl_max((int)r_c), kWave - 1);
             const uint32_t last_j = vm ? 63u - (uint32_t)__clzll(vm) : 0u;
             const bool is_last = vm != 0 && j == last_j;
-            if (is_last) p_c += S - sum;   // the fold (its value matters only if sum <= S)
-            const uint32_t ir = wave_incl_add(r_c);
-            const uint32_t ip = wave_incl_add(p_c);
+            uint32_t sum, ir, ip;
+            const int32_t mx = read_lane(wave_incl_max((int)r_c), kWave - 1);
+            if (small_s) {   // uniform
+                // 64 clamped lengths of at most S + 1 < 2^25 + 1 sum without
+                // wrapping: plain scans, and the folded padded scan is the
+                // unfolded one plus the fold from the row's last entry on
+                const uint32_t ipre = wave_incl_add(p_c);
+                sum = (uint32_t)read_lane((int)ipre, kWave - 1);
+                const uint32_t fold = S - sum;   // matters only if sum <= S
+                if (is_last) p_c += fold;
+                ir = wave_incl_add(r_c);
+                ip = ipre + ((vm != 0 && j >= last_j) ? fold : 0u);
+            } else {
+                sum = (uint32_t)read_lane((int)wave_incl_sat(p_c, sat), kWave - 1);
+                if (is_last) p_c += S - sum;   // the fold (its value matters only if sum <= S)
+                ir = wave_incl_add(r_c);
+                ip = wave_incl_add(p_c);
+            }
             exc[i] = (uint32_t)__popcll(vm & ((1ull << j) - 1ull));
             exr[i] = ir - r_c;
             exq[i] = ip - p_c;
-            const uint32_t g = r / Bc;
+            const uint32_t g = group_of(r);
             const bool group_last_row = r + 1u == (g + 1u) * Bc;
             // every sequence but its group's last must be tight
             const bool loose = valid && r_c != p_c && !(group_last_row && is_last);
@@ -1008,12 +1024,17 @@ __device__ __forceinline__ void thd_rows_meta(const ThdArgs<TL> &args, RowsMeta 
     // longest group's boundary count, n + 1: lane g holds group g's.  The
     // shuffles run on every lane (a source lane outside the exec mask would
     // read as 0); lanes past the groups read lane 0 and are discarded.
-    const uint32_t g_hi = j < G ? (j + 1u) * Bc - 1u : 0u;
-    const uint32_t g_lo = (j < G && j) ? j * Bc - 1u : 0u;
-    const uint32_t c_hi = (uint32_t)__shfl((int)ic, (int)g_hi);
-    const uint32_t c_lo = (uint32_t)__shfl((int)ic, (int)g_lo);
-    const uint32_t n_lane = j < G ? c_hi - (j ? c_lo : 0u) + 1u : 0u;
-    const uint32_t width = (uint32_t)read_lane(wave_incl_max((int)n_lane), kWave - 1);
+    uint32_t width;
+    if (G == 1) {   // uniform: one group, the whole table
+        width = (uint32_t)read_lane((int)ic, (int)B - 1) + 1u;
+    } else {
+        const uint32_t g_hi = j < G ? (j + 1u) * Bc - 1u : 0u;
+        const uint32_t g_lo = (j < G && j) ? j * Bc - 1u : 0u;
+        const uint32_t c_hi = (uint32_t)__shfl((int)ic, (int)g_hi);
+        const uint32_t c_lo = (uint32_t)__shfl((int)ic, (int)g_lo);
+        const uint32_t n_lane = j < G ? c_hi - (j ? c_lo : 0u) + 1u : 0u;
+        width = (uint32_t)read_lane(wave_incl_max((int)n_lane), kWave - 1);
+    }
     const uint32_t stride = G > 1 ? width : 0u;   // output row of group g starts at g * stride
 
     // boundaries of every sequence (group-relative)
@@ -1022,7 +1043,7 @@ __device__ __forceinline__ void thd_rows_meta(const ThdArgs<TL> &args, RowsMeta 
         for (uint32_t i = 0; i < kRowsPerWave; ++i) {
             const uint32_t r = w + i * (uint32_t)kSmallWaves;
             if (r < B) {   // uniform
-                const uint32_t g = r / Bc, r0 = g * Bc;
+                const uint32_t g = group_of(r), r0 = g * Bc;
                 const uint32_t bc = pre(ic, r) - pre(ic, r0);
                 const uint32_t br = pre(ir, r) - pre(ir, r0);
                 const uint32_t bp = pre(ip, r) - pre(ip, r0);
