@@ -326,6 +326,26 @@ def test_thd_hand_cases(dev, L, Lp, S):
     check_thd(dev, np.array(L), None if Lp is None else np.array(Lp), S)
 
 
+@pytest.mark.parametrize("S", [(1 << 25) - 1, 1 << 25, (1 << 25) + 7])
+@pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
+def test_thd_rows_long_rows(dev, S, dtype):
+    """Small tables (one wave per row) with rows on either side of 2^25
+    positions: below it the row scans are plain sums, from it on they
+    saturate; both must give the oracle's outputs and status bits."""
+    rng = np.random.default_rng(S)
+    lens = rng.integers(1, 1 << 19, size=60)
+    L = np.full((3, 64), V, dtype=np.int64)
+    Lp = np.full((3, 64), V, dtype=np.int64)
+    L[0, :60] = lens
+    Lp[0, :60] = lens + rng.integers(0, 5, size=60)
+    L[1, :2], Lp[1, :2] = [S - 100, 40], [S - 100, 60]       # padded sum S - 40
+    L[2, 0], Lp[2, 0] = S, S                                 # one full row
+    check_thd(dev, L, Lp, S, dtype)
+    # a padded sum of S + 1, and a length beyond the row: ROW_OVERFLOW
+    check_thd(dev, np.array([[S, 1]]), np.array([[S, 1]]), S, dtype)
+    check_thd(dev, np.array([[S + 5, V]]), np.array([[S + 5, V]]), S, dtype)
+
+
 @pytest.mark.parametrize("L,Lp,S", [
     ([[3, V]], [[3, 2]], 8),
     ([[3, 2]], [[3, V]], 8),
