@@ -68,8 +68,9 @@ def _same(a, b):
 
 
 def _maps():
-    """Largest first: 256, 8 and 1 workgroups, then an int64 map of 74 and a
-    4.2 M-position map whose workgroups walk two chunks each."""
+    """Largest first: 256 workgroups (chunks of 4096 positions), 32 (chunks of
+    1024) and 1, then an int64 map of 147 chunks of 2048, and a 4.2 M-position
+    map whose two-launch workgroups walk two chunks each."""
     long_row = np.ones((1, 4096 * 1024 + 9), dtype=np.int32)
     long_row[0, 5000:9000] = 0
     long_row[0, 2_000_000:] = 3
@@ -98,7 +99,7 @@ def test_noalloc_calls_in_a_row_match_the_workspace_call(dev):
 
 
 def test_noalloc_second_call_smaller(dev):
-    """Exactly two calls: a map of 256 workgroups, then one of 8."""
+    """Exactly two calls: a map of 256 workgroups, then one of 32."""
     big = synth.stage_embedding()["doc_ids"]
     small = synth.doc_map_medium()
     for doc_np in (big, small):
