@@ -134,12 +134,14 @@ int psq_workspace_init(void *workspace, size_t bytes, void *stream);
  *   workspace     device scratch of psq_params_from_doc_ids_workspace(B, S)
  *                 bytes (at most 49664 for any size), 16-byte aligned,
  *                 zero-filled once like every workspace.
- * Each workgroup reduces a range of 4096-position chunks to a 16-byte
- * record (boundary count, first and last boundary, longest inner segment)
- * and starts its boundaries at the sum of the counts before it.  Maps of
- * more than 256 chunks take two launches (records, then boundaries); maps
- * of 2..256 chunks take one, each workgroup reading the earlier workgroups'
- * records as they are published; a map of one chunk is one workgroup.
+ * Each workgroup reduces a chunk (or a range of chunks) to a record
+ * (boundary count, first and last boundary, longest inner segment) and
+ * starts its boundaries at the sum of the counts before it.  A map of at
+ * most 4096 positions is one workgroup.  Maps of up to 2^20 positions take
+ * one launch over at most 256 chunks of 1024, 2048 or 4096 positions (the
+ * smallest that fits), each workgroup reading the earlier workgroups'
+ * records as they are published; larger maps take two launches over chunks
+ * of 4096 (records, then boundaries).
  * Host errors: PSQ_ERR_ARG (null pointer, B or S < 0, bad dtype),
  * PSQ_ERR_OVERFLOW (B*S >= 2^31), PSQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
