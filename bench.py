@@ -920,11 +920,11 @@ WORKLOAD_OF = {
     "k_thd_small": "thd_tables: 16 x 64 tables, S=8192, three int64 collapses "
                    "(whole batch, and split into 4 row groups)",
     "k_thd_tables_copy": "length tables above 2048 entries, with collapses",
-    "k_doc_small": "document maps of 4097 .. 1048576 positions (one launch over up to 256 "
-                   "tiles of 1024, 2048 or 4096 positions)",
+    "k_doc_small": "document maps of 4097 .. 4194304 positions (one launch over up to 256 "
+                   "tiles of 1024 to 16384 positions)",
     "k_doc_scatter": "document maps of up to 4096 positions (one workgroup), or launch 2 of "
                      "larger maps than one launch takes",
-    "k_doc_reduce": "launch 1 of document maps above 1048576 positions",
+    "k_doc_reduce": "launch 1 of document maps above 4194304 positions",
     "k_pad_ids": "pad_tail_stream: 131072 int64 ids with a pad tail",
     "k_zero_fill": "workspace zero fill (once per workspace)",
 }

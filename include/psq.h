@@ -137,8 +137,8 @@ int psq_workspace_init(void *workspace, size_t bytes, void *stream);
  * Each workgroup reduces a chunk (or a range of chunks) to a record
  * (boundary count, first and last boundary, longest inner segment) and
  * starts its boundaries at the sum of the counts before it.  A map of at
- * most 4096 positions is one workgroup.  Maps of up to 2^20 positions take
- * one launch over at most 256 chunks of 1024, 2048 or 4096 positions (the
+ * most 4096 positions is one workgroup.  Maps of up to 2^22 positions take
+ * one launch over at most 256 chunks of 1024 to 16384 positions (the
  * smallest that fits), each workgroup reading the earlier workgroups'
  * records as they are published; larger maps take two launches over chunks
  * of 4096 (records, then boundaries).

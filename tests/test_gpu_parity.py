@@ -140,10 +140,10 @@ def test_doc_many_chunks_per_workgroup(dev, B, S, kind):
 
 
 def test_doc_one_launch_sequence(dev):
-    """Maps of up to 256 chunks of 4096 positions take one launch, over the
-    smallest tiles (1024, 2048 or 4096 positions) that need at most 256 of
-    them, whose workgroups publish tagged records; the tags of a call must
-    never be taken for those of a later one.  The sequence changes the tile
+    """Maps of up to 256 chunks of 16384 positions take one launch, over the
+    smallest tiles (1024 to 16384 positions) that need at most 256 of them,
+    whose workgroups publish tagged records; the tags of a call must never
+    be taken for those of a later one.  The sequence changes the tile
     count and size up and down on one workspace (256 tiles, then 32, then 256
     again reuses tiles 32..255 with the first call's parity; 64, 65, 128 and
     129 tiles put the last record at either side of a wave's slice), with
@@ -152,7 +152,7 @@ def test_doc_one_launch_sequence(dev):
               (7, 9000), (1, 65 * 4096), (129, 4096), (4, 64), (64, 4096), (3, 4096),
               (128, 4096), (1, 257 * 4096 - 3), (1, 256 * 4096), (16, 16384), (1, 8193),
               (255, 4096), (16, 4096), (1, 65537), (32, 4096), (1, 131073), (1, 262145),
-              (1, 524289), (1, 2000), (32, 32768)]
+              (1, 524289), (1, 2000), (1, (1 << 22) + 1), (2, 1 << 20), (32, 32768)]
     for i, (B, S) in enumerate(shapes):
         rng = np.random.default_rng(100 + i)
         d = _long_runs(rng, B, S, [3, 300, 5000][i % 3]) if B * S > 64 else \
@@ -161,11 +161,12 @@ def test_doc_one_launch_sequence(dev):
 
 
 @pytest.mark.parametrize("total", [1024, 1025, 2048, 2049, 4096, 4097, 65536, 65537, 131072,
-                                   131073, 262144, 262145, 524288, 524289, 1048576, 1048577])
+                                   131073, 262144, 262145, 524288, 524289, 1048576, 1048577,
+                                   2097152, 2097153, 4194304, 4194305])
 def test_doc_tile_size_boundaries(dev, total):
     """Each side of every change of tile size and path: one chunk of 1024,
-    2048 or 4096 positions, one launch over tiles of 1024 (up to 256 of
-    them), 2048 or 4096 positions, then two launches.  Each total runs as
+    2048 or 4096 positions, one launch over up to 256 tiles of 1024, 2048,
+    4096, 8192 or 16384 positions, then two launches.  Each total runs as
     one row and as several rows (its smallest divisor above 1, when it has
     one), so row starts fall inside tiles."""
     rows = [1] + [r for r in range(2, 64) if total % r == 0][:1]

@@ -9,8 +9,8 @@ call to call.  Each case runs repeatedly on the same inputs and every run
 must equal the CPU oracle exactly and leave the workspace zero-filled.
 
 The kernels covered: the one-launch document map of up to 256 tiles of
-1024, 2048 or 4096 positions (tagged records, waits on the earlier tiles,
-the last tile's reset of the state),
+1024 to 16384 positions (tagged records, waits on the earlier tiles, the
+last tile's reset of the state),
 the multi-workgroup length-table kernel with and without row groups (ticket,
 look-back over rows, completion count), the squeeze (completion word) and
 the pad-id mask (tagged words, read and zeroed by the last workgroup).  Larger document maps take two
@@ -69,9 +69,10 @@ def _assert_zero(ws, scratch=None):
 
 
 # tiles of 1024 positions: (8, 4096) 32, (16, 16384) 256, (7, 9000) 62, (2, 4097) 9;
-# of 2048: (3, 100003) 147; of 4096: (32, 32768) 256; (1, 257 * 4096) takes two launches
+# of 2048: (3, 100003) 147; of 4096: (32, 32768) 256; of 8192: (1, 257 * 4096) 129;
+# of 16384: (16, 131072) 128; (2, 2100000) takes two launches
 @pytest.mark.parametrize("shape", [(8, 4096), (32, 32768), (3, 100003), (16, 16384), (7, 9000),
-                                   (2, 4097), (1, 257 * 4096)])
+                                   (2, 4097), (1, 257 * 4096), (16, 131072), (2, 2100000)])
 def test_doc_map_tiles_under_jitter(jl, dev, shape):
     B, S = shape
     doc_np = synth.stage_embedding(5, B, S)["doc_ids"] if S == 32768 else \
@@ -98,11 +99,11 @@ def test_doc_map_tiles_under_jitter(jl, dev, shape):
 
 def test_doc_map_one_launch_sequence_under_jitter(jl, dev):
     """One workspace, tile counts and sizes going up and down (256 of 4096
-    positions, 32 of 1024, 256 of 4096, 12 of 1024, 129 of 4096, a two-launch
-    map, 256 of 4096): every call's tagged records must be told apart from
-    the previous calls' under shuffled progress."""
+    positions, 32 of 1024, 256 of 4096, 12 of 1024, 129 of 4096, 129 of 8192,
+    a two-launch map, 256 of 4096): every call's tagged records must be told
+    apart from the previous calls' under shuffled progress."""
     shapes = [(32, 32768), (8, 4096), (32, 32768), (3, 4096), (129, 4096), (1, 257 * 4096),
-              (32, 32768)]
+              (2, 2100000), (32, 32768)]
     maps = [synth.doc_map_medium(20 + i, B, S) for i, (B, S) in enumerate(shapes)]
     refs = [oracle.doc_segments(m) for m in maps]
     ws = _workspace(dev, max(jl.psq_params_from_doc_ids_workspace(B, S) for B, S in shapes))

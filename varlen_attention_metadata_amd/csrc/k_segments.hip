@@ -9,7 +9,7 @@
 // cu_seqlens); max_seqlen is the longest segment, padding runs included
 // (PackedSeqParams.max_seqlen).  The padding mask marks doc == 0.
 //
-// Layout of the work: a chunk of 1024 k positions (k = 1, 2 or 4) per pass
+// Layout of the work: a chunk of 1024 k positions (k = 1 ... 16) per pass
 // of a 256-thread workgroup; each wave owns 256 k consecutive positions of
 // the chunk, visited as k sub-chunks of 256 with 4 consecutive positions per
 // lane (one 16-byte load for int32 maps).  Each lane folds its 4 boundary
@@ -23,9 +23,10 @@
 // Three paths, by the map's size (doc_plan):
 //  - at most 4096 positions: one workgroup does everything (k_doc_scatter
 //    with kSolo), over the smallest chunk that holds the map;
-//  - up to 256 chunks of 4096 positions: one launch of one workgroup per
+//  - up to 256 chunks of 16384 positions: one launch of one workgroup per
 //    chunk that exchange records through memory (k_doc_small, below), over
-//    the smallest chunk that needs at most 256 of them;
+//    the smallest chunk of 1024 k positions (k = 1, 2, 4, 8 or 16) that
+//    needs at most 256 of them;
 //  - larger maps: two launches over chunks of 4096 positions, with no
 //    cross-workgroup protocol.  Workgroup g owns `cpw` consecutive chunks
 //    (one each, unless the map holds more than 1024 chunks).
@@ -55,9 +56,9 @@ constexpr int kPerLane = 4;
 constexpr uint32_t kSub = kWave * kPerLane;            // 256 positions
 // A wave visits kIt sub-chunks of 256 positions, so a chunk holds
 // 1024 kIt positions.  The two-launch path takes kIt = 4 (4096 positions);
-// one-launch maps take the smallest kIt of 1, 2, 4 that needs at most 256
-// chunks, and one-chunk maps the smallest that holds the map: less work per
-// wave before its record is out, and more workgroups.
+// one-launch maps take the smallest kIt of 1, 2, 4, 8, 16 that needs at most
+// 256 chunks, and one-chunk maps the smallest of 1, 2, 4 that holds the map:
+// less work per wave before its record is out, and more workgroups.
 constexpr int kIters = 4;
 template <int kIt> constexpr uint32_t wave_span() { return kSub * (uint32_t)kIt; }
 template <int kIt> constexpr uint32_t chunk_of() { return wave_span<kIt>() * kWaves; }
@@ -565,9 +566,9 @@ __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
 // hang).
 //
 // A record is one 64-bit word: bit 63 valid, bit 62 the call's parity, then
-// the tile's boundary count (bits 0..12), first boundary (13..24) and one
-// past its last boundary (25..37), both relative to the tile, and its inner
-// maximum (38..50).  The 32-bit state word, on the line before the records,
+// the tile's boundary count (bits 0..14), first boundary (15..28) and one
+// past its last boundary (29..43), both relative to the tile, and its inner
+// maximum (44..58): tiles of up to 16384 positions.  The 32-bit state word, on the line before the records,
 // holds the parity (bit 0) and the previous call's tile count (bits 1..10);
 // every workgroup reads it while its map loads are in flight (a 32-bit word:
 // with a 64-bit one whose low half goes unused, the compiler reused that
@@ -592,6 +593,7 @@ template <typename T, int kIt>
 __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *state,
                                                        uint64_t *desc) {
     constexpr uint32_t kCh = chunk_of<kIt>();
+    static_assert(kCh <= 16384, "record fields hold tiles of up to 16384 positions");
     __shared__ uint32_t s_cnt[kWaves], s_first[kWaves], s_last[kWaves], s_imax[kWaves];
     __shared__ uint32_t s_lb_c[kWaves], s_lb_l[kWaves], s_err;
     __shared__ int32_t s_max;                   // the last tile's longest segment
@@ -643,13 +645,13 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *
             }
             rec.imax = max(rec.imax, s_imax[v]);
         }
-        // relative to the tile: count and last1 <= 4096 (13 bits), first
-        // < 4096 (12 bits), the inner maximum < 4096 (13 bits)
+        // relative to the tile: count and last1 <= 16384 (15 bits), first
+        // < 16384 (14 bits), the inner maximum < 16384 (15 bits)
         const uint64_t f_rel = rec.cnt ? rec.first - tile_base : 0u;
         const uint64_t l_rel = rec.cnt ? rec.last1 - tile_base : 0u;
         jitter(5);
-        st_relaxed(desc + tile * kStride, small_tag(parity) | (uint64_t)rec.cnt | (f_rel << 13) |
-                                              (l_rel << 25) | ((uint64_t)rec.imax << 38));
+        st_relaxed(desc + tile * kStride, small_tag(parity) | (uint64_t)rec.cnt | (f_rel << 15) |
+                                              (l_rel << 29) | ((uint64_t)rec.imax << 44));
     }
     // the tile's totals, and its boundaries staged in LDS while the earlier
     // tiles' records are awaited
@@ -682,11 +684,11 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *
                 d = ld_relaxed(desc + rt * kStride);
             }
         }
-        const uint32_t c = (uint32_t)d & 0x1fffu;
-        const uint32_t f_abs = rt * kCh + ((uint32_t)(d >> 13) & 0xfffu);
-        const uint32_t l_rel = (uint32_t)(d >> 25) & 0x1fffu;
+        const uint32_t c = (uint32_t)d & 0x7fffu;
+        const uint32_t f_abs = rt * kCh + ((uint32_t)(d >> 15) & 0x3fffu);
+        const uint32_t l_rel = (uint32_t)(d >> 29) & 0x7fffu;
         const uint32_t l_abs = l_rel ? rt * kCh + l_rel : 0u;
-        const uint32_t im = (uint32_t)(d >> 38) & 0x1fffu;
+        const uint32_t im = (uint32_t)(d >> 44) & 0x7fffu;
         const uint32_t incl = (uint32_t)wave_incl_max((int)l_abs);
         const uint32_t csum = (uint32_t)read_lane(wave_incl_sum((int)c), kWave - 1);
         const bool bad = __ballot(expired) != 0;
@@ -757,26 +759,29 @@ __global__ __launch_bounds__(kThreads) void k_doc_small(DocArgs<T> a, uint32_t *
     }
 }
 
-// The metadata launches, then the collapse copies in one-wave workgroups.
-// The copies are not fused into the metadata grid: on MI355X the 8 GiB
-// collapse of the stage-embedding workload streamed 3 % faster in its own
-// launch of one-wave workgroups (1 KiB each) than as 256-thread workgroups
-// appended to the metadata grid.
+// One workgroup for a one-chunk map, or the one-launch kernel, over chunks
+// of 1024 kIt positions.
 template <typename T, int kIt>
 void launch_solo_or_small(const DocArgs<T> &a, bool solo, uint32_t *small_state,
                           uint64_t *small_desc, hipStream_t stream) {
-    if (solo)
-        hipLaunchKernelGGL((k_doc_scatter<T, true, kIt>), dim3(1), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_doc_small<T, kIt>), dim3(a.n_chunks), dim3(kThreads), 0, stream,
-                           a, small_state, small_desc);
+    if constexpr (kIt <= kIters) {
+        if (solo) {
+            hipLaunchKernelGGL((k_doc_scatter<T, true, kIt>), dim3(1), dim3(kThreads), 0, stream,
+                               a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_doc_small<T, kIt>), dim3(a.n_chunks), dim3(kThreads), 0, stream, a,
+                       small_state, small_desc);
 }
 
-// How a map is cut.  Maps of at most 256 chunks of 4096 positions take one
-// launch: a one-chunk map one workgroup, and others k_doc_small; both take
-// the smallest chunk of 1024 kit positions (kit 1, 2 or 4) that keeps the
-// map in one chunk or in at most 256.  Larger maps take the two launches
-// over chunks of 4096 positions (kit 4).
+// How a map is cut.  A map of at most 4096 positions is one workgroup over
+// the smallest chunk of 1024, 2048 or 4096 positions that holds it.  Maps of
+// up to 256 chunks of 16384 positions take one launch of k_doc_small over
+// the smallest chunk of 1024 kit positions (kit 1, 2, 4, 8 or 16) that needs
+// at most 256 of them.  Larger maps take the two launches over chunks of
+// 4096 positions.
+constexpr int kSmallMaxIt = 16;
 struct DocPlan {
     bool solo, small;
     int kit;
@@ -796,11 +801,11 @@ DocPlan doc_plan(uint32_t total) {
     DocPlan p{};
     doc_grid(total, &p.n_chunks, &p.cpw, &p.n_groups);
     p.kit = kIters;
-    if (p.n_chunks > kDocSmallTiles) return p;
-    p.solo = p.n_chunks <= 1;
-    p.small = !p.solo;
+    p.solo = total <= kChunk;
+    p.small = !p.solo && (uint64_t)total <= (uint64_t)kDocSmallTiles * chunk_of<kSmallMaxIt>();
+    if (!p.solo && !p.small) return p;
     const uint32_t limit = p.solo ? 1u : kDocSmallTiles;
-    for (int k = 1; k <= kIters; k *= 2) {
+    for (int k = 1; k <= kSmallMaxIt; k *= 2) {
         const uint64_t ch = (uint64_t)kSub * kWaves * (uint64_t)k;
         const uint64_t tiles = ((uint64_t)total + ch - 1) / ch;
         if (tiles <= limit) {
@@ -824,12 +829,13 @@ hipError_t launch_typed(DocArgs<T> a, const DocPlan &p, uint32_t *small_state,
                         uint64_t *small_desc, const psq_copy *copies, int n_copies,
                         hipStream_t stream) {
     if (p.solo || p.small) {
-        if (p.kit == 1)
-            launch_solo_or_small<T, 1>(a, p.solo, small_state, small_desc, stream);
-        else if (p.kit == 2)
-            launch_solo_or_small<T, 2>(a, p.solo, small_state, small_desc, stream);
-        else
-            launch_solo_or_small<T, 4>(a, p.solo, small_state, small_desc, stream);
+        switch (p.kit) {
+        case 1: launch_solo_or_small<T, 1>(a, p.solo, small_state, small_desc, stream); break;
+        case 2: launch_solo_or_small<T, 2>(a, p.solo, small_state, small_desc, stream); break;
+        case 4: launch_solo_or_small<T, 4>(a, p.solo, small_state, small_desc, stream); break;
+        case 8: launch_solo_or_small<T, 8>(a, p.solo, small_state, small_desc, stream); break;
+        default: launch_solo_or_small<T, 16>(a, p.solo, small_state, small_desc, stream); break;
+        }
     } else {
         hipLaunchKernelGGL(k_doc_reduce<T>, dim3(a.n_groups), dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
@@ -845,10 +851,9 @@ hipError_t launch_typed(DocArgs<T> a, const DocPlan &p, uint32_t *small_state,
 }  // namespace
 
 size_t doc_segments_workspace(int64_t B, int64_t S) {
-    uint32_t nc, cpw, ng;
-    doc_grid((uint32_t)(B * S), &nc, &cpw, &ng);
-    if (nc >= 2 && nc <= kDocSmallTiles) return kWsDocEnd;
-    return round_up(kWsDocOffset + sizeof(DocRec) * (size_t)ng, 256);
+    const DocPlan p = doc_plan((uint32_t)(B * S));
+    if (p.small) return kWsDocEnd;
+    return round_up(kWsDocOffset + sizeof(DocRec) * (size_t)p.n_groups, 256);
 }
 
 hipError_t launch_doc_segments(const void *doc, int doc_dtype, int64_t B, int64_t S,
