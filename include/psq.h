@@ -50,6 +50,9 @@
  *    workspace can serve every call on a stream.  (The document-map calls
  *    keep records and state in bytes 256 .. 49664, which no other call
  *    reads; there they leave data that the next document-map call expects.)
+ *    A call whose *status holds PSQ_DATA_WORKSPACE may leave records behind
+ *    (a bounded wait gave up while other workgroups still ran): zero-fill
+ *    the workspace again, after the stream has drained, before reusing it.
  *    A query returns 0 for sizes its call would reject (PSQ_ERR_ARG or
  *    PSQ_ERR_OVERFLOW).
  *  - Grids: one HIP launch runs fewer than 2^32 threads.  Sizes that would
@@ -168,6 +171,10 @@ int psq_params_from_doc_ids(const void *doc_ids, int doc_dtype, int64_t B, int64
  * need would return PSQ_ERR_OVERFLOW.  Each call leaves the scratch ready
  * for the next one.  Calls that overlap in time on one GPU (several streams
  * or host threads) share the scratch and race: order them on one stream.
+ * The caller cannot zero-fill the scratch again: should a call report
+ * PSQ_DATA_WORKSPACE from a bounded wait that gave up (a dispatched
+ * workgroup made no progress for seconds), stop using this call on that GPU
+ * and use psq_params_from_doc_ids with a freshly zero-filled workspace.
  * Host errors: as psq_params_from_doc_ids (without PSQ_ERR_WORKSPACE), and
  * PSQ_ERR_HIP when the scratch's device address cannot be looked up.
  * ---------------------------------------------------------------------- */

@@ -318,6 +318,33 @@ def test_python_api_refuses_cpu_tensors():
         psq.pack_padded_rows(torch.zeros((2, 4), dtype=torch.int64), [1, 2], [[0, 1]], 4, 8)
 
 
+def test_workspace_status_drops_the_cached_workspace(monkeypatch):
+    """A status word with the workspace bit raises and discards the stream's
+    cached workspace (it may hold records left by a wait that gave up); any
+    other bit raises and keeps it."""
+    import torch
+    import varlen_attention_metadata_amd as psq
+    monkeypatch.setattr(psq, "_stream", lambda device: 77)
+    dev = torch.device("cuda", 0)
+    cache = psq._WORKSPACES
+    saved = dict(cache)
+    try:
+        cache.clear()
+        cache[(0, 77)] = "kept"
+        cache[(0, 78)] = "other stream"
+        with pytest.raises(ValueError, match="0x81"):
+            psq._raise_status(_lib.DATA_BAD_LENGTH | _lib.DATA_WORKSPACE, "call", dev)
+        assert (0, 77) not in cache and cache[(0, 78)] == "other stream"
+        cache[(0, 77)] = "kept"
+        with pytest.raises(ValueError, match="negative length"):
+            psq._raise_status(_lib.DATA_BAD_LENGTH, "call", dev)
+        assert cache[(0, 77)] == "kept"
+        psq._raise_status(0, "call", dev)
+    finally:
+        cache.clear()
+        cache.update(saved)
+
+
 def test_header_is_c_and_matches_the_binding(tmp_path):
     """``include/psq.h`` compiles as C99 and as C++, every function it declares
     links against ``libpsq.so``, and its structs and constants have the

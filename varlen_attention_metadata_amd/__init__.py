@@ -80,9 +80,16 @@ def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def _raise_status(code: int, what: str) -> None:
-    if code != 0:
-        raise ValueError(f"{what}: {_lib.status_string(code, True)} (status bits {code:#x})")
+def _raise_status(code: int, what: str, device: torch.device) -> None:
+    """Raise on a nonzero status word (read back, so the stream has drained).
+    A call that reports DATA_WORKSPACE may leave records in the workspace,
+    so the stream's cached one is dropped and the next call zero-fills a
+    fresh one."""
+    if code == 0:
+        return
+    if code & _lib.DATA_WORKSPACE:
+        _WORKSPACES.pop((device.index, _stream(device)), None)
+    raise ValueError(f"{what}: {_lib.status_string(code, True)} (status bits {code:#x})")
 
 
 def packed_seq_params_from_doc_ids(doc_ids: torch.Tensor) -> PackedSeqParams:
@@ -106,7 +113,7 @@ def packed_seq_params_from_doc_ids(doc_ids: torch.Tensor) -> PackedSeqParams:
     _lib.psq_params_from_doc_ids(doc_ids.data_ptr(), dt, B, S, cu.data_ptr(), sp, sp + 4, None,
                                  sp + 8, ws.data_ptr(), ws.numel(), _stream(dev))
     n, mx, st, _ = scal.cpu().tolist()
-    _raise_status(st, "packed_seq_params_from_doc_ids")
+    _raise_status(st, "packed_seq_params_from_doc_ids", dev)
     return PackedSeqParams(cu_seqlens=cu[: n + 1], max_seqlen=int(mx), doc_ids=doc_ids)
 
 
@@ -224,7 +231,7 @@ def process_input_for_thd(batch: dict, seq_lens_padding_value: int = -1000,
                          sp, sp + 4, sp + 8, mask.data_ptr(), arr, n_copies, sp + 12,
                          ws.data_ptr(), ws.numel(), stream)
     n, _, pad_between, st = scal.cpu().tolist()
-    _raise_status(st, "process_input_for_thd")
+    _raise_status(st, "process_input_for_thd", dev)
     out["cu_seqlens"] = cu[: n + 1]
     if cp is not None:
         out["cu_seqlens_padded"] = cp[: n + 1]
@@ -279,7 +286,7 @@ def pack_rows(src_tokens: torch.Tensor, src_offsets: torch.Tensor, real_len: tor
                        capacity, int(bool(fold)), pad_token, packed.data_ptr(), tmask.data_ptr(),
                        cu.data_ptr(), cp.data_ptr(), status.data_ptr(), ws.data_ptr(),
                        ws.numel(), _stream(dev))
-    _raise_status(int(status.item()), "pack_rows")
+    _raise_status(int(status.item()), "pack_rows", dev)
     psl = ps_host.tolist()
     used = (psl[-1] + P) if P > 0 else 0
     cu_list = [cu[psl[p] + p: psl[p + 1] + p + 1] for p in range(P)]
@@ -371,7 +378,7 @@ def split_batch_into_thd_chunks(batch: dict, num_chunks: int, seq_lens_padding_v
                        sp, pp, pp + 4 * G, pp + 8 * G, mask.data_ptr(), arr, n_copies, sp + 4,
                        ws.data_ptr(), ws.numel(), stream)
     width, st = scal.cpu().tolist()
-    _raise_status(st, "split_batch_into_thd_chunks")
+    _raise_status(st, "split_batch_into_thd_chunks", dev)
     out["cu_seqlens"] = cu[: G * width].view(G, width)
     if cp is not None:
         out["cu_seqlens_padded"] = cp[: G * width].view(G, width)
@@ -404,7 +411,7 @@ def thd_padding_mask_from_token_ids(input_ids: torch.Tensor, padding_token_id: i
     _lib.psq_padding_mask_from_token_ids(input_ids.data_ptr(), dt, T, int(padding_token_id),
                                          mask.data_ptr(), sp, sp + 4, ws.data_ptr(), ws.numel(),
                                          _stream(dev))
-    _raise_status(int(scal[1].item()), "thd_padding_mask_from_token_ids")
+    _raise_status(int(scal[1].item()), "thd_padding_mask_from_token_ids", dev)
     return mask
 
 
@@ -457,7 +464,7 @@ def pack_padded_rows(input_ids: torch.Tensor, input_lengths, bins, pad_to: int, 
                               pad_token, packed.data_ptr(), tmask.data_ptr(), cu.data_ptr(),
                               cp.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(),
                               _stream(dev))
-    _raise_status(int(status.item()), "pack_padded_rows")
+    _raise_status(int(status.item()), "pack_padded_rows", dev)
     psl = ps_host.tolist()
     used = (psl[-1] + P) if P > 0 else 0
     return {"input_ids": packed, "token_mask": tmask, "width": width,
