@@ -188,7 +188,11 @@ int psq_params_from_doc_ids_noalloc(const void *doc_ids, int doc_dtype, int64_t 
  * bytes, read at a stride of src_row_stride_bytes and written at a stride of
  * dst_row_stride_bytes (0 = row_bytes, i.e. densely).  A contiguous tensor
  * is one row (or rows with both strides == row_bytes).  Strides are at least
- * row_bytes; src and dst must not overlap. */
+ * row_bytes; src and dst must not overlap (checked over their whole spans).
+ * The copies of one call run concurrently with each other and with the
+ * call's metadata work: the bytes a copy writes must not be read or written
+ * by another copy or be any other buffer of the call (not checked; several
+ * copies may write interleaved rows of one buffer, and read one source). */
 typedef struct psq_copy {
     const void *src;
     void *dst;

@@ -17,9 +17,9 @@
 // comparing their starts in registers (on MI355X 0.4 % faster on the
 // 65536-source workload than a per-chunk owner map filled in LDS by a max
 // scan, 3 % on the trainer batch), and every slot takes either its member's
-// token or the pad token.  Lane l
-// owns slots l, l+64, l+128, ... of the chunk, so every load and store
-// instruction of the wave covers 64 consecutive slots.  Every slot issues
+// token or the pad token.  Lane l owns slots l, l+64, l+128, ... of the
+// chunk, so every load and store instruction of the wave covers 64
+// consecutive slots.  Every slot issues
 // its load (a pad slot re-reads a token of its own member, which is already
 // in flight), so the loads are straight-line code and the stores wait only
 // for the loads they need.  On MI355X this shape beat 256-thread workgroups
@@ -31,10 +31,9 @@
 // loads alone 181 us.  The stores are the compiler's non-temporal stores:
 // the collapse copy's agent-scope streaming stores (inline assembly) gained
 // only 0.4 % here (161.7 against 162.3 us), against 2 % on the copy.
-// The chunk-0 workgroup of each
-// pack also writes the pack's boundary arrays and reports data errors
-// through one relaxed 64-bit word (finished count | status bits); the last
-// of those to finish publishes *status.
+// The chunk-0 workgroup of each pack also writes the pack's boundary arrays
+// and reports data errors through one relaxed 64-bit word (finished count |
+// status bits); the last of those to finish publishes *status.
 // Every access is bounds-checked against the caller's sizes, so bad data
 // can only produce wrong values and status bits, never a stray access.
 //
@@ -60,22 +59,6 @@ constexpr int kMembers = kThreads;       // members per LDS batch
 constexpr uint32_t kBigSlots = 896;
 constexpr uint32_t kSmallSlots = 256;
 constexpr uint64_t kFillGroups = 1024;
-
-__device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat) {
-    const uint32_t s = a + b;
-    return s > sat ? sat : s;
-}
-
-// Inclusive wave scan with saturation at `sat` (<= 2^31, so no wrap).
-__device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
-    x = sat_add(x, (uint32_t)dpp0<0x111>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x112>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x114>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x118>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x142, 0xa>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x143, 0xc>((int)x), sat);
-    return x;
-}
 
 // 4 to 5 waves per SIMD: 5 measured best for this shape (6 were slower).
 template <uint32_t kSlots>

@@ -568,12 +568,13 @@ __global__ __launch_bounds__(kThreads) void k_doc_scatter(DocArgs<T> a) {
 // A record is one 64-bit word: bit 63 valid, bit 62 the call's parity, then
 // the tile's boundary count (bits 0..14), first boundary (15..28) and one
 // past its last boundary (29..43), both relative to the tile, and its inner
-// maximum (44..58): tiles of up to 16384 positions.  The 32-bit state word, on the line before the records,
-// holds the parity (bit 0) and the previous call's tile count (bits 1..10);
-// every workgroup reads it while its map loads are in flight (a 32-bit word:
-// with a 64-bit one whose low half goes unused, the compiler reused that
-// half's register and so waited for this uncached load before the flags).  Once the last tile
-// has seen every other tile's record, every workgroup has read the state: it
+// maximum (44..58): tiles of up to 16384 positions.  The 32-bit state word,
+// on the line before the records, holds the parity (bit 0) and the previous
+// call's tile count (bits 1..10); every workgroup reads it while its map
+// loads are in flight (a 32-bit word: with a 64-bit one whose low half goes
+// unused, the compiler reused that half's register and so waited for this
+// uncached load before the flags).  Once the last tile has seen every other
+// tile's record, every workgroup has read the state: it
 // clears the words of the tiles the previous call used beyond this call's
 // count and stores the next call's state (the other parity, this call's
 // count).  At the start of a call the word of every tile below its count is

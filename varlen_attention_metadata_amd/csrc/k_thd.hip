@@ -593,12 +593,6 @@ struct SmallMeta {
     uint32_t err;
 };
 
-// a + b saturated at `sat` (sat <= 2^31; a, b <= sat, so a wrap is caught)
-__device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat) {
-    const uint32_t s = a + b;
-    return (s < a || s > sat) ? sat : s;
-}
-
 template <typename TL, int kSmallPer>
 __device__ __forceinline__ void thd_small_meta(const ThdArgs<TL> &args, SmallMeta<kSmallPer> &m) {
     const uint32_t B = args.B, P = args.P, S = args.S, G = args.G, Bc = args.Bc;
@@ -889,17 +883,6 @@ __device__ __forceinline__ uint32_t wave_incl_add(uint32_t x) {
     x += (uint32_t)dpp0<0x118>((int)x);
     x += (uint32_t)dpp0<0x142, 0xa>((int)x);
     x += (uint32_t)dpp0<0x143, 0xc>((int)x);
-    return x;
-}
-
-// inclusive sum over the wave, saturated at `sat` (sat <= 2^31)
-__device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
-    x = sat_add(x, (uint32_t)dpp0<0x111>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x112>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x114>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x118>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x142, 0xa>((int)x), sat);
-    x = sat_add(x, (uint32_t)dpp0<0x143, 0xc>((int)x), sat);
     return x;
 }
 

@@ -201,6 +201,23 @@ __device__ __forceinline__ int wave_incl_max(int x) {
     return x;
 }
 
+// a + b saturated at `sat` (sat <= 2^31; a, b <= sat, so a wrap is caught)
+__device__ __forceinline__ uint32_t sat_add(uint32_t a, uint32_t b, uint32_t sat) {
+    const uint32_t s = a + b;
+    return (s < a || s > sat) ? sat : s;
+}
+
+// Inclusive wave sum, saturated at `sat` (sat <= 2^31).
+__device__ __forceinline__ uint32_t wave_incl_sat(uint32_t x, uint32_t sat) {
+    x = sat_add(x, (uint32_t)dpp0<0x111>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x112>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x114>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x118>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x142, 0xa>((int)x), sat);
+    x = sat_add(x, (uint32_t)dpp0<0x143, 0xc>((int)x), sat);
+    return x;
+}
+
 // Lane l receives lane l-1's value; lane 0 receives `first`.
 __device__ __forceinline__ int wave_shr1(int x, int first) {
     return __builtin_amdgcn_update_dpp(first, x, 0x138, 0xf, 0xf, false);
