@@ -239,3 +239,107 @@ def test_two_streams_with_own_workspaces(dev):
         assert st == 0 and n == ref["num_seqs"] and mx == ref["max_seqlen"]
         assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
         assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
+
+
+def _big_tables(seed, B, P, S):
+    rng = np.random.default_rng(seed)
+    L = np.full((B, P), V, dtype=np.int64)
+    for r in range(B):
+        m = int(rng.integers(1, P))
+        L[r, :m] = rng.integers(0, S // (2 * m) + 1, size=m)
+    return L
+
+
+def test_two_streams_protocol_kernels(dev):
+    """The kernels that exchange records through the workspace on two
+    streams at once: the one-launch document map (tile counts alternating
+    between 256 and 147, int32 and int64 maps), the pad-id mask (one grid
+    of 1465 workgroups, one of 2048 striding over 2442 tiles; clean and
+    colliding streams) and the multi-workgroup table kernel (64 x 100
+    entries).  Each stream has one workspace that all its calls share, as
+    the Python binding does; every call writes its own outputs and each is
+    compared with the oracle.  A 4 GiB fill heads each stream, so both
+    streams' calls are queued before either starts and their kernels can
+    run side by side (the streams sit on separate hardware queues)."""
+    rounds = 4
+    doc_shapes = [(16, 16384), (3, 100001)]
+    pad_T = [3000001, 5000000]
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    plans = []
+    for k in range(2):
+        dtype = torch.int32 if k == 0 else torch.int64
+        docs = [synth.doc_map_medium(40 + 2 * k + i, B, S) for i, (B, S) in enumerate(doc_shapes)]
+        pw = synth.pad_tail_stream(7 + k, T=pad_T[k])
+        ids_clean = pw["input_ids"].copy()
+        ids_coll = ids_clean.copy()
+        ids_coll[1000 + k] = pw["pad_id"]
+        L = _big_tables(50 + k, 64, 100, 4096)
+        lay_dummy = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, 1, None, _lib.I64, 100, V)
+        need = max([_lib.load().psq_params_from_doc_ids_workspace(B, S) for B, S in doc_shapes]
+                   + [_lib.load().psq_padding_mask_from_token_ids_workspace(pad_T[k]),
+                      _lib.psq_process_thd_workspace(lay_dummy, 64, 4096)])
+        plans.append(dict(
+            dtype=dtype, docs=[torch.from_numpy(d).to(dev, dtype) for d in docs],
+            doc_refs=[oracle.doc_segments(d) for d in docs],
+            ids=[torch.from_numpy(x).to(dev) for x in (ids_clean, ids_coll)],
+            pad_refs=[oracle.pad_mask_from_ids(x, pw["pad_id"]) for x in (ids_clean, ids_coll)],
+            pad_id=pw["pad_id"], tL=torch.from_numpy(L).to(dev),
+            thd_ref=oracle.thd_tables(L, None, 4096), ws=zeroed_workspace(dev, need)))
+    outs = []
+    for r in range(rounds):
+        for k in range(2):
+            B, S = doc_shapes[r % 2]
+            T = pad_T[k]
+            outs.append(dict(
+                cu=torch.full((B * S + 1,), -7, dtype=torch.int32, device=dev),
+                dmask=torch.full((B * S,), 7, dtype=torch.uint8, device=dev),
+                pmask=torch.full((T,), 7, dtype=torch.uint8, device=dev),
+                tcu=torch.full((64 * 100 + 1,), -7, dtype=torch.int32, device=dev),
+                tmask=torch.full((64 * 4096,), 7, dtype=torch.uint8, device=dev),
+                scal=torch.full((12,), -7, dtype=torch.int32, device=dev)))
+    heads = [torch.empty(1 << 32, dtype=torch.uint8, device=dev) for _ in range(2)]
+    torch.cuda.synchronize(dev)
+    say("two streams: document maps, pad-id masks and tables, one workspace per stream")
+    for k, s in enumerate(streams):
+        with torch.cuda.stream(s):
+            heads[k].fill_(k + 1)
+    for r in range(rounds):
+        for k, s in enumerate(streams):
+            p, o = plans[k], outs[2 * r + k]
+            B, S = doc_shapes[r % 2]
+            dt = _lib.I32 if p["dtype"] == torch.int32 else _lib.I64
+            ws, sp = p["ws"], o["scal"].data_ptr()
+            st = s.cuda_stream
+            assert _lib.load().psq_params_from_doc_ids(
+                p["docs"][r % 2].data_ptr(), dt, B, S, o["cu"].data_ptr(), sp, sp + 4,
+                o["dmask"].data_ptr(), sp + 8, ws.data_ptr(), ws.numel(), st) == 0
+            assert _lib.load().psq_padding_mask_from_token_ids(
+                p["ids"][r % 2].data_ptr(), _lib.I64, pad_T[k], p["pad_id"],
+                o["pmask"].data_ptr(), sp + 12, sp + 16, ws.data_ptr(), ws.numel(), st) == 0
+            lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, p["tL"].data_ptr(), None, _lib.I64,
+                                   100, V)
+            arr, _ = _lib.make_copies([])
+            _lib.psq_process_thd(lay, 64, 4096, o["tcu"].data_ptr(), None, sp + 20, sp + 24,
+                                 sp + 28, o["tmask"].data_ptr(), arr, 0, sp + 32, ws.data_ptr(),
+                                 ws.numel(), st)
+    torch.cuda.synchronize(dev)
+    for r in range(rounds):
+        for k in range(2):
+            p, o = plans[k], outs[2 * r + k]
+            say(f"two streams: check round {r} stream {k}")
+            n, mx, dst, nc, pst, tn, tmx, tpb, tst = o["scal"].cpu().tolist()[:9]
+            dref = p["doc_refs"][r % 2]
+            assert dst == 0 and n == dref["num_segments"] and mx == dref["max_seqlen"]
+            assert np.array_equal(o["cu"][: n + 1].cpu().numpy(), dref["cu_seqlens"])
+            assert np.array_equal(o["dmask"].cpu().numpy(), dref["padding_mask"])
+            pref = p["pad_refs"][r % 2]
+            assert pst == pref["status"] and nc == pref["num_content"]
+            assert np.array_equal(o["pmask"].cpu().numpy(), pref["padding_mask"])
+            tref = p["thd_ref"]
+            assert tst == 0 and tn == tref["num_seqs"] and tmx == tref["max_seqlen"]
+            assert tpb == tref["pad_between_seqs"]
+            assert np.array_equal(o["tcu"][: tn + 1].cpu().numpy(), tref["cu_seqlens"])
+            assert np.array_equal(o["tmask"].cpu().numpy(), tref["padding_mask"])
+    for p in plans:
+        w = p["ws"].cpu().numpy()
+        assert not w[:256].any() and not w[49664:].any(), "workspace left dirty"
