@@ -626,8 +626,8 @@ def test_pack_many_members_per_pack(dev):
     check_pack(dev, src, off, rl, 1, [0, 1000, N], C, True, what="many members")
 
 
-@pytest.mark.parametrize("case", ["overflow", "empty", "pack_range", "order_range",
-                                  "src_range", "neg_len", "neg_len_bad_off", "neg_len_neg_off",
+@pytest.mark.parametrize("case", ["overflow", "empty", "pack_range", "pack_range_long_order",
+                                  "order_range", "src_range", "neg_len", "neg_len_bad_off", "neg_len_neg_off",
                                   "neg_len_and_other_src_range", "neg_off"])
 def test_pack_error_bits(dev, case):
     """Each status word is compared exactly with the oracle's, also when one
@@ -644,6 +644,10 @@ def test_pack_error_bits(dev, case):
         ps = [0, 0, 3]
     elif case == "pack_range":
         ps = [0, 4]
+    elif case == "pack_range_long_order":
+        # the range passes the N member entries; the order buffer holds one
+        # more (valid) entry, which must not be taken as a member
+        ps, order = [0, 4], [0, 1, 2, 0]
     elif case == "order_range":
         ps, order = [0, 3], [0, 1, 3]
     elif case == "src_range":

@@ -39,6 +39,8 @@ MUTATIONS = [
      DOC),
     ("doc_mask_inverted", C_SRC, "mask[t] = (uint8_t)(doc[t] == 0);",
      "mask[t] = (uint8_t)(doc[t] != 0);", DOC),
+    ("doc_second_position_skipped", C_SRC, "int new_doc = (t > 0) && (doc[t] != doc[t - 1]);",
+     "int new_doc = (t > 1) && (doc[t] != doc[t - 1]);", DOC),
     # process_input_for_thd on length tables
     ("thd_no_mismatch_check", C_SRC, "status |= ORC_TABLE_MISMATCH;", "status |= 0;", THD),
     ("thd_padded_below_real_allowed", C_SRC, "if (l < 0 || lp < l)", "if (l < 0)", THD),
@@ -61,6 +63,17 @@ MUTATIONS = [
      "if (cu[i] > cp[i])\n            *pad_between = 1;", THD),
     ("thd_no_padded_table_pads_one", C_SRC, "phys[n] = (Lp != NULL) ? Lp[r * P + j] : l;",
      "phys[n] = (Lp != NULL) ? Lp[r * P + j] : l + (l & 1);", THD),
+    ("thd_real_boundaries_physical", C_SRC, "cu[i + 1] = cu[i] + (int32_t)real[i];",
+     "cu[i + 1] = cu[i] + (int32_t)phys[i];", THD),
+    ("thd_physical_boundaries_real", C_SRC, "cp[i + 1] = cp[i] + (int32_t)phys[i];",
+     "cp[i + 1] = cp[i] + (int32_t)real[i];", THD),
+    ("thd_overflow_clamp_at_row", C_SRC, "padded_sum += (lp > S) ? S + 1 : lp;",
+     "padded_sum += (lp > S) ? S : lp;", THD),
+    ("thd_mask_starts_as_tokens", C_SRC, "for (t = 0; t < T; t++)\n        mask[t] = 1;",
+     "for (t = 0; t < T; t++)\n        mask[t] = 0;", THD),
+    ("thd_negative_length_allowed", C_SRC, "if (l < 0 || lp < l)", "if (lp < l)", THD),
+    ("thd_mismatch_one_sided", C_SRC, "if (Lp != NULL && ((lp != v) != valid))",
+     "if (Lp != NULL && lp == v && valid)", THD),
     # the squeeze
     ("pack_no_fold", C_SRC, "pcp[k] = C;", "pcp[k] = pcp[k];", PACK),
     ("pack_padding_rounds_down", C_SRC, "int64_t padded = (real + q - 1) / q * q;",
@@ -78,6 +91,17 @@ MUTATIONS = [
     ("pack_order_ignored", C_SRC, "int64_t i = (order != NULL) ? (int64_t)order[a + j] : a + j;",
      "int64_t i = a + j;", PACK),
     ("rect_stride_off_by_one", C_SRC, "off[i] = i * W;", "off[i] = i * W - i;", PACK),
+    ("pack_range_upper_unchecked", C_SRC, "if (a < 0 || b > N || b < a) {",
+     "if (a < 0 || b < a) {", PACK),
+    ("pack_empty_unflagged", C_SRC, "status |= ORC_EMPTY_PACK;", "status |= 0;", PACK),
+    ("pack_source_end_exclusive", C_SRC, "src_off[i] > src_len - real",
+     "src_off[i] >= src_len - real", PACK),
+    ("pack_real_boundary_padded", C_SRC, "pcu[j + 1] = pcu[j] + (int32_t)real;",
+     "pcu[j + 1] = pcu[j] + (int32_t)padded;", PACK),
+    ("pack_first_token_unmasked", C_SRC, "row[off + s] = src[src_off[i] + s];\n                mrow[off + s] = 1;",
+     "row[off + s] = src[src_off[i] + s];\n                mrow[off + s] = (uint8_t)(s > 0);", PACK),
+    ("pack_tail_skips_first_slot", C_SRC, "for (s = off; s < C; s++) {",
+     "for (s = off + 1; s < C; s++) {", PACK),
     ("rect_length_at_width_rejected", C_SRC, "real > row_width", "real >= row_width", PACK),
     ("trainer_width_from_real", PY_SRC,
      "widths = [sum(-(-int(rl[i]) // q) * q for i in b) for b in bins]",
@@ -89,11 +113,15 @@ MUTATIONS = [
      "mask[t] = (uint8_t)(ids[t] != pad);", PADIDS),
     ("padids_content_count_short", C_SRC, "*num_content = first_pad;",
      "*num_content = first_pad - (first_pad > 0);", PADIDS),
+    ("padids_no_pad_means_empty", C_SRC, "int64_t t, first_pad = T;",
+     "int64_t t, first_pad = 0;", PADIDS),
     # split_batch_into_thd_chunks (the Python stacking over the table oracle)
     ("split_fill_zero", PY_SRC, "out = np.full((num_chunks, width), pad_value, dtype=np.int32)",
      "out = np.zeros((num_chunks, width), dtype=np.int32)", THD),
     ("split_uneven_rows", PY_SRC, "rows = B // num_chunks",
      "rows = max(1, B // num_chunks - 1) if B > 2 else B // num_chunks", THD),
+    ("split_status_of_last_chunk", PY_SRC, 'status |= part["status"]',
+     'status = part["status"]', THD),
 ]
 
 ALL_PINS = sorted({f for m in MUTATIONS for f in m[4]})

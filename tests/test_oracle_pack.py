@@ -137,6 +137,9 @@ def test_error_bits():
     assert oracle.pack(src, off, rl, 2, [0, 0, 3], 8)["status"] == oracle.EMPTY_PACK
     assert oracle.pack(src, off, rl, 2, [0, 4], 8)["status"] == oracle.BAD_INDEX
     assert oracle.pack(src, off, rl, 2, [0, 3], 8, order=[0, 1, 3])["status"] == oracle.BAD_INDEX
+    # a pack range reaching past the N member entries is out of range, even
+    # where the caller's order buffer happens to hold more (valid) entries
+    assert oracle.pack(src, off, rl, 2, [0, 4], 8, order=[0, 1, 2, 0])["status"] == oracle.BAD_INDEX
     bad = rl.copy()
     bad[1] = -2
     assert oracle.pack(src, off, bad, 2, [0, 3], 8)["status"] == oracle.BAD_LENGTH

@@ -158,6 +158,18 @@ def test_split_rejects_uneven_chunks():
         oracle.split_thd([[1], [1], [1]], None, S=2, num_chunks=2)
 
 
+def test_split_status_is_the_or_over_chunks():
+    # Each chunk is its own process_input_for_thd call, and the split fails
+    # when any of them does: an empty row in the first chunk only, then a
+    # row overflow in the last chunk as well.
+    L = [[V, V], [2, 3], [1, V], [4, V]]
+    out = oracle.split_thd(L, None, S=6, num_chunks=2)
+    assert out["status"] == oracle.EMPTY_ROW
+    L2 = [[V, V], [2, 3], [1, V], [7, V]]
+    out = oracle.split_thd(L2, None, S=6, num_chunks=2)
+    assert out["status"] == oracle.EMPTY_ROW | oracle.ROW_OVERFLOW
+
+
 def test_row_fold_with_tail_pad_in_every_row():
     out = oracle.thd_tables([[3, 2], [6, V]], [[4, 2], [6, V]], S=8)
     assert out["cu_seqlens"].tolist() == [0, 3, 5, 11]
