@@ -39,6 +39,11 @@ MUTATIONS = [
      DOC),
     ("doc_mask_inverted", C_SRC, "mask[t] = (uint8_t)(doc[t] == 0);",
      "mask[t] = (uint8_t)(doc[t] != 0);", DOC),
+    # the collapse of a [B, S, ...] tensor (pinned in the document-map pins)
+    ("copy_ignores_source_stride", C_SRC, "src[r * src_row_stride_bytes + b]",
+     "src[r * row_bytes + b]", DOC),
+    ("copy_drops_last_byte", C_SRC, "for (b = 0; b < row_bytes; b++)",
+     "for (b = 0; b + 1 < row_bytes; b++)", DOC),
     ("doc_second_position_skipped", C_SRC, "int new_doc = (t > 0) && (doc[t] != doc[t - 1]);",
      "int new_doc = (t > 1) && (doc[t] != doc[t - 1]);", DOC),
     # process_input_for_thd on length tables
