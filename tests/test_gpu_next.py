@@ -160,6 +160,16 @@ def test_split_hand_ragged(dev):
     check_split(dev, np.array([[2, 3, 1], [1, V, V]]), np.array([[2, 3, 1], [1, V, V]]), 8, 2)
 
 
+# no rows (each chunk is an empty batch: cu_seqlens [0]); rows of length 0
+# holding empty sequences; rows without a slot (EMPTY_ROW)
+@pytest.mark.parametrize("L,S,G", [(np.zeros((0, 3), np.int64), 8, 2),
+                                   (np.array([[0], [0]]), 0, 2),
+                                   (np.zeros((4, 0), np.int64), 8, 2)],
+                         ids=["no_rows", "zero_length_rows", "no_slots"])
+def test_split_degenerate_shapes(dev, L, S, G):
+    check_split(dev, L, None, S, G)
+
+
 @pytest.mark.parametrize("L,Lp,S,G", [
     ([[3, 2], [5, V]], [[4, 2], [4, V]], 8, 2),     # real > padded in chunk 1
     ([[3, 2], [V, V]], [[4, 2], [V, V]], 8, 2),     # empty row in chunk 1

@@ -327,6 +327,25 @@ def test_thd_hand_cases(dev, L, Lp, S):
     check_thd(dev, np.array(L), None if Lp is None else np.array(Lp), S)
 
 
+# Empty tables and rows of no length (they take the multi-workgroup kernel):
+# no rows at all; rows without a slot (EMPTY_ROW); rows of length 0 holding
+# empty sequences; a token in a row of length 0 (ROW_OVERFLOW).
+@pytest.mark.parametrize("L,S", [
+    (np.zeros((0, 3), np.int64), 8),
+    (np.zeros((0, 100), np.int64), 8),
+    (np.zeros((2, 0), np.int64), 8),
+    (np.zeros((100, 0), np.int64), 8),
+    (np.array([[0]]), 0),
+    (np.array([[0, V], [0, 0]]), 0),
+    (np.array([[1]]), 0),
+], ids=["no_rows", "no_rows_wide", "no_slots", "no_slots_many_rows", "zero_length_row",
+        "zero_length_rows", "token_in_zero_length_row"])
+@pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
+def test_thd_degenerate_shapes(dev, L, S, dtype):
+    check_thd(dev, L, None, S, dtype)
+    check_thd(dev, L, L.copy(), S, dtype)
+
+
 @pytest.mark.parametrize("S", [(1 << 25) - 1, 1 << 25, (1 << 25) + 7])
 @pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
 def test_thd_rows_long_rows(dev, S, dtype):
@@ -667,6 +686,12 @@ def test_pack_error_bits(dev, case):
 
 def test_pack_no_packs(dev):
     check_pack(dev, np.arange(3), [0], [3], 1, [0], 8, True, what="P=0")
+
+
+def test_pack_no_sources(dev):
+    """Packs but no sources: every pack is empty (EMPTY_PACK)."""
+    empty = np.zeros(0, np.int64)
+    check_pack(dev, empty, empty, np.zeros(0, np.int32), 2, [0, 0, 0], 8, True, what="N=0")
 
 
 def test_pack_workspace_header_left_zeroed(dev):
