@@ -139,6 +139,20 @@ def test_doc_many_chunks_per_workgroup(dev, B, S, kind):
     check_doc(dev, d)
 
 
+@pytest.mark.parametrize("B,S", [(3, 300001), (2, 1000000), (1, 4194304), (1, 4194305),
+                                 (3, 2100000)],
+                         ids=["one_launch_4", "one_launch_8", "one_launch_16", "two_launch",
+                              "two_launch_rows"])
+def test_doc_int64_maps_on_every_path(dev, B, S):
+    """int64 maps large enough for the one-launch kernel at 4096, 8192 and
+    16384 positions per tile and for the two launches; neighbouring ids
+    differ only in their upper 32 bits, and padding (0) stays 0."""
+    rng = np.random.default_rng(B * 1000003 + S)
+    d = _long_runs(rng, B, S, 300).astype(np.int64)
+    d = np.where(d == 0, 0, d * (1 << 32) + 7)
+    check_doc(dev, d, torch.int64)
+
+
 def test_doc_one_launch_sequence(dev):
     """Maps of up to 256 chunks of 16384 positions take one launch, over the
     smallest tiles (1024 to 16384 positions) that need at most 256 of them,
