@@ -191,25 +191,33 @@ def test_doc_tile_size_boundaries(dev, total):
         check_doc(dev, rng.integers(0, 3, size=(B, S)).astype(np.int32))
 
 
-def test_doc_unaligned_input(dev):
-    # a view that starts 4 bytes into its storage: the scalar-load path
-    d = synth.doc_map_medium()
-    base = torch.from_numpy(np.concatenate([[9], d.reshape(-1)]).astype(np.int32)).to(dev)
+@pytest.mark.parametrize("B,S", [(3, 1000), (8, 4096), (3, 300001), (1, 4194304), (3, 2100000)],
+                         ids=["one_workgroup", "one_launch_1", "one_launch_4", "one_launch_16",
+                              "two_launch"])
+@pytest.mark.parametrize("dtype", [torch.int32, torch.int64])
+def test_doc_unaligned_input(dev, B, S, dtype):
+    """A map view one element into its storage (not 16-byte aligned: the
+    scalar-load path) and a mask one byte in (not 4-byte aligned: byte
+    stores), on every kernel path."""
+    rng = np.random.default_rng(B * 7 + S)
+    d = _long_runs(rng, B, S, 300) if B * S > 100000 else synth.doc_map_medium(2, B, S)
+    np_dt = np.int32 if dtype == torch.int32 else np.int64
+    base = torch.from_numpy(np.concatenate([[9], d.reshape(-1)]).astype(np_dt)).to(dev)
     view = base[1:].view(d.shape)
     assert view.data_ptr() % 16 != 0
-    B, S = d.shape
     cu = torch.empty(B * S + 1, dtype=torch.int32, device=dev)
     scal = torch.empty(4, dtype=torch.int32, device=dev)
     mask = torch.empty(B * S + 1, dtype=torch.uint8, device=dev)[1:]   # unaligned mask too
     ws = psq.workspace_for(dev, _lib.psq_params_from_doc_ids_workspace(B, S))
     sp = scal.data_ptr()
-    say("doc map unaligned")
-    _lib.psq_params_from_doc_ids(view.data_ptr(), _lib.I32, B, S, cu.data_ptr(), sp, sp + 4,
-                                 mask.data_ptr(), sp + 8, ws.data_ptr(), ws.numel(),
+    say(f"doc map unaligned {B}x{S} {dtype}")
+    _lib.psq_params_from_doc_ids(view.data_ptr(), _lib.I32 if dtype == torch.int32 else _lib.I64,
+                                 B, S, cu.data_ptr(), sp, sp + 4, mask.data_ptr(), sp + 8,
+                                 ws.data_ptr(), ws.numel(),
                                  torch.cuda.current_stream(dev).cuda_stream)
     n, mx, st, _ = scal.cpu().tolist()
     ref = oracle.doc_segments(d)
-    assert st == 0 and mx == ref["max_seqlen"]
+    assert st == 0 and n == ref["num_segments"] and mx == ref["max_seqlen"]
     assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
     assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
 
@@ -540,6 +548,79 @@ def test_thd_embeddings_mrope_and_strided(dev):
     assert "cu_seqlens_padded" not in out
     ref = oracle.thd_tables(L.cpu().numpy(), None, S)
     assert np.array_equal(out["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+
+
+# One copy of each kind the planner tells apart: unit size 16/8/4/1 bytes,
+# dense or strided rows (a strided destination too), ragged unit counts.
+# (byte offset from 16-byte alignment, rows, row_bytes, src stride, dst stride)
+COPY_SPECS = [(0, 1, 16 * 1000, 16 * 1000, 0), (0, 37, 48, 80, 0),
+              (8, 1, 8 * 777, 8 * 777, 0), (8, 5, 24, 40, 0),
+              (4, 1, 4 * 999, 4 * 999, 0), (4, 9, 12, 20, 16),
+              (1, 1, 1001, 1001, 0), (1, 13, 7, 11, 9)]
+
+
+@pytest.mark.parametrize("path", ["small_tables", "large_tables", "doc_map", "split"])
+def test_copy_kinds_on_every_path(dev, path):
+    """Every copy kind in one call, on each launch that carries copies: the
+    16-byte dense copy fused into the single-workgroup table kernel, into
+    the multi-workgroup table kernel, or launched alone after a document
+    map, and the split.  The whole destination buffer is compared, so a
+    write outside a copy's rows would show."""
+    rng = np.random.default_rng(17)
+    placed, s_cur, d_cur = [], 0, 0
+    for off, rows, rb, ss, ds in COPY_SPECS:
+        s0 = -(-s_cur // 16) * 16 + off
+        d0 = -(-d_cur // 16) * 16 + off
+        dstep = ds if ds else rb
+        placed.append((s0, d0, rows, rb, ss, ds))
+        s_cur = s0 + (rows - 1) * ss + rb + 32
+        d_cur = d0 + (rows - 1) * dstep + rb + 32
+    src_np = rng.integers(0, 256, size=s_cur, dtype=np.uint8)
+    src = torch.from_numpy(src_np).to(dev)
+    dst = torch.full((d_cur,), 0xA5, dtype=torch.uint8, device=dev)
+    want = np.full(d_cur, 0xA5, dtype=np.uint8)
+    descs = []
+    for s0, d0, rows, rb, ss, ds in placed:
+        descs.append((src.data_ptr() + s0, dst.data_ptr() + d0, rows, rb, ss, ds))
+        dense = oracle.copy_rows(src_np[s0:], rows, rb, ss).reshape(rows, rb)
+        step = ds if ds else rb
+        for r in range(rows):
+            want[d0 + r * step: d0 + r * step + rb] = dense[r]
+    arr, n_c = _lib.make_copies(descs)
+    assert n_c == _lib.MAX_COPIES
+    say(f"copy kinds on the {path} path")
+    scal = torch.full((8,), -7, dtype=torch.int32, device=dev)
+    sp = scal.data_ptr()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if path == "doc_map":
+        doc = torch.ones((2, 64), dtype=torch.int32, device=dev)
+        lay = _lib.make_layout(_lib.LAYOUT_DOC_IDS, doc_ids=doc.data_ptr())
+        B, S, P = 2, 64, 0
+    else:
+        B, P = (2, 1) if path != "large_tables" else (1, 5000)
+        S = 64
+        L = np.full((B, P), V, dtype=np.int64)
+        L[:, 0] = S
+        tL = torch.from_numpy(L).to(dev)
+        lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, tL.data_ptr(), None, _lib.I64, P, V)
+    cu = torch.empty(max(B * max(P, S), 1) + 4, dtype=torch.int32, device=dev)
+    mask = torch.empty(B * S, dtype=torch.uint8, device=dev)
+    if path == "split":
+        G = 2
+        per = torch.empty((3, G), dtype=torch.int32, device=dev)
+        pp = per.data_ptr()
+        ws = psq.workspace_for(dev, _lib.psq_split_thd_workspace(lay, B, S, G))
+        _lib.psq_split_thd(lay, B, S, G, cu.data_ptr(), None, sp, pp, pp + 4 * G, pp + 8 * G,
+                           mask.data_ptr(), arr, n_c, sp + 4, ws.data_ptr(), ws.numel(), stream)
+        status = int(scal[1].item())
+    else:
+        ws = psq.workspace_for(dev, _lib.psq_process_thd_workspace(lay, B, S))
+        _lib.psq_process_thd(lay, B, S, cu.data_ptr(), None, sp, sp + 4, sp + 8,
+                             mask.data_ptr(), arr, n_c, sp + 12, ws.data_ptr(), ws.numel(),
+                             stream)
+        status = int(scal[3].item())
+    assert status == 0
+    assert np.array_equal(dst.cpu().numpy(), want)
 
 
 def test_stage_embedding_full(dev):
