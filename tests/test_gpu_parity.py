@@ -441,7 +441,7 @@ def rand_tables(rng, B, P, S, q, tight=False, holes=False, zero_frac=0.1, maxlen
 
 @pytest.mark.parametrize("B,P,S", [(1, 1, 1), (1, 4, 7), (3, 5, 16), (2, 8, 4096),
                                    (3, 16, 4097), (2, 64, 8192), (4, 7, 12345),
-                                   (1, 2000, 30000), (2, 3000, 9000)])
+                                   (1, 2000, 30000), (1, 3000, 9000), (2, 3000, 9000)])
 @pytest.mark.parametrize("mode", ["plain", "tight", "holes", "nopad", "int32"])
 def test_thd_fuzz(dev, B, P, S, mode):
     rng = np.random.default_rng(hash((B, P, S, mode)) % 2**32)
