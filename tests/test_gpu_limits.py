@@ -56,6 +56,16 @@ def test_closed_form_matches_oracle_small():
     assert ref["cu_seqlens_padded"].tolist() == [r * S for r in range(B + 1)]
     assert ref["cu_seqlens"].tolist() == [r * (S - pad) for r in range(B + 1)]
     assert ref["pad_between_seqs"] == 1 and ref["max_seqlen"] == S - pad
+    # a content prefix then a pad tail; and the same with the pad id planted at 7
+    T, tail = 50, 9
+    ids = np.ones(T, dtype=np.int64)
+    ids[T - tail:] = 0
+    ref = oracle.pad_mask_from_ids(ids, 0)
+    assert ref["status"] == 0 and ref["num_content"] == T - tail
+    assert int(ref["padding_mask"].sum()) == tail and ref["padding_mask"][T - tail] == 1
+    ids[7] = 0
+    ref = oracle.pad_mask_from_ids(ids, 0)
+    assert ref["status"] == oracle.PAD_IS_CONTENT and ref["num_content"] == 7
 
 
 def test_doc_map_at_int32_limit(dev):
@@ -144,3 +154,33 @@ def test_pack_at_capacity_limit(dev):
     assert int(tm.sum(dtype=torch.int64).item()) == sum(lens)
     assert bool((packed[0, at:] == -1).all())
     del packed, tm
+
+
+@pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
+def test_pad_ids_at_int32_limit(dev, dtype):
+    """2^31 - 1 ids: the first pad slot and one past the last content slot
+    fill their 31-bit record fields, and each workgroup strides over 512
+    tiles or more."""
+    T, tail = (1 << 31) - 1, 12345
+    say(f"pad ids at the int32 limit: T={T} {dtype}")
+    ids = torch.ones(T, dtype=dtype, device=dev)
+    ids[T - tail:] = 0
+    mask = torch.empty(T, dtype=torch.uint8, device=dev)
+    scal = torch.full((2,), -7, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, _lib.psq_padding_mask_from_token_ids_workspace(T))
+    sp = scal.data_ptr()
+    kind = _lib.I64 if dtype == torch.int64 else _lib.I32
+    for planted in (None, 7):
+        if planted is not None:
+            ids[planted] = 0
+        _lib.psq_padding_mask_from_token_ids(ids.data_ptr(), kind, T, 0, mask.data_ptr(), sp,
+                                             sp + 4, ws.data_ptr(), ws.numel(), _stream(dev))
+        nc, st = scal.cpu().tolist()
+        if planted is None:
+            assert st == 0 and nc == T - tail
+            assert int(mask.sum(dtype=torch.int64).item()) == tail
+            assert int(mask[T - tail - 1].item()) == 0 and int(mask[T - tail].item()) == 1
+        else:
+            assert st == _lib.DATA_PAD_IS_CONTENT and nc == planted
+            assert int(mask.sum(dtype=torch.int64).item()) == tail + 1
+    del ids, mask
