@@ -56,6 +56,12 @@ def test_closed_form_matches_oracle_small():
     assert ref["cu_seqlens_padded"].tolist() == [r * S for r in range(B + 1)]
     assert ref["cu_seqlens"].tolist() == [r * (S - pad) for r in range(B + 1)]
     assert ref["pad_between_seqs"] == 1 and ref["max_seqlen"] == S - pad
+    # the same rows split into row groups: every group has the same closed form
+    ref = oracle.split_thd(np.array([[S - pad, V]] * 6), np.array([[S - pad, V]] * 6), S, 2)
+    assert ref["cu_seqlens_padded"].tolist() == [[r * S for r in range(4)]] * 2
+    assert ref["cu_seqlens"].tolist() == [[r * (S - pad) for r in range(4)]] * 2
+    assert ref["num_seqs"].tolist() == [3, 3] and ref["max_seqlen"].tolist() == [S - pad] * 2
+    assert ref["pad_between_seqs"].tolist() == [1, 1]
     # a content prefix then a pad tail; and the same with the pad id planted at 7
     T, tail = 50, 9
     ids = np.ones(T, dtype=np.int64)
@@ -116,6 +122,37 @@ def test_thd_tables_at_int32_limit(dev):
     # every row folds its tail pad: no interior boundary agrees, no absorption
     assert cu[: n + 1].cpu().tolist() == [r * real for r in range(B + 1)]
     assert pb == 1 and mx == real
+    assert int(mask.sum(dtype=torch.int64).item()) == B * (S - real)
+    del mask
+
+
+def test_split_at_int32_limit(dev):
+    """The table batch near 2^31 tokens split into 2 row groups: each group
+    holds 1023 rows (over 2^30 tokens) and is stacked into a [2, 1024] array."""
+    B, S, real, G = 2046, 1 << 20, (1 << 20) - 4099, 2
+    T, Bc = B * S, B // G
+    say(f"split at the int32 limit: B={B} S={S} G={G}")
+    L = torch.tensor([[real, V]] * B, dtype=torch.int64, device=dev)
+    cap = G * (Bc * 2 + 1)
+    cu = torch.empty(cap, dtype=torch.int32, device=dev)
+    cp = torch.empty(cap, dtype=torch.int32, device=dev)
+    mask = torch.empty(T, dtype=torch.uint8, device=dev)
+    per = torch.full((3, G), -7, dtype=torch.int32, device=dev)
+    scal = torch.full((2,), -7, dtype=torch.int32, device=dev)
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, L.data_ptr(), L.data_ptr(), _lib.I64, 2, V)
+    ws = psq.workspace_for(dev, _lib.psq_split_thd_workspace(lay, B, S, G))
+    arr, n_c = _lib.make_copies([])
+    pp, sp = per.data_ptr(), scal.data_ptr()
+    _lib.psq_split_thd(lay, B, S, G, cu.data_ptr(), cp.data_ptr(), sp, pp, pp + 4 * G,
+                       pp + 8 * G, mask.data_ptr(), arr, n_c, sp + 4, ws.data_ptr(), ws.numel(),
+                       _stream(dev))
+    width, st = scal.cpu().tolist()
+    assert st == 0 and width == Bc + 1
+    want_cp = [r * S for r in range(Bc + 1)]
+    want_cu = [r * real for r in range(Bc + 1)]
+    assert cp[: G * width].view(G, width).cpu().tolist() == [want_cp] * G
+    assert cu[: G * width].view(G, width).cpu().tolist() == [want_cu] * G
+    assert per.cpu().tolist() == [[Bc] * G, [real] * G, [1] * G]
     assert int(mask.sum(dtype=torch.int64).item()) == B * (S - real)
     del mask
 
