@@ -45,6 +45,18 @@ def two_run_rows(B, S, pad):
     return np.array(starts + [B * S], dtype=np.int64)
 
 
+def squeeze_closed_form(lens, order, q):
+    """Closed form of one pack holding sources `order` (lengths `lens`) end
+    to end, each padded to a multiple of q, fold off: the real and padded
+    boundaries and each member's first slot."""
+    cu, cp, at = [0], [0], []
+    for i in order:
+        at.append(cp[-1])
+        cu.append(cu[-1] + lens[i])
+        cp.append(cp[-1] + -(-lens[i] // q) * q)
+    return cu, cp, at
+
+
 def test_closed_form_matches_oracle_small():
     B, S, pad = 5, 12, 3
     doc = np.ones((B, S), dtype=np.int64)
@@ -62,6 +74,16 @@ def test_closed_form_matches_oracle_small():
     assert ref["cu_seqlens"].tolist() == [[r * (S - pad) for r in range(4)]] * 2
     assert ref["num_seqs"].tolist() == [3, 3] and ref["max_seqlen"].tolist() == [S - pad] * 2
     assert ref["pad_between_seqs"].tolist() == [1, 1]
+    # a padded rectangle squeezed into one bin, members out of row order
+    lens, order, q, W = [5, 1000, 7000], [2, 0, 1], 64, 7003
+    rng = np.random.default_rng(4)
+    rows = rng.integers(0, 1 << 40, size=(3, W))
+    ref = oracle.pack_rect(rows, lens, q, [order], width=9000)
+    cu, cp, at = squeeze_closed_form(lens, order, q)
+    assert ref["status"] == 0
+    assert ref["cu_seqlens"].tolist() == cu and ref["cu_seqlens_padded"].tolist() == cp
+    for i, a in zip(order, at):
+        assert np.array_equal(ref["packed"][0, a:a + lens[i]], rows[i, :lens[i]])
     # a content prefix then a pad tail; and the same with the pad id planted at 7
     T, tail = 50, 9
     ids = np.ones(T, dtype=np.int64)
@@ -221,3 +243,41 @@ def test_pad_ids_at_int32_limit(dev, dtype):
             assert st == _lib.DATA_PAD_IS_CONTENT and nc == planted
             assert int(mask.sum(dtype=torch.int64).item()) == tail + 1
     del ids, mask
+
+
+def test_trainer_rows_beyond_int32_elements(dev):
+    """A padded rectangle whose rows start past 2^31 elements (row 2 begins
+    at byte 16 GiB): the trainer squeeze's row offsets are 64-bit."""
+    W, q, C = (1 << 30) + 3, 64, 1 << 20
+    lens, order = [5, 1000, 70000], [2, 0, 1]
+    N = len(lens)
+    say(f"trainer squeeze from a [{N}, {W}] rectangle")
+    rng = np.random.default_rng(5)
+    rows = torch.empty((N, W), dtype=torch.int64, device=dev)
+    toks = []
+    for i, n in enumerate(lens):
+        t = rng.integers(0, 1 << 40, size=n)
+        rows[i, :n] = torch.from_numpy(t).to(dev)
+        toks.append(t)
+    rl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    od = torch.tensor(order, dtype=torch.int32, device=dev)
+    ps = torch.tensor([0, N], dtype=torch.int64, device=dev)
+    packed = torch.empty((1, C), dtype=torch.int64, device=dev)
+    tm = torch.empty((1, C), dtype=torch.uint8, device=dev)
+    cu_d = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    cp_d = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    st = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, _lib.psq_pack_rows_workspace(N, 1, C))
+    _lib.psq_pack_padded_rows(rows.data_ptr(), W, rl.data_ptr(), N, q, od.data_ptr(),
+                              ps.data_ptr(), 1, C, 0, -1, packed.data_ptr(), tm.data_ptr(),
+                              cu_d.data_ptr(), cp_d.data_ptr(), st.data_ptr(), ws.data_ptr(),
+                              ws.numel(), _stream(dev))
+    assert int(st.item()) == 0
+    cu, cp, at = squeeze_closed_form(lens, order, q)
+    assert cu_d.cpu().tolist() == cu and cp_d.cpu().tolist() == cp
+    for i, a in zip(order, at):
+        assert np.array_equal(packed[0, a:a + lens[i]].cpu().numpy(), toks[i])
+        assert bool((packed[0, a + lens[i]:a + -(-lens[i] // q) * q] == -1).all())
+    assert bool((packed[0, cp[-1]:] == -1).all())
+    assert int(tm.sum(dtype=torch.int64).item()) == sum(lens)
+    del rows, packed, tm
