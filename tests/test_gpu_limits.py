@@ -84,6 +84,14 @@ def test_closed_form_matches_oracle_small():
     assert ref["cu_seqlens"].tolist() == cu and ref["cu_seqlens_padded"].tolist() == cp
     for i, a in zip(order, at):
         assert np.array_equal(ref["packed"][0, a:a + lens[i]], rows[i, :lens[i]])
+    # loader sources end to end in one folded pack, a source ending exactly at
+    # the token buffer's end; one token less in the buffer is BAD_INDEX
+    src, offs = np.arange(100, 100 + 8005), [1000, 0, 1005]
+    ref = oracle.pack(src, offs, lens, q, [0, 3], 9000, fold=True)
+    cu, cp, at = squeeze_closed_form(lens, range(3), q)
+    assert ref["status"] == 0
+    assert ref["cu_seqlens"].tolist() == cu and ref["cu_seqlens_padded"].tolist() == cp[:-1] + [9000]
+    assert oracle.pack(src[:-1], offs, lens, q, [0, 3], 9000)["status"] == oracle.BAD_INDEX
     # a content prefix then a pad tail; and the same with the pad id planted at 7
     T, tail = 50, 9
     ids = np.ones(T, dtype=np.int64)
@@ -281,3 +289,48 @@ def test_trainer_rows_beyond_int32_elements(dev):
     assert bool((packed[0, cp[-1]:] == -1).all())
     assert int(tm.sum(dtype=torch.int64).item()) == sum(lens)
     del rows, packed, tm
+
+
+def test_loader_sources_beyond_int32_elements(dev):
+    """Loader sources at offsets past 2^31 elements of a 16 GiB token buffer,
+    the last one ending exactly at the buffer's end (the inclusive bound)."""
+    q, C = 64, 1 << 20
+    lens = [5, 1000, 70000]
+    base = 1 << 31
+    offs = [base + 7, 3, base + 10000]
+    src_len = offs[2] + lens[2]
+    say(f"loader squeeze from a {src_len}-token buffer")
+    rng = np.random.default_rng(6)
+    src = torch.empty(src_len, dtype=torch.int64, device=dev)
+    toks = []
+    for o, n in zip(offs, lens):
+        t = rng.integers(0, 1 << 40, size=n)
+        src[o:o + n] = torch.from_numpy(t).to(dev)
+        toks.append(t)
+    N = len(lens)
+    off = torch.tensor(offs, dtype=torch.int64, device=dev)
+    rl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ps = torch.tensor([0, N], dtype=torch.int64, device=dev)
+    packed = torch.empty((1, C), dtype=torch.int64, device=dev)
+    tm = torch.empty((1, C), dtype=torch.uint8, device=dev)
+    cu_d = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    cp_d = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    st = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    ws = psq.workspace_for(dev, _lib.psq_pack_rows_workspace(N, 1, C))
+    _lib.psq_pack_rows(src.data_ptr(), src_len, off.data_ptr(), rl.data_ptr(), N, q, None,
+                       ps.data_ptr(), 1, C, 1, -1, packed.data_ptr(), tm.data_ptr(),
+                       cu_d.data_ptr(), cp_d.data_ptr(), st.data_ptr(), ws.data_ptr(),
+                       ws.numel(), _stream(dev))
+    assert int(st.item()) == 0
+    cu, cp, at = squeeze_closed_form(lens, range(N), q)
+    assert cu_d.cpu().tolist() == cu and cp_d.cpu().tolist() == cp[:-1] + [C]
+    for i, a in enumerate(at):
+        assert np.array_equal(packed[0, a:a + lens[i]].cpu().numpy(), toks[i])
+    assert int(tm.sum(dtype=torch.int64).item()) == sum(lens)
+    # one token more and the last source runs past the buffer: BAD_INDEX
+    _lib.psq_pack_rows(src.data_ptr(), src_len - 1, off.data_ptr(), rl.data_ptr(), N, q, None,
+                       ps.data_ptr(), 1, C, 1, -1, packed.data_ptr(), tm.data_ptr(),
+                       cu_d.data_ptr(), cp_d.data_ptr(), st.data_ptr(), ws.data_ptr(),
+                       ws.numel(), _stream(dev))
+    assert int(st.item()) == _lib.DATA_BAD_INDEX
+    del src, packed, tm
