@@ -12,7 +12,6 @@ entry point (sizes around the int32 and int64 limits, strides and
 overlapping copies, chunk counts around their edges, null and misaligned
 pointers), checking each workspace query against its call.
 """
-import glob
 import os
 import re
 import shutil

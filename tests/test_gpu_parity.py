@@ -5,7 +5,6 @@ Cases cover the five workloads at full size, seeded fuzz across tile and
 chunk boundaries, the degenerate shapes, the data-error bits, repeat-run
 determinism (the cross-workgroup look-back), and the workspace contract.
 """
-import ctypes
 
 import numpy as np
 import pytest
