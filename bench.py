@@ -90,9 +90,9 @@ COUNTER_TABLE = [
 ]
 
 COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
-COUNTER_COMMANDS = """rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- python3 bench.py --profile-launches 3 --launch-info gpurun_out/launch_info.json
-rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- python3 bench.py --profile-launches 3
-python bench.py --summarize-counters gpurun_out/pmc_fetch/fetch_counter_collection.csv gpurun_out/pmc_write/write_counter_collection.csv --launch-info gpurun_out/launch_info.json"""
+COUNTER_COMMANDS = """rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc_fetch -o fetch -- python3 bench.py --profile-launches 3 --launch-info rocprof_out/launch_info.json
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc_write -o write -- python3 bench.py --profile-launches 3
+python bench.py --summarize-counters rocprof_out/pmc_fetch/fetch_counter_collection.csv rocprof_out/pmc_write/write_counter_collection.csv --launch-info rocprof_out/launch_info.json"""
 
 COUNTERS_NOTES = """Per-kernel values are medians over the launches. `profiles/traffic_stage_embedding.json`
 holds the full output, tagged with the hash of the stage kernels' code. bench.py uses
