@@ -345,6 +345,23 @@ def test_workspace_status_drops_the_cached_workspace(monkeypatch):
         cache.update(saved)
 
 
+def test_readme_c_example_compiles(tmp_path):
+    """The C example in README.md compiles as C99 against include/psq.h and
+    the HIP runtime headers, with no warnings."""
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    text = open(os.path.join(root, "README.md")).read()
+    blocks = re.findall(r"```c\n(.*?)```", text, flags=re.S)
+    assert len(blocks) == 1
+    src = tmp_path / "example.c"
+    src.write_text(blocks[0])
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                        "-I", "/opt/rocm/include", str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_header_is_c_and_matches_the_binding(tmp_path):
     """``include/psq.h`` compiles as C99 and as C++, every function it declares
     links against ``libpsq.so``, and its structs and constants have the
