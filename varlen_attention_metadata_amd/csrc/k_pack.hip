@@ -195,12 +195,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 5))
                 uint32_t own[kPerThread];
 #pragma unroll
                 for (int t = 0; t < kPerThread; ++t) own[t] = (uint32_t)j0;
-                for (int j = j0 + 1; j < upto; ++j) {
-                    const uint32_t st = (uint32_t)read_lane((int)my_start, j);
+                for (int mj = j0 + 1; mj < upto; ++mj) {
+                    const uint32_t st = (uint32_t)read_lane((int)my_start, mj);
 #pragma unroll
                     for (int t = 0; t < kPerThread; ++t) {
                         const uint32_t s = ub + threadIdx.x + (uint32_t)kThreads * (uint32_t)t;
-                        own[t] = s >= st ? (uint32_t)j : own[t];
+                        own[t] = s >= st ? (uint32_t)mj : own[t];
                     }
                 }
 #pragma unroll
