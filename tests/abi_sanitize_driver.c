@@ -497,30 +497,30 @@ static void record(int rc, long launches_before)
  * sizes; the call is made with a good workspace of q bytes, then q-1 */
 #define WS_CONSISTENCY(q, CALL, a)                                                      \
     do {                                                                                \
-        long l0 = stub_launches;                                                        \
-        int rc;                                                                         \
+        long ws_l0 = stub_launches;                                                     \
+        int ws_rc;                                                                      \
         (a).ws = P(FAKE);                                                               \
         (a).wsb = (q) ? (q) : ((size_t)1 << 40);                                        \
-        rc = CALL(a);                                                                   \
-        record(rc, l0);                                                                 \
-        if ((q) == 0 && rc != PSQ_ERR_ARG && rc != PSQ_ERR_OVERFLOW) {                  \
-            fprintf(stderr, "line %d: query 0 but call returned %d\n", __LINE__, rc);   \
+        ws_rc = CALL(a);                                                                \
+        record(ws_rc, ws_l0);                                                           \
+        if ((q) == 0 && ws_rc != PSQ_ERR_ARG && ws_rc != PSQ_ERR_OVERFLOW) {            \
+            fprintf(stderr, "line %d: query 0 but call returned %d\n", __LINE__, ws_rc); \
             ++failures;                                                                 \
         }                                                                               \
-        if ((q) > 0 && rc == PSQ_OK) {                                                  \
+        if ((q) > 0 && ws_rc == PSQ_OK) {                                               \
             (a).wsb = (q) - 1;                                                          \
-            l0 = stub_launches;                                                         \
-            rc = CALL(a);                                                               \
+            ws_l0 = stub_launches;                                                      \
+            ws_rc = CALL(a);                                                            \
             ++rc_count[3];                                                              \
-            if (rc != PSQ_ERR_WORKSPACE || stub_launches != l0) {                       \
-                fprintf(stderr, "line %d: one byte short returned %d\n", __LINE__, rc); \
+            if (ws_rc != PSQ_ERR_WORKSPACE || stub_launches != ws_l0) {                 \
+                fprintf(stderr, "line %d: one byte short returned %d\n", __LINE__, ws_rc); \
                 ++failures;                                                             \
             }                                                                           \
             (a).wsb = (q);                                                              \
             (a).ws = P(FAKE + 8);                                                       \
-            rc = CALL(a);                                                               \
-            if (rc != PSQ_ERR_WORKSPACE || stub_launches != l0) {                       \
-                fprintf(stderr, "line %d: misaligned returned %d\n", __LINE__, rc);     \
+            ws_rc = CALL(a);                                                            \
+            if (ws_rc != PSQ_ERR_WORKSPACE || stub_launches != ws_l0) {                 \
+                fprintf(stderr, "line %d: misaligned returned %d\n", __LINE__, ws_rc);  \
                 ++failures;                                                             \
             }                                                                           \
         }                                                                               \
