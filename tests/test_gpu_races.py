@@ -8,6 +8,10 @@ orders in which workgroups reach those steps are therefore shuffled from
 call to call.  Each case runs repeatedly on the same inputs and every run
 must equal the CPU oracle exactly and leave the workspace zero-filled.
 
+A last case interleaves random calls of the three kernels that exchange
+records through the workspace (maps, pad-id streams, split tables), all
+through one shared workspace.
+
 The kernels covered: the one-launch document map of up to 256 tiles of
 1024 to 16384 positions (tagged records, waits on the earlier tiles, the
 last tile's reset of the state),
@@ -239,3 +243,110 @@ def test_pad_ids_under_jitter(jl, dev, kind, T):
         assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
         assert nc == ref["num_content"]
         _assert_zero(ws)
+
+
+def test_random_calls_share_one_workspace_under_jitter(jl, dev):
+    """Random calls of the three kernels that exchange records through the
+    workspace, interleaved through one workspace as the Python binding shares
+    it on a stream: document maps of 4097 to 6 M positions (the one-launch
+    path at every chunk size, and two launches), pad-id streams of up to 5 M
+    ids with and without a planted pad id, and length tables above the
+    single-workgroup size split into random row groups.  Each call's outputs
+    equal the oracle's; the workspace is clean at the end."""
+    rng = np.random.default_rng(2024)
+
+    def lu(lo, hi):
+        return int(np.exp(rng.uniform(np.log(lo), np.log(hi + 1))))
+
+    cases = []
+    for i in range(60):
+        kind = i % 3
+        if kind == 0:
+            total = lu(4097, 6_000_000)
+            B = max(1, min(lu(1, 64), total // 64))
+            S = max(1, total // B)
+            cases.append(("doc", B, S, synth.doc_map_medium(300 + i, B, min(S, 4096))
+                          if S <= 4096 else None))
+        elif kind == 1:
+            cases.append(("pad", lu(1, 5_000_000)))
+        else:
+            B = lu(1, 1200)
+            P = max(-(-4097 // B), lu(1, 16))
+            G = int(rng.choice([g for g in range(1, min(B, 300) + 1) if B % g == 0]))
+            cases.append(("tables", B, P, lu(64, 5000), G))
+    need = 256
+    for c in cases:
+        if c[0] == "doc":
+            need = max(need, jl.psq_params_from_doc_ids_workspace(c[1], c[2]))
+        elif c[0] == "pad":
+            need = max(need, jl.psq_padding_mask_from_token_ids_workspace(c[1]))
+        else:
+            lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, 1, 1, _lib.I64, c[2], V)
+            need = max(need, jl.psq_split_thd_workspace(ctypes.byref(lay), c[1], c[3], c[4]))
+    ws = _workspace(dev, need)
+    arr, n_c = _lib.make_copies([])
+    for i, c in enumerate(cases):
+        if c[0] == "doc":
+            B, S = c[1], c[2]
+            d = c[3] if c[3] is not None else np.repeat(
+                rng.integers(0, 4, size=(B, S // 97 + 1)), 97, axis=1)[:, :S].astype(np.int32)
+            say(f"jitter random call {i}: doc map {B}x{S}")
+            ref = oracle.doc_segments(d)
+            t = torch.from_numpy(np.ascontiguousarray(d)).to(dev)
+            cu = torch.full((B * S + 1,), -7, dtype=torch.int32, device=dev)
+            mask = torch.full((B * S,), 7, dtype=torch.uint8, device=dev)
+            scal = torch.full((3,), -7, dtype=torch.int32, device=dev)
+            sp = scal.data_ptr()
+            assert jl.psq_params_from_doc_ids(t.data_ptr(), _lib.I32, B, S, cu.data_ptr(), sp,
+                                              sp + 4, mask.data_ptr(), sp + 8, ws.data_ptr(),
+                                              ws.numel(), _stream(dev)) == 0
+            n, mx, st = scal.cpu().tolist()
+            assert st == 0 and n == ref["num_segments"] and mx == ref["max_seqlen"]
+            assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"])
+            assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
+        elif c[0] == "pad":
+            T = c[1]
+            w = synth.pad_tail_stream(400 + i, T=T, tail_hi=max(1, T // 2))
+            ids = w["input_ids"].copy()
+            if rng.random() < 0.3:
+                ids[int(rng.integers(0, T))] = w["pad_id"]
+            say(f"jitter random call {i}: pad ids T={T}")
+            ref = oracle.pad_mask_from_ids(ids, w["pad_id"])
+            t = torch.from_numpy(ids).to(dev)
+            mask = torch.full((T,), 7, dtype=torch.uint8, device=dev)
+            scal = torch.full((2,), -7, dtype=torch.int32, device=dev)
+            sp = scal.data_ptr()
+            assert jl.psq_padding_mask_from_token_ids(t.data_ptr(), _lib.I64, T, w["pad_id"],
+                                                      mask.data_ptr(), sp, sp + 4, ws.data_ptr(),
+                                                      ws.numel(), _stream(dev)) == 0
+            nc, st = scal.cpu().tolist()
+            assert st == ref["status"] and nc == ref["num_content"]
+            assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"])
+        else:
+            B, P, S, G = c[1], c[2], c[3], c[4]
+            L, Lp = _tables(500 + i, B, P, S)
+            say(f"jitter random call {i}: tables B={B} P={P} S={S} G={G}")
+            ref = oracle.split_thd(L, Lp, S, G)
+            assert ref["status"] == 0
+            tL, tLp = torch.from_numpy(L).to(dev), torch.from_numpy(Lp).to(dev)
+            lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, tL.data_ptr(), tLp.data_ptr(), _lib.I64,
+                                   P, V)
+            cap = G * (B // G * P + 1)
+            cu = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+            cp = torch.full((cap,), -7, dtype=torch.int32, device=dev)
+            mask = torch.full((B * S,), 7, dtype=torch.uint8, device=dev)
+            per = torch.full((3, G), -7, dtype=torch.int32, device=dev)
+            scal = torch.full((2,), -7, dtype=torch.int32, device=dev)
+            pp, sp = per.data_ptr(), scal.data_ptr()
+            assert jl.psq_split_thd(ctypes.byref(lay), B, S, G, cu.data_ptr(), cp.data_ptr(), sp,
+                                    pp, pp + 4 * G, pp + 8 * G, mask.data_ptr(), arr, n_c,
+                                    sp + 4, ws.data_ptr(), ws.numel(), _stream(dev)) == 0
+            width, st = scal.cpu().tolist()
+            assert st == 0 and width == ref["cu_seqlens"].shape[1]
+            assert np.array_equal(cu[: G * width].view(G, width).cpu().numpy(), ref["cu_seqlens"])
+            assert np.array_equal(cp[: G * width].view(G, width).cpu().numpy(),
+                                  ref["cu_seqlens_padded"])
+            for j, key in enumerate(("num_seqs", "max_seqlen", "pad_between_seqs")):
+                assert np.array_equal(per[j].cpu().numpy(), ref[key]), key
+            assert np.array_equal(mask.cpu().numpy().reshape(G, B // G * S), ref["padding_mask"])
+    _assert_zero(ws, scratch=(256, 49664))
