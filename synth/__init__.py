@@ -193,8 +193,8 @@ def token_budget_bins(padded_len, budget: int) -> tuple:
 def trainer_rectangle(seed: int = 6, N: int = 256, q: int = 64, budget: int = 16384,
                       median: float = 400.0, sigma: float = 1.2, max_len: int = 8192) -> dict:
     """A trainer micro-batch: padded rectangle, lengths, token-budget bins,
-    and the packed row width the packer chose (its fullest bin's fill: the
-    row is as wide as the batch needs)."""
+    and the packed row width the packer chose: the padded fill of its
+    fullest bin, so no row is wider than that bin requires."""
     rng_len, rng_tok = _streams(seed)
     real = _lognormal_int(rng_len, median, sigma, 1, max_len, size=N)
     W = int(real.max()) if N > 0 else 0
