@@ -14,7 +14,7 @@
  *   psq_split_thd            the same for equal row groups, results stacked
  *       (split_batch_into_thd_chunks, same page).
  *   psq_padding_mask_from_token_ids   the metadata-free padding mask,
- *       rejecting a pad id that is also content
+ *       which fails when the pad id also occurs among the content ids
  *       (thd_padding_mask_from_token_ids, same page).
  *   psq_pack_rows            the squeeze of padded sources into fixed-capacity
  *       packs, last padded boundary folded to capacity

@@ -259,7 +259,7 @@ void orc_copy_rows(const uint8_t *src, uint8_t *dst, int64_t rows,
 /* Each source is padded to a multiple of q, the padded sources of a pack    */
 /* are laid end to end (Trainer packs: [0,5,15] real, [0,8,20] padded), the  */
 /* rest of the row up to capacity is pad, token_mask is 1 exactly on real    */
-/* tokens (Loader packs), and with fold the last padded boundary is set to   */
+/* tokens (Loader packs), and with fold the last padded boundary becomes    */
 /* the capacity (Loader packs: [0,8,36]).                                    */
 /*                                                                          */
 /* Members of pack p are entries pack_start[p] .. pack_start[p+1]-1 of       */
@@ -396,8 +396,8 @@ uint32_t orc_pack_rect(const int64_t *rows, int64_t W, const int32_t *real_len,
 /* ------------------------------------------------------------------------ */
 /* [P2] thd_padding_mask_from_token_ids: the metadata-free mask.             */
 /*                                                                          */
-/* A slot is padding when its id equals the pad id.  That comparison is only */
-/* right when the pad id fills a right-padded tail and occurs nowhere else,  */
+/* A slot is padding when its id equals the pad id.  That comparison gives  */
+/* the right mask only if the pad slots are one run that ends the stream,   */
 /* so the stream is checked for exactly that: from the first pad slot on,    */
 /* every slot must be pad.  Otherwise the pad id is also content (the        */
 /* page's pad == end-of-text case) and the call fails.                       */

@@ -3,8 +3,8 @@
 The oracle follows the NeMo AutoModel 0.5 API page
 ``nemo_automodel.components.distributed.thd_utils``,
 ``thd_padding_mask_from_token_ids``: padding is marked by comparing ids with
-the pad id, which the page calls correct only when the pad id fills a
-right-padded tail and occurs nowhere else; anything else is rejected (the
+the pad id.  By the page, that comparison is only valid when the pad slots
+form one run at the end of the stream; anything else is rejected (the
 page's example is a model whose pad id is also its end-of-text id).
 
 Pinned by hand cases, the pad == end-of-text collision, the degenerate

@@ -5,7 +5,7 @@
 // multiple of q and the sources of a bin are laid end to end
 // (cu_seqlens [0,5,15], cu_seqlens_padded [0,8,20]).  Loader packs: the row
 // is always `capacity` wide, the tail is pad, token_mask is 1 where a token
-// counts, and the last padded boundary is set to the capacity
+// counts, and the last padded boundary becomes the capacity
 // (cu_seqlens_padded [0,8,36]).
 //
 // Work layout: one single-wave workgroup (64 threads) per (pack, chunk of
