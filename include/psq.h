@@ -304,7 +304,7 @@ int psq_split_thd(const psq_thd_layout *layout, int64_t B, int64_t S, int64_t nu
  * That comparison is a correct mask only when the pad slots form a right-
  * padded tail, so the call checks exactly that and sets
  * PSQ_DATA_PAD_IS_CONTENT in *status when some pad slot comes before a
- * non-pad slot (the pad id is also content).
+ * non-pad slot (the pad id then also stands for content tokens).
  *
  *   input_ids     [T], element type ids_dtype (PSQ_I32 or PSQ_I64).  With
  *                 int32 ids, a pad_id outside the int32 range matches none.

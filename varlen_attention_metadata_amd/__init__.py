@@ -93,10 +93,10 @@ def _raise_status(code: int, what: str, device: torch.device) -> None:
 
 
 def packed_seq_params_from_doc_ids(doc_ids: torch.Tensor) -> PackedSeqParams:
-    """Build packed-sequence metadata from a ``[B, S]`` document map.
+    """Segment boundaries and the longest segment of a ``[B, S]`` document map.
 
-    Segments are maximal runs of one document index within a row, with a
-    boundary at every row start; runs of padding (index 0) are segments too.
+    A segment ends wherever the document index changes and at the end of
+    every row; a run of padding (index 0) counts as a segment like any other.
     """
     _require_gpu(doc_ids, "doc_ids")
     dt = _int_dtype(doc_ids, "doc_ids")
@@ -392,7 +392,7 @@ def split_batch_into_thd_chunks(batch: dict, num_chunks: int, seq_lens_padding_v
 
 
 def thd_padding_mask_from_token_ids(input_ids: torch.Tensor, padding_token_id: int) -> torch.Tensor:
-    """Padding mask by token value, for callers with no pack metadata.
+    """The padding mask from token values alone, when no pack layout is at hand.
 
     ``input_ids`` ``[total_tokens]``; returns bool ``[total_tokens]``, True on
     padding.  Raises ``ValueError`` when ``padding_token_id`` also occurs as

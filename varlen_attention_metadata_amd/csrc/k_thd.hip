@@ -4,8 +4,9 @@
 // NeMo AutoModel 0.5 API, nemo_automodel.components.distributed.thd_utils:
 // process_input_for_thd (sentinel filter of seq_lens / seq_lens_padded,
 // cumulative real and physical boundaries, trailing-pad absorption,
-// pad_between_seqs, max_seqlen) and _thd_padding_mask (sequence i owns
-// [start_i, start_i + padded_i) and holds tokens in its first real_i slots).
+// pad_between_seqs, max_seqlen) and _thd_padding_mask (the padded_i slots
+// from start_i belong to sequence i, and only the first real_i of them are
+// tokens).
 //
 // Readings where the page leaves a step open:
 //   * each row's trailing pad is folded into the row's last sequence, so the

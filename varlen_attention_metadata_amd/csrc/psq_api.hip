@@ -77,7 +77,8 @@ const char *psq_status_string(int code, int is_status) {
     if (code & PSQ_DATA_BAD_INDEX) return "member, pack or source index out of range";
     if (code & PSQ_DATA_WORKSPACE) return "workspace was not zero-filled before use";
     if (code & PSQ_DATA_PAD_IS_CONTENT)
-        return "padding_token_id also occurs as content (pad slots are not a right-padded tail)";
+        return "the pad id appears among the content tokens (its slots do not form one run "
+               "ending the stream)";
     return "unknown status bits";
 }
 
