@@ -90,14 +90,19 @@ def test_graph_thd_tables_with_copies(dev):
     replay_and_check(dev, call, [cu, cp, mask, scal] + list(outs.values()), check)
 
 
-def test_graph_doc_map_with_copy(dev):
-    d = synth.doc_map_medium()
-    B, S = d.shape
+# every document-map path: one workgroup; one launch of 32 tiles of 1024
+# positions, of 220 tiles of 4096, of 256 tiles of 16384; and two launches
+@pytest.mark.parametrize("B,S", [(4, 64), (8, 4096), (3, 300001), (1, 4194304), (3, 2100000)],
+                         ids=["one_workgroup", "one_launch_1", "one_launch_4", "one_launch_16",
+                              "two_launch"])
+def test_graph_doc_map_with_copy(dev, B, S):
+    d = synth.doc_map_medium(2, B, S)
     T = B * S
-    say("graph: doc map + bf16 collapse")
+    H = 64 if T <= 100000 else 8
+    say(f"graph: doc map {B}x{S} + bf16 collapse of {H} columns")
     doc = torch.from_numpy(d).to(dev)
-    hidden = torch.randn((B, S, 64), dtype=torch.bfloat16, device=dev)
-    out_h = torch.empty((T, 64), dtype=torch.bfloat16, device=dev)
+    hidden = torch.randn((B, S, H), dtype=torch.bfloat16, device=dev)
+    out_h = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     cu = torch.empty(T + 1, dtype=torch.int32, device=dev)
     mask = torch.empty(T, dtype=torch.uint8, device=dev)
     scal = torch.empty(4, dtype=torch.int32, device=dev)
@@ -117,7 +122,7 @@ def test_graph_doc_map_with_copy(dev):
         assert (n, mx, pb, st) == (ref["num_segments"], ref["max_seqlen"], 0, 0), rep
         assert np.array_equal(cu[: n + 1].cpu().numpy(), ref["cu_seqlens"]), rep
         assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"]), rep
-        assert torch.equal(out_h.view(torch.int16), hidden.reshape(T, 64).view(torch.int16)), rep
+        assert torch.equal(out_h.view(torch.int16), hidden.reshape(T, H).view(torch.int16)), rep
 
     replay_and_check(dev, call, [cu, mask, scal, out_h], check)
 
