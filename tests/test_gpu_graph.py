@@ -51,12 +51,16 @@ def replay_and_check(dev, call, outputs, check, replays=4):
         check(rep)
 
 
-def test_graph_thd_tables_with_copies(dev):
-    w = synth.thd_tables()
-    S = w["S"]
-    B, P = w["seq_lens"].shape
+# workload 3's 16 x 64 tables (the single-workgroup kernel), and 64 x 128 tables
+# (the multi-workgroup kernel with its ticket, look-back and clean-up, the
+# 16-byte collapses fused into its launch)
+@pytest.mark.parametrize("B,S,P", [(16, 8192, 64), (64, 4096, 128)],
+                         ids=["single_workgroup", "multi_workgroup"])
+def test_graph_thd_tables_with_copies(dev, B, S, P):
+    w = synth.thd_tables(3, B=B, S=S, P=P)
+    assert w["seq_lens"].shape == (B, P)
     T = B * S
-    say("graph: thd tables + 3 collapses")
+    say(f"graph: thd tables {B}x{P} S={S} + 3 collapses")
     t = {k: torch.from_numpy(w[k]).to(dev) for k in
          ("input_ids", "labels", "position_ids", "seq_lens", "seq_lens_padded")}
     outs = {k: torch.empty(T, dtype=torch.int64, device=dev) for k in ("input_ids", "labels", "position_ids")}
@@ -204,6 +208,47 @@ def test_graph_pack_split_and_padids(dev):
 
     replay_and_check(dev, call, [packed, tm, pcu, pcp, pst, scu, scp, smask, per, sscal, imask,
                                  iscal], check)
+
+
+def test_graph_split_on_the_multi_workgroup_kernel(dev):
+    """The split of 64 x 128 tables into 4 row groups: the multi-workgroup
+    kernel stages each group's boundaries in the workspace and the last
+    workgroup stacks them and clears the staging, on every replay."""
+    w = synth.thd_tables(3, B=64, S=4096, P=128)
+    B, P, S, G = 64, 128, 4096, 4
+    say(f"graph: split of {B}x{P} tables into {G} row groups")
+    L = torch.from_numpy(w["seq_lens"]).to(dev)
+    Lp = torch.from_numpy(w["seq_lens_padded"]).to(dev)
+    cap = G * (B // G * P + 1)
+    cu = torch.empty(cap, dtype=torch.int32, device=dev)
+    cp = torch.empty(cap, dtype=torch.int32, device=dev)
+    mask = torch.empty(B * S, dtype=torch.uint8, device=dev)
+    per = torch.empty((3, G), dtype=torch.int32, device=dev)
+    scal = torch.empty(2, dtype=torch.int32, device=dev)
+    lay = _lib.make_layout(_lib.LAYOUT_SEQ_LENS, L.data_ptr(), Lp.data_ptr(), _lib.I64, P, V)
+    ws = zeroed_workspace(dev, _lib.psq_split_thd_workspace(lay, B, S, G))
+    noc, _ = _lib.make_copies([])
+    ref = oracle.split_thd(w["seq_lens"], w["seq_lens_padded"], S, G)
+    assert ref["status"] == 0
+    pp, sp = per.data_ptr(), scal.data_ptr()
+
+    def call(stream):
+        _lib.psq_split_thd(lay, B, S, G, cu.data_ptr(), cp.data_ptr(), sp, pp, pp + 4 * G,
+                           pp + 8 * G, mask.data_ptr(), noc, 0, sp + 4, ws.data_ptr(), ws.numel(),
+                           stream)
+
+    def check(rep):
+        width, st = scal.cpu().tolist()
+        assert st == 0 and width == ref["cu_seqlens"].shape[1], rep
+        assert np.array_equal(cu[: G * width].view(G, width).cpu().numpy(), ref["cu_seqlens"]), rep
+        assert np.array_equal(cp[: G * width].view(G, width).cpu().numpy(),
+                              ref["cu_seqlens_padded"]), rep
+        for i, key in enumerate(("num_seqs", "max_seqlen", "pad_between_seqs")):
+            assert np.array_equal(per[i].cpu().numpy(), ref[key]), (rep, key)
+        assert np.array_equal(mask.cpu().numpy().reshape(G, B // G * S), ref["padding_mask"]), rep
+
+    replay_and_check(dev, call, [cu, cp, mask, per, scal], check)
+    assert int(ws.count_nonzero().item()) == 0, "workspace left dirty"
 
 
 def test_two_streams_with_own_workspaces(dev):
