@@ -251,6 +251,38 @@ def test_graph_split_on_the_multi_workgroup_kernel(dev):
     assert int(ws.count_nonzero().item()) == 0, "workspace left dirty"
 
 
+@pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
+def test_graph_pad_ids_grid_stride(dev, dtype):
+    """The pad-id mask over 5 M ids: 2048 workgroups striding over more tiles
+    than that (int64: 2442 tiles), its tagged words read and zeroed by the
+    last workgroup on every replay; a planted pad id in the content."""
+    T = 5_000_000
+    w = synth.pad_tail_stream(9, T=T, tail_hi=T // 3)
+    ids_np = w["input_ids"].copy()
+    ids_np[12345] = w["pad_id"]
+    ref = oracle.pad_mask_from_ids(ids_np, w["pad_id"])
+    say(f"graph: pad ids T={T} {dtype}")
+    ids = torch.from_numpy(ids_np).to(dev, dtype)
+    mask = torch.empty(T, dtype=torch.uint8, device=dev)
+    scal = torch.empty(2, dtype=torch.int32, device=dev)
+    ws = zeroed_workspace(dev, _lib.psq_padding_mask_from_token_ids_workspace(T))
+    kind = _lib.I64 if dtype == torch.int64 else _lib.I32
+    sp = scal.data_ptr()
+
+    def call(stream):
+        _lib.psq_padding_mask_from_token_ids(ids.data_ptr(), kind, T, w["pad_id"],
+                                             mask.data_ptr(), sp, sp + 4, ws.data_ptr(),
+                                             ws.numel(), stream)
+
+    def check(rep):
+        nc, st = scal.cpu().tolist()
+        assert st == ref["status"] and nc == ref["num_content"], rep
+        assert np.array_equal(mask.cpu().numpy(), ref["padding_mask"]), rep
+
+    replay_and_check(dev, call, [mask, scal], check)
+    assert int(ws.count_nonzero().item()) == 0, "workspace left dirty"
+
+
 def test_two_streams_with_own_workspaces(dev):
     """Two different tables on two streams at once, each with its workspace."""
     rng = np.random.default_rng(21)
