@@ -251,6 +251,49 @@ def test_graph_split_on_the_multi_workgroup_kernel(dev):
     assert int(ws.count_nonzero().item()) == 0, "workspace left dirty"
 
 
+def test_graph_trainer_squeeze(dev):
+    """The trainer's squeeze of a 256-row rectangle into 15 bins: few enough
+    chunks that the 256-slot kernel runs; its completion word is cleared by
+    the last pack leader on every replay."""
+    w = synth.trainer_rectangle()
+    rows_np, rl_np, bins, q, C = w["rows"], w["real_len"], w["bins"], w["q"], w["width"]
+    N, W = rows_np.shape
+    order, start = oracle.bins_to_csr(bins)
+    P = len(bins)
+    ref = oracle.pack_rect(rows_np, rl_np, q, bins, width=C)
+    assert ref["status"] == 0
+    say(f"graph: trainer squeeze {N}x{W} into {P} bins of {C}")
+    rows = torch.from_numpy(rows_np).to(dev)
+    rl = torch.from_numpy(np.asarray(rl_np, dtype=np.int32)).to(dev)
+    order_full = np.zeros(N, dtype=np.int32)
+    order_full[:order.size] = order
+    od = torch.from_numpy(order_full).to(dev)
+    ps = torch.from_numpy(start).to(dev)
+    packed = torch.empty((P, C), dtype=torch.int64, device=dev)
+    tm = torch.empty((P, C), dtype=torch.uint8, device=dev)
+    cu = torch.empty(N + P, dtype=torch.int32, device=dev)
+    cp = torch.empty(N + P, dtype=torch.int32, device=dev)
+    st = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = zeroed_workspace(dev, _lib.psq_pack_rows_workspace(N, P, C))
+    used = order.size + P
+
+    def call(stream):
+        _lib.psq_pack_padded_rows(rows.data_ptr(), W, rl.data_ptr(), N, q, od.data_ptr(),
+                                  ps.data_ptr(), P, C, 0, 0, packed.data_ptr(), tm.data_ptr(),
+                                  cu.data_ptr(), cp.data_ptr(), st.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), stream)
+
+    def check(rep):
+        assert int(st.item()) == 0, rep
+        assert np.array_equal(packed.cpu().numpy(), ref["packed"]), rep
+        assert np.array_equal(tm.cpu().numpy(), ref["token_mask"]), rep
+        assert np.array_equal(cu[:used].cpu().numpy(), ref["cu_seqlens"]), rep
+        assert np.array_equal(cp[:used].cpu().numpy(), ref["cu_seqlens_padded"]), rep
+
+    replay_and_check(dev, call, [packed, tm, cu, cp, st], check)
+    assert int(ws.count_nonzero().item()) == 0, "workspace left dirty"
+
+
 @pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
 def test_graph_pad_ids_grid_stride(dev, dtype):
     """The pad-id mask over 5 M ids: 2048 workgroups striding over more tiles
