@@ -260,7 +260,7 @@ def bins_to_csr(bins):
 
 
 def trainer_width(real_len, bins, q: int) -> int:
-    """Trainer packs: the row is as wide as the widest bin's padded sources."""
+    """Trainer packs: the row width is the largest padded fill over the bins."""
     rl = np.asarray(real_len, dtype=np.int64)
     widths = [sum(-(-int(rl[i]) // q) * q for i in b) for b in bins]
     return max(widths) if widths else 0

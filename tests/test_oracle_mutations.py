@@ -108,6 +108,12 @@ MUTATIONS = [
     ("pack_tail_skips_first_slot", C_SRC, "for (s = off; s < C; s++) {",
      "for (s = off + 1; s < C; s++) {", PACK),
     ("rect_length_at_width_rejected", C_SRC, "real > row_width", "real >= row_width", PACK),
+    ("trainer_width_of_narrowest_bin", PY_SRC, "return max(widths) if widths else 0",
+     "return min(widths) if widths else 0", PACK),
+    ("bins_to_csr_starts_shifted", PY_SRC, "start[1:] = np.cumsum([len(b) for b in bins])",
+     "start[1:] = np.cumsum([len(b) for b in bins]) - (len(bins) > 1)", PACK),
+    ("pack_slices_without_pack_offset", PY_SRC, "out.append(np.asarray(cu_csr)[a + p: b + p + 1])",
+     "out.append(np.asarray(cu_csr)[a: b + 1])", PACK),
     ("trainer_width_from_real", PY_SRC,
      "widths = [sum(-(-int(rl[i]) // q) * q for i in b) for b in bins]",
      "widths = [sum(int(rl[i]) for i in b) for b in bins]", PACK),
