@@ -83,3 +83,51 @@ def test_pad_tail_stream():
     ids, pad, tail = w["input_ids"], w["pad_id"], w["tail"]
     assert ids.size == 131072 and pad > synth.TOKEN_HIGH
     assert np.all(ids[ids.size - tail:] == pad) and not np.any(ids[:ids.size - tail] == pad)
+
+
+def _runs(row):
+    """(value, length) of each maximal run of a row."""
+    edges = np.flatnonzero(np.diff(row)) + 1
+    starts = np.concatenate([[0], edges])
+    ends = np.concatenate([edges, [row.size]])
+    return [(int(row[a]), int(b - a)) for a, b in zip(starts, ends)]
+
+
+def _check_doc_rows(d, max_doc, max_pad):
+    for row in d:
+        runs = _runs(row)
+        pad = runs[-1][1] if runs[-1][0] == 0 else 0
+        assert pad <= max_pad
+        docs = runs[:-1] if pad else runs
+        # indices restart at 1 and count up by one; only the last document may
+        # be cut short by the row end, none is longer than the recipe allows
+        assert [v for v, _ in docs] == list(range(1, len(docs) + 1))
+        assert all(1 <= n <= max_doc for _, n in docs)
+
+
+def test_recipes_match_the_configs():
+    # config 1 and the stage map: documents of 1..24 tokens, a pad tail of 0..16
+    _check_doc_rows(synth.doc_map_small(), 24, 16)
+    st = synth.stage_embedding()
+    _check_doc_rows(st["doc_ids"], 24, 16)
+    assert st["doc_ids"].shape == (32, 32768)
+    assert np.array_equal(st["position_ids"], synth.run_positions(st["doc_ids"]))
+    # config 2: documents clipped to 1..4096, a pad tail of 0..512
+    _check_doc_rows(synth.doc_map_medium(), 4096, 512)
+    # config 3: real lengths 1..2048, padded exactly to the next multiple of 8,
+    # at most 64 per row, tokens 0..151935
+    w = synth.thd_tables()
+    L, Lp = w["seq_lens"], w["seq_lens_padded"]
+    valid = L != -1000
+    assert L[valid].min() >= 1 and L[valid].max() <= 2048
+    assert np.array_equal(Lp[valid], -(-L[valid] // 8) * 8)
+    assert valid.sum(axis=1).max() <= 64
+    assert w["input_ids"].shape == (16, 8192) and w["input_ids"].min() >= 0
+    assert w["input_ids"].max() <= synth.TOKEN_HIGH == 151935
+    # config 4: 65 536 sources of 1..8192 tokens, stored end to end
+    p = synth.pack_sources()
+    rl = p["real_len"]
+    assert rl.size == 65536 and rl.min() >= 1 and rl.max() <= 8192
+    assert np.array_equal(p["src_off"], np.concatenate([[0], np.cumsum(rl)[:-1]]))
+    assert p["src"].size == int(rl.sum()) and p["src"].max() <= 151935
+    assert p["capacity"] == 16384 and p["q"] == 64
